@@ -1,0 +1,158 @@
+"""Stable LatentMoE forward layer -- oracle.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Plain NumPy in float64
+from the (fp32 / bf16-valued / MXFP4-decoded) inputs; no intermediate is
+rounded.  Routing decisions come from :mod:`oracle.qb` on fp32 scores.
+
+Steps, in the pages' order:
+
+1. Router: s = sigmoid(x W_r^T + p) on the full-width token, fp32 scores
+   ([K3-structure-5] Q&A on routing: sigmoid on the full-width input).
+   ``p`` is an optional per-expert logit offset (synthetic popularity skew).
+2. Routing: Quantile Balancing or a frozen bias, top-k on the biased scores,
+   weights = chosen raw scores renormalised (:mod:`oracle.qb`).
+3. Latent down-projection z = x W_down^T, 7168 -> 3584 (half width)
+   ([K3-LatentMoE] "Why does the router need three moves?", first move;
+   [K3-structure-5] 延伸解读 "为什么K3选择半宽latent空间").
+4. Routed experts in the latent space, GLU FFNs with SiTU-GLU:
+   h = SiLU(4 tanh(g/4)) * 25 tanh(u/25), y_e = h W_d,e^T
+   ([K3-structure-5] Q&A "SiTU-GLU 激活函数是如何工作的？": softcap
+   beta*tanh(x/beta) on the gate (beta1=4) and up (beta2=25) branches of SwiGLU,
+   output bounded by 100).
+5. Weighted sum in the latent space, RMSNorm after aggregation and before the
+   up-projection ([K3-structure-5] Q&A on RMSNorm; [K3-LatentMoE] second move).
+6. Up-projection back to d, plus the two shared experts merged into one MLP of
+   intermediate 6144 at full width, added to the routed output
+   ([K3-structure-5] Q&A on the shared expert).
+
+Readings (also in the design doc): the projections carry no bias terms; the shared
+MLP uses SiTU-GLU too (``hidden_act: situ`` is model-wide); RMSNorm eps = 1e-6
+with gain gamma; routed scaling factor 1.
+
+Parity status: sigmoid, SiTU-GLU, RMSNorm, MXFP4 decoding and the shared-MLP
+merge are pinned by tests (closed forms, bounds, identities, the OCP code
+table); the composition of the whole layer is "parity unpinned" beyond those
+component pins, since the pages print no worked example.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import qb
+
+BETA_GATE = 4.0
+BETA_UP = 25.0
+
+
+def sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def router_scores(x, w_router, logit_offset=None):
+    """fp32 sigmoid scores [T, n] of full-width tokens (float64 inside)."""
+    logits = np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+    if logit_offset is not None:
+        logits = logits + np.asarray(logit_offset, np.float64)[None, :]
+    return sigmoid(logits).astype(np.float32)
+
+
+def softcap(v, beta):
+    return beta * np.tanh(np.asarray(v, np.float64) / beta)
+
+
+def situ_glu(g, u):
+    """SiTU-GLU: SiLU of the soft-capped gate times the soft-capped up branch."""
+    gc = softcap(g, BETA_GATE)
+    return gc * sigmoid(gc) * softcap(u, BETA_UP)
+
+
+def rmsnorm(y, gamma, eps):
+    y = np.asarray(y, np.float64)
+    return y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps) * np.asarray(gamma, np.float64)
+
+
+# OCP Microscaling E2M1 magnitudes for codes 0..7 (bit 3 = sign).
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mxfp4_decode(codes, scales):
+    """Decode MXFP4 [rows, K/2] codes and [rows, K/32] E8M0 scales to float64.
+
+    Element 2i is the low nibble of byte i, element 2i+1 the high nibble;
+    value = (-1)^sign * E2M1[mag] * 2^(scale - 127).
+    """
+    codes = np.asarray(codes, np.uint8)
+    scales = np.asarray(scales, np.uint8)
+    rows, half = codes.shape
+    nib = np.empty((rows, 2 * half), np.uint8)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    mag = E2M1_VALUES[nib & 7]
+    val = np.where(nib & 8, -mag, mag)
+    scale = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return val * np.repeat(scale, 32, axis=1)
+
+
+def as_f64(t):
+    """torch tensor / ndarray (fp32, bf16) -> float64 ndarray."""
+    if hasattr(t, "detach"):
+        t = t.detach().cpu()
+        if str(t.dtype) == "torch.bfloat16":
+            t = t.float()
+        t = t.numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def expert_matrix(w, e):
+    """Weight matrix of routed expert e as float64 [rows, K]; ``w`` is either
+    a dense [n, rows, K] tensor or an MXFP4 (codes, scales) pair."""
+    if isinstance(w, tuple):
+        codes, scales = w
+        c = codes[e].cpu().numpy() if hasattr(codes, "cpu") else codes[e]
+        s = scales[e].cpu().numpy() if hasattr(scales, "cpu") else scales[e]
+        return mxfp4_decode(c, s)
+    return as_f64(w[e])
+
+
+def shared_mlp(x, ws_gate, ws_up, ws_down):
+    x = as_f64(x)
+    h = situ_glu(x @ as_f64(ws_gate).T, x @ as_f64(ws_up).T)
+    return h @ as_f64(ws_down).T
+
+
+def route_layer(inp, k, mode=qb.MODE_BATCH, bias=None):
+    """Router scores and routing of a whole batch."""
+    s = router_scores(as_f64(inp["x"]), as_f64(inp["w_router"]),
+                      None if inp.get("logit_offset") is None else as_f64(inp["logit_offset"]))
+    r = qb.route_qb(s, k, bias=bias, mode=mode)
+    r["scores"] = s
+    return r
+
+
+def layer_forward(inp, idx, w, eps, tokens=None):
+    """Layer output (float64) for the given routing ``idx``/``w`` [T, k].
+
+    ``tokens`` restricts the computation to those token rows (experts are
+    decoded one at a time, so full-size layers can be sampled).
+    """
+    x = as_f64(inp["x"])
+    T = x.shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    xs = x[tokens]
+    z = xs @ as_f64(inp["w_down"]).T
+    idx_s = np.asarray(idx)[tokens]
+    w_s = np.asarray(w, np.float64)[tokens]
+    y = np.zeros((len(tokens), z.shape[1]))
+    for e in np.unique(idx_s):
+        rows, slots = np.nonzero(idx_s == e)
+        wg = expert_matrix(inp["w_gate"], int(e))
+        wu = expert_matrix(inp["w_uproj"], int(e))
+        wd = expert_matrix(inp["w_dn"], int(e))
+        ze = z[rows]
+        h = situ_glu(ze @ wg.T, ze @ wu.T)
+        y[rows] += w_s[rows, slots][:, None] * (h @ wd.T)
+    yn = rmsnorm(y, as_f64(inp["rms_gamma"]), eps)
+    out = yn @ as_f64(inp["w_up"]).T
+    out += shared_mlp(xs, inp["ws_gate"], inp["ws_up"], inp["ws_down"])
+    return out

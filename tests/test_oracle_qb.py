@@ -1,0 +1,237 @@
+"""Pins of the QB routing oracle against what the pages and mathematics fix.
+
+Each pin is chosen so that a plausible mistake in ``oracle.qb`` (a wrong sign,
+an off-by-one order statistic, a dropped tie rule, a transposed index) fails:
+
+* brute force over every balanced assignment on tiny inputs,
+* the LP optimum of the balanced-assignment problem (totally unimodular, so
+  the LP optimum is the integral optimum) -- the problem QB starts from,
+* k = 1 against the textbook Hungarian algorithm with expert slots replicated,
+* dual optimality, the fixed-point (idempotence) property, the coordinate
+  step, the DeepSeek-V3 sign-update relation, the weights' definition and
+  the degenerate cases.
+"""
+import itertools
+
+import numpy as np
+import pytest
+from scipy.optimize import linear_sum_assignment, linprog
+
+from oracle import qb
+
+
+def rand_scores(T, n, seed, skew=0.5):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, n)) + skew * rng.standard_normal(n)[None, :]
+    return (1 / (1 + np.exp(-logits))).astype(np.float32)
+
+
+def sel_matrix(idx, n):
+    S = np.zeros((idx.shape[0], n), bool)
+    np.put_along_axis(S, idx.astype(np.int64), True, axis=1)
+    return S
+
+
+def test_targets_sum_and_spread():
+    for T, n, k in [(64, 32, 4), (4096, 896, 16), (64, 896, 16), (5, 3, 2), (0, 7, 3)]:
+        C = qb.targets(T, n, k)
+        assert C.sum() == T * k
+        assert set(np.unique(C)) <= {T * k // n, -(-T * k // n)}
+        assert (np.diff(C) <= 0).all()       # ceilings go to the lowest indices
+
+
+def test_fixed_point_exact_for_normal_scores():
+    s = np.array([0.5, 0.75, 2.0 ** -17, 1.0, 0.0, 0.1], np.float32)
+    sfx = qb.to_fixed(s[None, :])[0]
+    assert list(sfx[:5]) == [2 ** 39, 3 * 2 ** 38, 2 ** 23, 2 ** 40, 0]
+    assert sfx[5] == round(float(np.float32(0.1)) * 2 ** 40)
+
+
+@pytest.mark.parametrize("T,n,k,seed", [(6, 4, 2, s) for s in range(4)] +
+                         [(5, 3, 2, s) for s in range(3)] + [(5, 5, 2, 7)])
+def test_brute_force(T, n, k, seed):
+    s = rand_scores(T, n, seed, skew=1.0)
+    r = qb.route_qb(s, k)
+    assert r["info"][1] == qb.STATUS_OK
+    C = qb.targets(T, n, k)
+    best, best_S = None, None
+    choices = list(itertools.combinations(range(n), k))
+    for combo in itertools.product(choices, repeat=T):
+        S = np.zeros((T, n), bool)
+        for t, c in enumerate(combo):
+            S[t, list(c)] = True
+        if not (S.sum(0) == C).all():
+            continue
+        F = qb.assignment_objective(s, S)
+        if best is None or F > best:
+            best, best_S = F, S
+    got = sel_matrix(r["idx"], n)
+    assert (got == best_S).all()
+    assert (r["loads"] == C).all()
+
+
+@pytest.mark.parametrize("T,n,k,seed", [(256, 16, 4, 0), (300, 24, 5, 1)])
+def test_lp_optimum(T, n, k, seed):
+    s = rand_scores(T, n, seed)
+    r = qb.route_qb(s, k)
+    assert r["info"][1] == qb.STATUS_OK
+    C = qb.targets(T, n, k)
+    # maximise sum x*s s.t. row sums k, column sums C, 0 <= x <= 1
+    A_eq = np.zeros((T + n, T * n))
+    for t in range(T):
+        A_eq[t, t * n:(t + 1) * n] = 1
+    for e in range(n):
+        A_eq[T + e, e::n] = 1
+    b_eq = np.concatenate([np.full(T, k), C])
+    res = linprog(-s.astype(np.float64).ravel(), A_eq=A_eq, b_eq=b_eq, bounds=(0, 1),
+                  method="highs")
+    assert res.status == 0
+    x = res.x.reshape(T, n)
+    assert np.abs(x - np.round(x)).max() < 1e-6
+    got = sel_matrix(r["idx"], n)
+    assert (got == (x > 0.5)).all()
+
+
+def test_k1_hungarian():
+    T, n = 60, 12
+    s = rand_scores(T, n, 3, skew=1.0)
+    r = qb.route_qb(s, 1)
+    C = qb.targets(T, n, 1)
+    slots = np.repeat(np.arange(n), C)
+    rows, cols = linear_sum_assignment(-s.astype(np.float64)[:, slots])
+    ref = slots[cols[np.argsort(rows)]]
+    assert (r["idx"][:, 0] == ref).all()
+
+
+def dual_value(sfx, bfx, C, k):
+    """D(b) = sum_t (sum of the k largest s+b of token t) - sum_e C_e b_e,
+    exact integers on the 2^-40 grid."""
+    v = sfx + bfx[None, :]
+    top = -np.sort(-v, axis=1)[:, :k]
+    return int(sum(int(x) for x in top.sum(axis=1))) - int(sum(int(c) * int(b) for c, b in zip(C, bfx)))
+
+
+def test_dual_optimality_and_sign_update():
+    T, n, k = 200, 16, 3
+    s = rand_scores(T, n, 11, skew=1.0)
+    r = qb.route_qb(s, k)
+    sfx = qb.to_fixed(s)
+    C = qb.targets(T, n, k)
+    b = r["bfx"]
+    D0 = dual_value(sfx, b, C, k)
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        delta = rng.integers(-2 ** 30, 2 ** 30, size=n)
+        assert dual_value(sfx, b + delta, C, k) >= D0
+    # DeepSeek-V3's sign rule is SignSGD on the same dual: from an unbalanced
+    # bias, the slope of D along e_e is L_e - C_e, and b + g*sign(C - L)
+    # with a small step g lowers D by g * sum |L - C|.
+    b0 = np.zeros(n, np.int64)
+    _, _, S0 = qb.select(sfx, b0, k)
+    L0 = S0.sum(0)
+    assert (L0 != C).any()
+    g = 1
+    step = np.sign(C - L0)
+    _, _, S1 = qb.select(sfx, b0 + g * step, k)
+    assert (S1 == S0).all()                  # no key crossed for so small a step
+    assert dual_value(sfx, b0 + g * step, C, k) - dual_value(sfx, b0, C, k) == -g * int(np.abs(L0 - C).sum())
+    for e in range(n):
+        one = np.zeros(n, np.int64)
+        one[e] = 1
+        assert dual_value(sfx, b0 + one, C, k) - dual_value(sfx, b0, C, k) == L0[e] - C[e]
+
+
+def test_idempotent_fixed_point():
+    s = rand_scores(512, 32, 5)
+    r1 = qb.route_qb(s, 4)
+    r2 = qb.route_qb(s, 4, bias=r1["bias"])
+    assert r2["info"][0] == 0 and r2["info"][3] == 0
+    assert (r2["bfx"] == r1["bfx"]).all()
+    assert (r2["idx"] == r1["idx"]).all()
+    assert 0 <= int(r1["bfx"].sum()) < 32        # common offset removed
+
+
+def test_coordinate_step_is_exact():
+    T, n, k = 500, 20, 3
+    s = rand_scores(T, n, 8, skew=1.0)
+    sfx = qb.to_fixed(s)
+    C = qb.targets(T, n, k)
+    rng = np.random.default_rng(1)
+    b = rng.integers(-2 ** 36, 2 ** 36, size=n)
+    th_k, th_k1, S = qb.select(sfx, b, k)
+    for e in range(n):
+        M = qb.margins(sfx[:, e], e, S[:, e], th_k, th_k1)
+        b2 = b.copy()
+        b2[e] = qb.coordinate_bias(M, int(C[e]))
+        _, _, S2 = qb.select(sfx, b2, k)
+        assert S2[:, e].sum() == C[e]
+
+
+def test_zero_bias_is_plain_topk_and_weights():
+    T, n, k = 100, 24, 5
+    s = rand_scores(T, n, 2)
+    r = qb.route_qb(s, k, mode=qb.MODE_FROZEN)
+    # plain top-k by raw score, ties to the lower index, written independently
+    order = np.lexsort((np.broadcast_to(np.arange(n), (T, n)), -s.astype(np.float64)), axis=1)
+    assert (r["idx"] == order[:, :k]).all()
+    raw = np.take_along_axis(s.astype(np.float64), r["idx"].astype(np.int64), 1)
+    assert np.allclose(r["w"].sum(1), 1.0, atol=1e-15)
+    assert np.allclose(r["w"], raw / raw.sum(1, keepdims=True), rtol=1e-15)
+    # a constant bias changes nothing
+    r2 = qb.route_qb(s, k, bias=np.full(n, 0.125), mode=qb.MODE_FROZEN)
+    assert (r2["idx"] == r["idx"]).all()
+
+
+def test_weights_do_not_depend_on_bias():
+    T, n, k = 300, 16, 4
+    s = rand_scores(T, n, 4, skew=1.5)
+    r = qb.route_qb(s, k)
+    plain = qb.route_qb(s, k, mode=qb.MODE_FROZEN)
+    assert not (r["idx"] == plain["idx"]).all()                 # skew: bias moved selection
+    assert np.ptp(r["bias"]) > 0
+    raw = np.take_along_axis(s.astype(np.float64), r["idx"].astype(np.int64), 1)
+    assert np.allclose(r["w"], raw / raw.sum(1, keepdims=True), rtol=1e-15)
+    # idx order: descending raw score
+    assert (np.diff(raw, axis=1) <= 0).all()
+
+
+def test_balanced_input_keeps_zero_bias():
+    n = 16
+    T = 4 * n
+    rng = np.random.default_rng(0)
+    s = (0.1 * rng.random((T, n))).astype(np.float32)
+    for t in range(T):
+        s[t, t % n] = 0.9
+    r = qb.route_qb(s, 1)
+    assert r["info"][0] == 0 and r["info"][3] == 0
+    assert (r["bfx"] == 0).all()
+    assert (r["idx"][:, 0] == np.arange(T) % n).all()
+
+
+def test_degenerate_duplicate_tokens_report_not_balanced():
+    s = np.tile(np.array([[0.7, 0.3]], np.float32), (4, 1))   # 4 identical tokens, C = (2, 2)
+    r = qb.route_qb(s, 1, max_rounds=8, max_sap=8)
+    assert r["info"][1] == qb.STATUS_NOT_BALANCED
+
+
+def test_edge_cases():
+    r = qb.route_qb(np.zeros((0, 8), np.float32), 2)
+    assert r["idx"].shape == (0, 2) and (r["loads"] == 0).all() and r["info"][1] == 0
+    s = rand_scores(10, 4, 0)
+    r = qb.route_qb(s, 4)                 # k == n: everything chosen
+    assert (r["loads"] == 10).all() and r["info"][1] == 0
+    with pytest.raises(ValueError):
+        qb.route_qb(s, 5)
+    with pytest.raises(ValueError):
+        qb.route_qb(np.full((2, 4), 1.5, np.float32), 1)
+
+
+def test_qb_balances_skewed_batch():
+    T, n, k = 1024, 64, 8
+    s = rand_scores(T, n, 9, skew=1.0)
+    r = qb.route_qb(s, k)
+    assert r["info"][1] == qb.STATUS_OK
+    assert (r["loads"] == qb.targets(T, n, k)).all()
+    # the returned bias reproduces the selection in frozen mode
+    f = qb.route_qb(s, k, bias=r["bias"], mode=qb.MODE_FROZEN)
+    assert (f["idx"] == r["idx"]).all()
