@@ -216,7 +216,57 @@ def shortest_paths(sfx, bfx, S, over, under):
             return packed
 
 
-def sap_step(sfx, bfx, k, C, state=None):
+def sparse_edges(sfx, bfx, S, th_k, th_k1, delta):
+    """Every (token t, chosen A, unchosen B) with rho_t(A, B) <= delta, as
+    arrays (A, B, rho).  A path no longer than delta uses only such edges, so
+    distances up to delta computed on this list are exact."""
+    T, n = sfx.shape
+    Kp = sfx + bfx[None, :]
+    kpk = (th_k >> IDX_BITS) - KEY_OFFSET
+    kpk1 = (th_k1 >> IDX_BITS) - KEY_OFFSET
+    rows = np.nonzero(kpk - kpk1 <= delta + 1)[0]
+    As, Bs, Rs = [], [], []
+    for t in rows:
+        low = np.nonzero(S[t] & (Kp[t] - kpk[t] <= delta + 1))[0]
+        high = np.nonzero(~S[t] & (kpk1[t] - Kp[t] <= delta + 1))[0]
+        if low.size == 0 or high.size == 0:
+            continue
+        A = np.repeat(low, high.size)
+        B = np.tile(high, low.size)
+        rho = Kp[t, A] - Kp[t, B] - (A > B)
+        keep = rho <= delta
+        As.append(A[keep]); Bs.append(B[keep]); Rs.append(rho[keep])
+    if not As:
+        z = np.zeros(0, np.int64)
+        return z, z, z
+    return (np.concatenate(As).astype(np.int64), np.concatenate(Bs).astype(np.int64),
+            np.concatenate(Rs).astype(np.int64))
+
+
+def shortest_paths_edges(A, B, rho, over, under):
+    """Bellman-Ford on an explicit edge list with the same packing, tie rule
+    and stopping rule as :func:`shortest_paths`."""
+    n = over.shape[0]
+    packed = np.where(over, np.arange(n, dtype=np.int64), PACKED_INF).astype(np.int64)
+    while True:
+        d = packed >> IDX_BITS
+        dA = d[A]
+        ok = dA < DIST_INF
+        cand = dA + rho
+        ok &= cand < DIST_INF
+        new = packed.copy()
+        np.minimum.at(new, B[ok], (cand[ok] << IDX_BITS) | A[ok])
+        D = np.where(under, new >> IDX_BITS, DIST_INF).min(initial=DIST_INF)
+        changed = new != packed
+        packed = new
+        if not (changed & ((packed >> IDX_BITS) <= D)).any():
+            return packed
+
+
+SPARSE_DELTA = 1 << 30
+
+
+def sap_step(sfx, bfx, k, C, state=None, sparse=True):
     """One shortest-augmenting-path move on the dual (reading 4).
 
     Lowers every expert's bias by (D* - min(d, D*)), which keeps every token's
@@ -224,12 +274,26 @@ def sap_step(sfx, bfx, k, C, state=None):
     the nearest underloaded expert u* tight, then raises the i-th expert on
     that path by i grid units so that each path token moves one step along
     it.  Returns the new biases, or None when no underloaded expert is
-    reachable.
+    reachable.  With ``sparse`` the distances come from the edges of reduced
+    cost <= delta (delta grows 16x until D* <= delta), which gives the same
+    distances and predecessors up to D* as the full relaxation.
     """
     th_k, th_k1, S = state if state is not None else select(sfx, bfx, k)
     L = S.sum(axis=0)
     over, under = L > C, L < C
-    packed = shortest_paths(sfx, bfx, S, over, under)
+    if sparse:
+        delta = SPARSE_DELTA
+        while True:
+            A, B, rho = sparse_edges(sfx, bfx, S, th_k, th_k1, delta)
+            packed = shortest_paths_edges(A, B, rho, over, under)
+            D = int(np.where(under, packed >> IDX_BITS, DIST_INF).min())
+            if D <= delta:
+                break
+            if delta >= (1 << 44):
+                return None
+            delta *= 16
+    else:
+        packed = shortest_paths(sfx, bfx, S, over, under)
     d = packed >> IDX_BITS
     pred = packed & (MAX_EXPERTS - 1)
     d_under = np.where(under, d, DIST_INF)
@@ -249,7 +313,7 @@ def sap_step(sfx, bfx, k, C, state=None):
     return new
 
 
-def route_qb(scores, k, bias=None, mode=MODE_BATCH, max_rounds=64, stall_rounds=4,
+def route_qb(scores, k, bias=None, mode=MODE_BATCH, max_rounds=64, stall_rounds=3,
              max_sap=4096):
     """Route a batch of fp32 scores [T, n] to k experts per token.
 

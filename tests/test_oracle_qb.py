@@ -235,3 +235,26 @@ def test_qb_balances_skewed_batch():
     # the returned bias reproduces the selection in frozen mode
     f = qb.route_qb(s, k, bias=r["bias"], mode=qb.MODE_FROZEN)
     assert (f["idx"] == r["idx"]).all()
+
+
+def test_sparse_paths_equal_full_relaxation():
+    # the augmenting-path step on the edges of reduced cost <= delta must give
+    # exactly the biases of the full Bellman-Ford relaxation
+    for seed, (T, n, k) in enumerate([(400, 24, 3), (600, 40, 5), (300, 16, 2)]):
+        s = rand_scores(T, n, 20 + seed, skew=1.0)
+        sfx = qb.to_fixed(s)
+        C = qb.targets(T, n, k)
+        b = np.zeros(n, np.int64)
+        for _ in range(3):
+            b = qb.coordinate_round(sfx, b, k, C)
+        moves = 0
+        while moves < 6:
+            st = qb.select(sfx, b, k)
+            if (st[2].sum(0) == C).all():
+                break
+            full = qb.sap_step(sfx, b, k, C, st, sparse=False)
+            fast = qb.sap_step(sfx, b, k, C, st, sparse=True)
+            assert (full == fast).all()
+            b = full
+            moves += 1
+        assert moves > 0
