@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Stable LatentMoE layer throughput on one MI355X.
+
+One step = one moe_latent_forward call over a batch already resident in HBM:
+router, Quantile Balancing on the batch, permutation, latent down-projection,
+shared gate/up, routed gate/up with SiTU-GLU, routed down, combine + RMSNorm,
+up-projection fused with the shared down-projection.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload k3_prefill]
+
+Prints one JSON line.  ``roofline`` describes the dominant kernel (the routed
+gate/up grouped GEMM), whose duration is measured with HIP events recorded by
+the library around that launch on its stream; ``cpu_baseline`` times the
+float64 oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
+
+
+def layer_flops_per_token(s):
+    """Matmul flops per token (routed experts counted k times)."""
+    dense = 2 * s.d * s.latent * 2 + 2 * s.d * s.shared * 3
+    routed = s.k * (2 * s.latent * s.m * 3)
+    router = 2 * s.d * s.n
+    return dense + routed, router
+
+
+def weight_bytes(s, touched):
+    eb = 2 if s.act == "bf16" else 4
+    if s.routed == "mxfp4":
+        per_expert = 3 * s.m * s.latent // 2 + 3 * s.m * s.latent // 32
+    else:
+        per_expert = 3 * s.m * s.latent * eb
+    dense = (2 * s.d * s.latent + 3 * s.d * s.shared) * eb + s.n * s.d * 4
+    return touched * per_expert, dense
+
+
+def gate_up_bytes(s, touched, T):
+    """Algorithmic HBM bytes of one routed gate/up launch: the gate and up
+    weights of every expert that received a token, the gathered latent rows
+    it reads and the SiTU-GLU output it writes."""
+    eb = 2 if s.act == "bf16" else 4
+    if s.routed == "mxfp4":
+        w = touched * 2 * (s.m * s.latent // 2 + s.m * s.latent // 32)
+    else:
+        w = touched * 2 * s.m * s.latent * eb
+    return w + T * s.k * s.latent * eb + T * s.k * s.m * eb
+
+
+def cpu_baseline(inp, shape, sample_tokens):
+    """The oracle as it stands, on the host: routing of the whole batch (router
+    + QB) and the layer for ``sample_tokens`` tokens; per-token time scaled."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import layer as olayer
+    from oracle import qb
+
+    x = inp["x"].float().cpu()
+    host = {"x": x, "w_router": inp["w_router"].cpu(),
+            "logit_offset": None if inp["logit_offset"] is None else inp["logit_offset"].cpu()}
+    t0 = time.perf_counter()
+    s = olayer.router_scores(olayer.as_f64(host["x"]), olayer.as_f64(host["w_router"]),
+                             None if host["logit_offset"] is None
+                             else olayer.as_f64(host["logit_offset"]))
+    r = qb.route_qb(s, shape.k)
+    t_route = time.perf_counter() - t0
+    tokens = np.arange(sample_tokens)
+    need = np.unique(r["idx"][tokens])
+    # copy only the experts the sample needs to the host (not timed)
+    def subset(w):
+        if isinstance(w, tuple):
+            return tuple({int(e): w[i][int(e)].cpu() for e in need} for i in range(2))
+        return {int(e): w[int(e)].cpu() for e in need}
+    lay = dict(x=x, w_down=inp["w_down"].cpu(), w_up=inp["w_up"].cpu(),
+               w_gate=subset(inp["w_gate"]), w_uproj=subset(inp["w_uproj"]),
+               w_dn=subset(inp["w_dn"]), rms_gamma=inp["rms_gamma"].cpu(),
+               ws_gate=inp["ws_gate"].cpu(), ws_up=inp["ws_up"].cpu(),
+               ws_down=inp["ws_down"].cpu())
+    t1 = time.perf_counter()
+    olayer.layer_forward(lay, r["idx"], r["w"], shape.eps, tokens=tokens)
+    t_layer = time.perf_counter() - t1
+    per_token = t_route / shape.T + t_layer / sample_tokens
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle router + QB on the full batch of {shape.T} tokens "
+                       f"({t_route:.1f} s) and the float64 layer on {sample_tokens} tokens "
+                       f"({t_layer:.1f} s); tokens/s = 1 / (route_s/T + layer_s/sample)")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="k3_prefill",
+                    choices=["k3_prefill", "k3_decode", "k3_mxfp4"])
+    ap.add_argument("--qb", default="batch", choices=["batch", "frozen"])
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: the layer here runs on a single GPU "
+              "(no sharding or collectives); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_moe_ffn_sigmoid_amd as moe
+    import workloads
+
+    shape = workloads.SHAPES[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = workloads.layer_inputs(shape, dev, seed=0)
+    w = {}
+    for key, v in inp.items():
+        if key == "x" or v is None:
+            continue
+        if isinstance(v, tuple):
+            w[key] = v[0]
+            w[{"w_gate": "s_gate", "w_uproj": "s_uproj", "w_dn": "s_dn"}[key]] = v[1]
+        else:
+            w[key] = v
+    if "logit_offset" in w:
+        w["router_logit_offset"] = w.pop("logit_offset")
+    act = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16}[shape.act]
+    routed = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "mxfp4": moe.MOE_MXFP4}[shape.routed]
+    qb_mode = moe.MOE_QB_BATCH if args.qb == "batch" else moe.MOE_QB_FROZEN
+    sh = moe.make_shape(shape.T, shape.d, shape.latent, shape.n, shape.k, shape.m, shape.shared,
+                        act, routed, shape.eps, qb_mode, 64)
+    ws = torch.empty(moe.forward_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+    bias0 = torch.zeros(shape.n, dtype=torch.float64, device=dev)
+    x = inp["x"]
+
+    def step():
+        return moe.latent_forward(sh, w, x, bias=bias0, workspace=ws)
+
+    for _ in range(args.warmup):
+        r = step()
+    torch.cuda.synchronize()
+    moe.stage_timing(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        r = step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = moe.stage_times()
+    moe.stage_timing(False)
+    ms_per_step = start.elapsed_time(end) / args.steps
+    tokens_per_s = shape.T / (ms_per_step / 1e3)
+
+    loads = r["loads"].cpu()
+    touched = int((loads > 0).sum())
+    info = [int(v) for v in r["info"].cpu()]
+    flops, router_flops = layer_flops_per_token(shape)
+    wb_routed, wb_dense = weight_bytes(shape, touched)
+    gu_ms, gu_n = stages["routed_gate_up"]
+    gu_avg_ms = gu_ms / max(gu_n, 1)
+    gu_bytes = gate_up_bytes(shape, touched, shape.T)
+    achieved = gu_bytes / (gu_avg_ms / 1e3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.act == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights, skewed router offsets)",
+        "config": {"workload": {"k3_prefill": "k3_prefill_bf16", "k3_decode": "k3_decode_bf16",
+                                "k3_mxfp4": "k3_prefill_mxfp4"}[args.workload],
+                   "T": shape.T, "d": shape.d, "latent": shape.latent, "experts": shape.n,
+                   "top_k": shape.k, "inter": shape.m, "shared_inter": shape.shared,
+                   "routed_weights": shape.routed, "qb": args.qb},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "routed gate/up grouped GEMM + SiTU-GLU",
+                     "bytes_per_launch": gu_bytes, "avg_ms": gu_avg_ms},
+        "layer": {
+            "hbm_gbs": (wb_routed + wb_dense) / (ms_per_step / 1e3) / 1e9,
+            "weight_bytes": wb_routed + wb_dense,
+            "mfma_util": (flops + router_flops) * shape.T / (ms_per_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
+            "experts_touched": touched,
+            "qb_info": info,
+            "stages_ms": {k: v[0] / max(v[1], 1) for k, v in stages.items()},
+            "wall_s": wall,
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, shape, args.cpu_sample_tokens)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

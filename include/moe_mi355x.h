@@ -1,0 +1,173 @@
+/*
+ * moe_mi355x.h -- C ABI of the Stable LatentMoE forward layer for MI355X (gfx950).
+ *
+ * The layer (sources by page title and section):
+ *   - sigmoid router on the full-width token; a per-expert bias picks the
+ *     top-k experts, the mixture weights are the chosen raw scores
+ *     renormalised, the bias acts on selection only
+ *     ("Kimi K3 模型结构（5）：宽度维度，Stable LatentMoE", Q&A on routing);
+ *   - Quantile Balancing: per-expert bias from the (1-k/n) quantile of the
+ *     expert's margin minus a common offset, exact target load per expert
+ *     (same page, Q&A on Quantile Balancing; 延伸解读 "Quantile Balancing与
+ *     DeepSeek-V3路由的异同": coordinate descent on the dual of the balanced
+ *     assignment problem);
+ *   - shared latent down-projection d -> d/2, routed GLU experts with
+ *     SiTU-GLU h = SiLU(4 tanh(g/4)) * 25 tanh(u/25), weighted sum, RMSNorm,
+ *     up-projection, plus the merged shared-expert MLP at full width
+ *     ("Kimi K3 — LatentMoE" (dimsnsums.com), section "Why does the router
+ *     need three moves?"; xhh.club page, Q&A on SiTU-GLU, RMSNorm and the
+ *     shared expert);
+ *   - routed-expert weights in MXFP4 for deployment (xhh.club page,
+ *     延伸解读 "参数规模与部署要点").
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller unless
+ *     stated otherwise.  The library never frees or retains caller memory and
+ *     keeps no state between calls apart from loaded code objects.
+ *   - Matrices are row-major [out_features][in_features] (K contiguous);
+ *     activations are [T][features].  bf16 values are passed as raw 16-bit
+ *     patterns.  MXFP4 weights: codes uint8 [rows][K/2] (element 2i in the
+ *     low nibble of byte i, 2i+1 in the high nibble, bit 3 = sign, E2M1
+ *     magnitudes 0,.5,1,1.5,2,3,4,6) and one E8M0 scale byte per 32
+ *     consecutive K elements, uint8 [rows][K/32] (value * 2^(byte-127)).
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Work is enqueued on it.  In MOE_QB_BATCH mode the balancing loop reads
+ *     small control words back to the host, so the call synchronises
+ *     `stream` while it runs; MOE_QB_FROZEN calls never synchronise.
+ *   - Return value: MOE_OK or a negative moe_status for invalid arguments,
+ *     unsupported combinations, a too-small workspace or a HIP error.  Nothing
+ *     is launched when validation fails.  The outcome of balancing (rounds,
+ *     balanced or not) is reported through `qb_info`, not the return value.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad shape, NULL where a buffer is required, k > n, ... */
+  MOE_EUNSUPPORTED = -2,  /* valid but not implemented (dtype combination, n > 1024) */
+  MOE_EWORKSPACE = -3,    /* workspace smaller than the *_workspace_bytes query */
+  MOE_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+
+typedef enum {
+  MOE_QB_FROZEN = 0,  /* use the given bias as is (inference: bias frozen) */
+  MOE_QB_BATCH = 1    /* Quantile Balancing on this batch, bias in/out */
+} moe_qb_mode;
+
+/* qb_info[4] (int32, device): rounds of quantile coordinate updates, status
+ * (0 balanced / frozen, 1 not balanced within the limits, 2 bias left the
+ * representable range), max |load - target| at exit, augmenting-path moves. */
+enum { MOE_QB_STATUS_OK = 0, MOE_QB_STATUS_NOT_BALANCED = 1, MOE_QB_STATUS_BIAS_RANGE = 2 };
+
+typedef struct {
+  int32_t T;             /* tokens in the batch (>= 0) */
+  int32_t d;             /* model width (7168 for K3), multiple of 64 */
+  int32_t latent;        /* latent width (d/2 = 3584 for K3), multiple of 64 */
+  int32_t n_experts;     /* routed experts (896), 1..1024 */
+  int32_t top_k;         /* experts per token (16), 1..n_experts */
+  int32_t inter;         /* routed intermediate width m, multiple of 64 */
+  int32_t shared_inter;  /* merged shared-expert intermediate (2 x 3072), multiple of 64 */
+  int32_t act_dtype;     /* MOE_F32 or MOE_BF16: x, out and the dense weights */
+  int32_t routed_dtype;  /* act_dtype, or MOE_MXFP4 with MOE_BF16 activations */
+  float rms_eps;         /* RMSNorm epsilon (1e-6) */
+  int32_t qb_mode;       /* moe_qb_mode */
+  int32_t qb_max_rounds; /* cap on quantile coordinate rounds (<= 0: 64) */
+} moe_shape_t;
+
+typedef struct {
+  const float* w_router;            /* [n][d] f32 */
+  const float* router_logit_offset; /* [n] f32 added to the logits, or NULL */
+  const void* w_down;               /* [latent][d]  act dtype: latent down-projection */
+  const void* w_up;                 /* [d][latent]  act dtype: latent up-projection */
+  const void* w_gate;               /* [n][inter][latent] routed gate (codes if MXFP4) */
+  const void* w_uproj;              /* [n][inter][latent] routed up   (codes if MXFP4) */
+  const void* w_dn;                 /* [n][latent][inter] routed down (codes if MXFP4) */
+  const uint8_t* s_gate;            /* MXFP4 scales [n][inter][latent/32], else NULL */
+  const uint8_t* s_uproj;           /* MXFP4 scales [n][inter][latent/32], else NULL */
+  const uint8_t* s_dn;              /* MXFP4 scales [n][latent][inter/32], else NULL */
+  const float* rms_gamma;           /* [latent] f32 RMSNorm gain */
+  const void* ws_gate;              /* [shared_inter][d] act dtype */
+  const void* ws_up;                /* [shared_inter][d] act dtype */
+  const void* ws_down;              /* [d][shared_inter] act dtype */
+} moe_weights_t;
+
+/* Bytes of device workspace moe_route_qb needs for (T, n, k); 0 on bad input. */
+size_t moe_route_workspace_bytes(int32_t T, int32_t n, int32_t k);
+
+/*
+ * moe_route_qb -- routing of T tokens given their sigmoid scores.
+ *   scores   [T][n] f32 in [0, 1] (read only)
+ *   mode     moe_qb_mode; max_rounds caps the quantile rounds (<= 0: 64)
+ *   bias     [n] f64, in: starting (BATCH) or frozen (FROZEN) bias; out (BATCH):
+ *            the balancing bias, exact multiples of 2^-40, common offset removed
+ *            (sum in [0, n) * 2^-40).  |bias| must stay below 1024.
+ *   topk_idx [T][k] i32: chosen experts by descending raw score, ties to the
+ *            lower expert index
+ *   topk_w   [T][k] f32: chosen raw scores divided by their sum
+ *   loads    [n] i32: tokens per expert; qb_info [4] i32 as described above
+ *   workspace/workspace_bytes: device scratch of at least
+ *            moe_route_workspace_bytes(T, n, k) bytes, 256-byte aligned
+ * Scores and biases are compared exactly on a 2^-40 fixed-point grid; with
+ * QB the chosen sets are the unique balanced optimum, independent of how the
+ * bias was reached.
+ */
+int moe_route_qb(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode,
+                 int32_t max_rounds, double* bias, int32_t* topk_idx, float* topk_w,
+                 int32_t* loads, int32_t* qb_info, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Bytes of device workspace moe_latent_forward needs for this shape; 0 on bad input. */
+size_t moe_forward_workspace_bytes(const moe_shape_t* shape);
+
+/*
+ * moe_latent_forward -- one forward pass of the layer.
+ *   shape, weights : host pointers to the structs above (read during the call)
+ *   x   [T][d] act dtype (read only); out [T][d] act dtype
+ *   bias [n] f64 in/out exactly as for moe_route_qb
+ *   scores_in  [T][n] f32 or NULL: when given, these scores replace the router
+ *              (e.g. scores computed elsewhere); when NULL the router runs
+ *   scores_out [T][n] f32 or NULL: receives the scores used for routing
+ *   topk_idx, topk_w, loads, qb_info: as for moe_route_qb; each may be NULL
+ *   workspace : >= moe_forward_workspace_bytes(shape) bytes, 256-byte aligned
+ */
+int moe_latent_forward(const moe_shape_t* shape, const moe_weights_t* weights, const void* x,
+                       void* out, double* bias, const float* scores_in, float* scores_out,
+                       int32_t* topk_idx, float* topk_w, int32_t* loads, int32_t* qb_info,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a moe_status value; never NULL. */
+const char* moe_status_str(int status);
+
+/*
+ * Stage timing (diagnostics; not a part of the layer's arithmetic).
+ * moe_stage_timing(1) makes later moe_latent_forward / moe_route_qb calls
+ * record a pair of HIP events around each stage on their stream, and clears
+ * the totals; moe_stage_timing(0) stops recording.  After the caller has
+ * synchronised those streams, moe_stage_times writes the summed milliseconds
+ * and the number of timed launches per stage (arrays of max_stages entries,
+ * either may be NULL) and returns the number of stages, or MOE_EHIP if an
+ * event has not completed.  Stages, in order: router, latent_down,
+ * shared_gate_up, routing, permute, routed_gate_up, routed_down,
+ * combine_rmsnorm, up_proj_shared_down; moe_stage_name gives these names
+ * (static strings, "unknown" out of range).  Host-side state, guarded by a
+ * mutex; events are created on first use and reused.
+ */
+int moe_stage_timing(int enable);
+int moe_stage_times(double* total_ms, int32_t* counts, int32_t max_stages);
+const char* moe_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,214 @@
+"""Python binding of the MI355X Stable LatentMoE library (``libmoe_mi355x.so``).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and the current HIP stream are passed to
+the C ABI declared in ``include/moe_mi355x.h``, and every step of the layer
+runs in the library's HIP kernels.  There is no fallback: if the library is
+missing or fails to load, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python sparse_moe_ffn_sigmoid_amd/build.py`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
+MOE_QB_FROZEN, MOE_QB_BATCH = 0, 1
+EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_forward_workspace_bytes",
+            "moe_latent_forward", "moe_status_str", "moe_stage_timing", "moe_stage_times",
+            "moe_stage_name")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("latent", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("routed_dtype", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("qb_mode", ctypes.c_int32),
+                ("qb_max_rounds", ctypes.c_int32)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "w_router", "router_logit_offset", "w_down", "w_up", "w_gate", "w_uproj", "w_dn",
+        "s_gate", "s_uproj", "s_dn", "rms_gamma", "ws_gate", "ws_up", "ws_down")]
+
+
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+_lib.moe_route_workspace_bytes.argtypes = [_i32, _i32, _i32]
+_lib.moe_route_workspace_bytes.restype = _sz
+_lib.moe_route_qb.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _sz, _vp]
+_lib.moe_route_qb.restype = ctypes.c_int
+_lib.moe_forward_workspace_bytes.argtypes = [ctypes.POINTER(MoeShape)]
+_lib.moe_forward_workspace_bytes.restype = _sz
+_lib.moe_latent_forward.argtypes = [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _vp,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_latent_forward.restype = ctypes.c_int
+_lib.moe_status_str.argtypes = [ctypes.c_int]
+_lib.moe_status_str.restype = ctypes.c_char_p
+_lib.moe_stage_timing.argtypes = [ctypes.c_int]
+_lib.moe_stage_timing.restype = ctypes.c_int
+_lib.moe_stage_times.argtypes = [_vp, _vp, _i32]
+_lib.moe_stage_times.restype = ctypes.c_int
+_lib.moe_stage_name.argtypes = [ctypes.c_int]
+_lib.moe_stage_name.restype = ctypes.c_char_p
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_lib.moe_status_str(status).decode()} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def route_workspace_bytes(T: int, n: int, k: int) -> int:
+    return int(_lib.moe_route_workspace_bytes(T, n, k))
+
+
+def route_qb(scores: torch.Tensor, k: int, bias: torch.Tensor | None = None,
+             mode: int = MOE_QB_BATCH, max_rounds: int = 64, workspace=None):
+    """Route fp32 scores [T, n] (device) to k experts per token.
+
+    Returns dict(idx [T,k] int32, w [T,k] fp32, loads [n] int32, bias [n] fp64,
+    info [4] int32) -- info = (quantile rounds, status, max |load-target|,
+    augmenting-path moves).  ``bias`` (fp64 [n]) is the start / frozen bias.
+    """
+    dev = scores.device
+    T, n = scores.shape
+    _check(scores, "scores", torch.float32, (T, n), dev)
+    b = torch.zeros(n, dtype=torch.float64, device=dev) if bias is None else bias.clone()
+    _check(b, "bias", torch.float64, (n,), dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    loads = torch.empty(n, dtype=torch.int32, device=dev)
+    info = torch.zeros(4, dtype=torch.int32, device=dev)
+    need = route_workspace_bytes(T, n, k)
+    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8,
+                                                             device=dev)
+    st = _lib.moe_route_qb(_ptr(scores), T, n, k, mode, max_rounds, _ptr(b), _ptr(idx), _ptr(w),
+                           _ptr(loads), _ptr(info), _ptr(ws), ws.numel(), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_route_qb")
+    return dict(idx=idx, w=w, loads=loads, bias=b, info=info)
+
+
+def make_shape(T, d, latent, n, k, inter, shared_inter, act_dtype, routed_dtype,
+               rms_eps=1e-6, qb_mode=MOE_QB_BATCH, qb_max_rounds=64) -> MoeShape:
+    return MoeShape(T, d, latent, n, k, inter, shared_inter, act_dtype, routed_dtype, rms_eps,
+                    qb_mode, qb_max_rounds)
+
+
+def forward_workspace_bytes(shape: MoeShape) -> int:
+    return int(_lib.moe_forward_workspace_bytes(ctypes.byref(shape)))
+
+
+_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
+
+
+def latent_forward(shape: MoeShape, weights: dict, x: torch.Tensor, bias=None,
+                   scores_in=None, want_scores=False, workspace=None):
+    """One forward pass of the layer.
+
+    ``weights`` holds device tensors keyed as in ``moe_weights_t`` (MXFP4
+    routed weights as uint8 codes plus ``s_gate``/``s_uproj``/``s_dn``).
+    Returns dict(out, idx, w, loads, bias, info[, scores]).
+    """
+    dev = x.device
+    T, d, l, n, k = shape.T, shape.d, shape.latent, shape.n_experts, shape.top_k
+    m, ms = shape.inter, shape.shared_inter
+    adt = _DT[shape.act_dtype]
+    _check(x, "x", adt, (T, d), dev)
+    _check(weights["w_router"], "w_router", torch.float32, (n, d), dev)
+    if weights.get("router_logit_offset") is not None:
+        _check(weights["router_logit_offset"], "router_logit_offset", torch.float32, (n,), dev)
+    _check(weights["w_down"], "w_down", adt, (l, d), dev)
+    _check(weights["w_up"], "w_up", adt, (d, l), dev)
+    if shape.routed_dtype == MOE_MXFP4:
+        for nm, sn, rows, K in (("w_gate", "s_gate", m, l), ("w_uproj", "s_uproj", m, l),
+                                ("w_dn", "s_dn", l, m)):
+            _check(weights[nm], nm, torch.uint8, (n, rows, K // 2), dev)
+            _check(weights[sn], sn, torch.uint8, (n, rows, K // 32), dev)
+    else:
+        rdt = _DT[shape.routed_dtype]
+        _check(weights["w_gate"], "w_gate", rdt, (n, m, l), dev)
+        _check(weights["w_uproj"], "w_uproj", rdt, (n, m, l), dev)
+        _check(weights["w_dn"], "w_dn", rdt, (n, l, m), dev)
+    _check(weights["rms_gamma"], "rms_gamma", torch.float32, (l,), dev)
+    _check(weights["ws_gate"], "ws_gate", adt, (ms, d), dev)
+    _check(weights["ws_up"], "ws_up", adt, (ms, d), dev)
+    _check(weights["ws_down"], "ws_down", adt, (d, ms), dev)
+    if scores_in is not None:
+        _check(scores_in, "scores_in", torch.float32, (T, n), dev)
+    wts = MoeWeights(*[None if weights.get(f) is None else weights[f].data_ptr()
+                       for f, _ in MoeWeights._fields_])
+    out = torch.empty((T, d), dtype=adt, device=dev)
+    b = torch.zeros(n, dtype=torch.float64, device=dev) if bias is None else bias.clone()
+    _check(b, "bias", torch.float64, (n,), dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    loads = torch.empty(n, dtype=torch.int32, device=dev)
+    info = torch.zeros(4, dtype=torch.int32, device=dev)
+    scores = torch.empty((T, n), dtype=torch.float32, device=dev) if want_scores else None
+    need = forward_workspace_bytes(shape)
+    if need == 0:
+        raise MoeError(-1, "moe_forward_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _lib.moe_latent_forward(ctypes.byref(shape), ctypes.byref(wts), _ptr(x), _ptr(out),
+                                 _ptr(b), _ptr(scores_in), _ptr(scores), _ptr(idx), _ptr(w),
+                                 _ptr(loads), _ptr(info), _ptr(ws), ws.numel(), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_latent_forward")
+    res = dict(out=out, idx=idx, w=w, loads=loads, bias=b, info=info)
+    if want_scores:
+        res["scores"] = scores
+    return res
+
+
+def stage_timing(enable: bool) -> None:
+    """Start (and reset) or stop per-stage HIP-event timing in the library."""
+    _lib.moe_stage_timing(1 if enable else 0)
+
+
+def stage_times() -> dict:
+    """{stage name: (total ms, launches)} since the last stage_timing(True);
+    synchronise the streams first."""
+    tot = (ctypes.c_double * 16)()
+    cnt = (ctypes.c_int32 * 16)()
+    n = _lib.moe_stage_times(ctypes.cast(tot, ctypes.c_void_p), ctypes.cast(cnt, ctypes.c_void_p), 16)
+    if n < 0:
+        raise MoeError(n, "moe_stage_times")
+    return {_lib.moe_stage_name(i).decode(): (tot[i], cnt[i]) for i in range(n)}

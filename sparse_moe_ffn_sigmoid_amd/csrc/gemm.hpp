@@ -1,0 +1,53 @@
+// GEMM interfaces of the latent MoE layer: C = epilogue(sum_s A_s B_s^T).
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+namespace gemm {
+
+enum Epilogue : int {
+  EPI_BF16 = 0,     // C (bf16) = acc
+  EPI_F32 = 1,      // C (f32)  = acc
+  EPI_SIGMOID = 2,  // C (f32)  = sigmoid(acc + col_add[col])
+  EPI_SITU = 3,     // C (act)  = SiTU-GLU(acc_gate, acc_up); B rows come in gate/up pairs
+};
+
+enum BFormat : int { B_DENSE = 0, B_MXFP4 = 1 };
+
+// One K segment: A [rows][K] (K contiguous, leading dim lda), B [N][K] (ldb).
+struct Seg {
+  const void* A;
+  int64_t lda;
+  const void* B;   // dense: element type of the GEMM; MXFP4: codes [N][K/2]
+  const void* B2;  // EPI_SITU: the "up" matrix paired with B (the gate matrix)
+  const uint8_t* Bs;   // MXFP4 scales [N][K/32] for B
+  const uint8_t* Bs2;  // MXFP4 scales for B2
+  int64_t ldb;         // elements (dense) or bytes (MXFP4 codes)
+  int K;
+};
+
+struct Params {
+  int M;             // rows (dense problems)
+  int N;             // output columns
+  int nseg;
+  Seg seg[3];
+  // Grouped problems: per-expert base offsets of B and its scales, the tile
+  // list and the gather map from output slot to A row.
+  int64_t b_expert_stride;   // elements / code bytes between experts
+  int64_t bs_expert_stride;  // scale bytes between experts
+  const int32_t* tiles;      // [max_tiles][4] = (expert, row0, rows, -) or null (dense)
+  const int32_t* ntiles;     // device count of tiles
+  int max_mtiles;            // grid bound on M tiles
+  const int32_t* a_rows;     // slot -> A row (null: identity)
+  void* C;
+  int64_t ldc;
+  const float* col_add;      // EPI_SIGMOID: per-column logit offset or null
+};
+
+// Launch helpers (defined in gemm.hip).  `act_bf16` selects the bf16 MFMA
+// kernels, otherwise the fp32 kernels run.
+int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipStream_t stream);
+
+}  // namespace gemm
+}  // namespace moe

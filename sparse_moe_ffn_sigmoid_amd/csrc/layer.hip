@@ -1,0 +1,448 @@
+// Forward pass of the Stable LatentMoE layer: router -> QB routing ->
+// token permutation -> latent down-projection and shared gate/up ->
+// routed gate/up with SiTU-GLU -> routed down -> weighted combine + RMSNorm
+// -> up-projection fused with the shared down-projection.
+//
+// Sources: "Kimi K3 — LatentMoE" (dimsnsums.com), section "Why does the
+// router need three moves?" (latent space of half the width, RMSNorm on the
+// combined routed signal, SiTU-GLU); xhh.club "Kimi K3 模型结构（5）：宽度维度，
+// Stable LatentMoE", Q&A on routing, SiTU-GLU, RMSNorm placement (after the
+// latent aggregation, before the up-projection) and the shared expert (two
+// experts merged into one MLP of width 6144 at full width, added to the
+// routed output).
+#include "common.hpp"
+#include "gemm.hpp"
+#include "prof.hpp"
+#include "route.hpp"
+
+namespace moe {
+
+
+namespace layer {
+
+// Exact split of an fp32 matrix into three bf16 matrices, w = hi + mid + lo
+// (each step rounds to nearest even and carries the exact fp32 remainder).
+__global__ void split3(const float* __restrict__ w, bf16_t* hi, bf16_t* mid, bf16_t* lo,
+                       int64_t count) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const float v = w[i];
+    const bf16_t h = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(h);
+    const bf16_t m = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(m);
+    hi[i] = h;
+    mid[i] = m;
+    lo[i] = f32_to_bf16(r2);
+  }
+}
+
+__global__ void copy_f32(const float* __restrict__ in, float* __restrict__ out, int64_t count) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    out[i] = in[i];
+}
+
+__global__ void fill_u32(uint32_t* p, uint32_t v, int64_t count) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+// offs = exclusive scan of loads; grouped tile list for tile height bm.
+__global__ __launch_bounds__(1024) void scan_and_tiles(const int32_t* loads, int n, int bm,
+                                                       int32_t* offs, int32_t* tiles,
+                                                       int32_t* ntiles) {
+  __shared__ int32_t s_l[1024], s_t[1024];
+  const int e = threadIdx.x;
+  const int32_t L = e < n ? loads[e] : 0;
+  const int32_t nt = (L + bm - 1) / bm;
+  s_l[e] = L;
+  s_t[e] = nt;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int32_t a = e >= off ? s_l[e - off] : 0;
+    const int32_t b = e >= off ? s_t[e - off] : 0;
+    __syncthreads();
+    s_l[e] += a;
+    s_t[e] += b;
+    __syncthreads();
+  }
+  const int32_t lo = s_l[e] - L, to = s_t[e] - nt;
+  if (e < n) {
+    offs[e] = lo;
+    for (int i = 0; i < nt; ++i) {
+      int32_t* q = tiles + 4 * (to + i);
+      q[0] = e;
+      q[1] = lo + i * bm;
+      q[2] = min(bm, L - i * bm);
+      q[3] = 0;
+    }
+  }
+  if (e == n - 1) {
+    offs[n] = s_l[e];
+    *ntiles = s_t[e];
+  }
+}
+
+// sel[e][t] = j + 1 when token t chose expert e as its j-th expert.
+__global__ void scatter_sel(const int32_t* idx, int T, int k, uint8_t* sel) {
+  const int64_t total = static_cast<int64_t>(T) * k;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = i / k;
+    const int j = static_cast<int>(i - t * k);
+    sel[static_cast<int64_t>(idx[i]) * T + t] = static_cast<uint8_t>(j + 1);
+  }
+}
+
+// One block per expert: the tokens that chose e, in increasing token order,
+// take the slots offs[e], offs[e]+1, ...: perm[slot] = token, inv[t][j] = slot.
+__global__ __launch_bounds__(256) void expert_slots(const uint8_t* sel, int T, int k,
+                                                    const int32_t* offs, int32_t* perm,
+                                                    int32_t* inv) {
+  __shared__ int32_t s_wave[4];
+  __shared__ int32_t s_base;
+  const int e = blockIdx.x;
+  const uint8_t* row = sel + static_cast<int64_t>(e) * T;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (threadIdx.x == 0) s_base = offs[e];
+  __syncthreads();
+  for (int t0 = 0; t0 < T; t0 += 256) {
+    const int t = t0 + threadIdx.x;
+    const int j = t < T ? row[t] : 0;
+    const uint64_t bal = __ballot(j != 0);
+    const int before = __popcll(bal & ((uint64_t(1) << lane) - 1));
+    if (lane == 0) s_wave[wv] = __popcll(bal);
+    __syncthreads();
+    int wbase = s_base;
+    for (int w = 0; w < wv; ++w) wbase += s_wave[w];
+    if (j != 0) {
+      const int slot = wbase + before;
+      perm[slot] = t;
+      inv[static_cast<int64_t>(t) * k + (j - 1)] = slot;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) s_base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    __syncthreads();
+  }
+}
+
+// y_t = sum_j w[t][j] * yp[inv[t][j]] in fp32 (j ascending), then
+// RMSNorm: y * rsqrt(mean(y^2) + eps) * gamma.  One block per token.
+template <typename ACT>
+__global__ __launch_bounds__(256) void combine_rmsnorm(const ACT* __restrict__ yp,
+                                                       const int32_t* __restrict__ inv,
+                                                       const float* __restrict__ w,
+                                                       const float* __restrict__ gamma, int k,
+                                                       int L, float eps, ACT* __restrict__ out) {
+  constexpr int MAXV = 16;  // L <= 256 * MAXV
+  __shared__ float s_red[256];
+  const int t = blockIdx.x;
+  float acc[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[static_cast<int64_t>(t) * k + j];
+    const ACT* src = yp + static_cast<int64_t>(inv[static_cast<int64_t>(t) * k + j]) * L;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      if (c < L) acc[i] = fmaf(wj, to_f32<ACT>(src[c]), acc[i]);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) ss = fmaf(acc[i], acc[i], ss);
+  s_red[threadIdx.x] = ss;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) s_red[threadIdx.x] += s_red[threadIdx.x + s];
+    __syncthreads();
+  }
+  const float scale = rsqrtf(s_red[0] / static_cast<float>(L) + eps);
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < L) out[static_cast<int64_t>(t) * L + c] = from_f32<ACT>(acc[i] * scale * gamma[c]);
+  }
+}
+
+struct ForwardWorkspace {
+  RouteWorkspace route;
+  float* scores;
+  int32_t* idx;
+  float* w;
+  int32_t* loads;
+  int32_t* info;
+  bf16_t* wsplit;     // [3][n][d] (bf16 activations)
+  void* z;            // [T][latent]
+  void* hs;           // [T][shared]
+  int32_t* offs;      // [n+1]
+  int32_t* tiles;     // [max_mtiles][4]
+  int32_t* ntiles;
+  uint8_t* sel;       // [n][T]
+  int32_t* perm;      // [T*k]
+  int32_t* inv;       // [T*k]
+  void* h;            // [T*k][inter]
+  void* yp;           // [T*k][latent]
+  void* yhat;         // [T][latent]
+  int bm;
+  int max_mtiles;
+};
+
+static int grouped_bm(const moe_shape_t& s) {
+  const int64_t avg = (static_cast<int64_t>(s.T) * s.top_k + s.n_experts - 1) / s.n_experts;
+  return (s.act_dtype == MOE_BF16 && avg <= 32) ? 32 : (s.act_dtype == MOE_BF16 ? 128 : 64);
+}
+
+static size_t forward_layout(const moe_shape_t& s, ForwardWorkspace* fw, void* base) {
+  Carver cv(base);
+  ForwardWorkspace f{};
+  const size_t es = s.act_dtype == MOE_BF16 ? 2 : 4;
+  const int64_t T = s.T, n = s.n_experts, k = s.top_k;
+  // the routing workspace is carved first, at offset 0
+  const size_t rb = route_workspace_layout(s.T, s.n_experts, &f.route, base);
+  cv.off = rb;
+  f.scores = cv.take<float>(T * n);
+  f.idx = cv.take<int32_t>(T * k);
+  f.w = cv.take<float>(T * k);
+  f.loads = cv.take<int32_t>(n);
+  f.info = cv.take<int32_t>(4);
+  f.wsplit = cv.take<bf16_t>(s.act_dtype == MOE_BF16 ? 3 * n * s.d : 0);
+  f.z = cv.take<char>(T * s.latent * es);
+  f.hs = cv.take<char>(T * s.shared_inter * es);
+  f.bm = grouped_bm(s);
+  f.max_mtiles = static_cast<int>((T * k + f.bm - 1) / f.bm + n);
+  f.offs = cv.take<int32_t>(n + 1);
+  f.tiles = cv.take<int32_t>(4 * static_cast<size_t>(f.max_mtiles));
+  f.ntiles = cv.take<int32_t>(1);
+  f.sel = cv.take<uint8_t>(align_up(static_cast<size_t>(n * T), 4));
+  f.perm = cv.take<int32_t>(T * k);
+  f.inv = cv.take<int32_t>(T * k);
+  f.h = cv.take<char>(T * k * s.inter * es);
+  f.yp = cv.take<char>(T * k * s.latent * es);
+  f.yhat = cv.take<char>(T * s.latent * es);
+  if (fw) *fw = f;
+  return cv.bytes();
+}
+
+static int validate(const moe_shape_t* sp, const moe_weights_t* w) {
+  if (!sp) return MOE_EINVAL;
+  const moe_shape_t& s = *sp;
+  int st = route_validate(s.T, s.n_experts, s.top_k);
+  if (st != MOE_OK) return st;
+  if (s.d <= 0 || s.latent <= 0 || s.inter <= 0 || s.shared_inter <= 0) return MOE_EINVAL;
+  if (s.d % 64 || s.latent % 64 || s.inter % 64 || s.shared_inter % 64) return MOE_EUNSUPPORTED;
+  if (s.latent > 256 * 16) return MOE_EUNSUPPORTED;
+  if (s.act_dtype != MOE_F32 && s.act_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (!(s.routed_dtype == s.act_dtype || (s.routed_dtype == MOE_MXFP4 && s.act_dtype == MOE_BF16)))
+    return MOE_EUNSUPPORTED;
+  if (s.qb_mode != MOE_QB_BATCH && s.qb_mode != MOE_QB_FROZEN) return MOE_EINVAL;
+  if (!(s.rms_eps >= 0.f)) return MOE_EINVAL;
+  if (w) {
+    if (!w->w_router || !w->w_down || !w->w_up || !w->w_gate || !w->w_uproj || !w->w_dn ||
+        !w->rms_gamma || !w->ws_gate || !w->ws_up || !w->ws_down)
+      return MOE_EINVAL;
+    if (s.routed_dtype == MOE_MXFP4 && (!w->s_gate || !w->s_uproj || !w->s_dn)) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+static gemm::Seg seg(const void* A, int64_t lda, const void* B, int64_t ldb, int K) {
+  gemm::Seg g{};
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.K = K;
+  return g;
+}
+
+static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x, void* out,
+                   double* bias, const float* scores_in, float* scores_out, int32_t* idx_out,
+                   float* w_out, int32_t* loads_out, int32_t* info_out,
+                   const ForwardWorkspace& f, hipStream_t st) {
+  const bool bf = s.act_dtype == MOE_BF16;
+  const int T = s.T, n = s.n_experts, k = s.top_k, d = s.d, L = s.latent, m = s.inter,
+            ms = s.shared_inter;
+  const int store_epi = bf ? gemm::EPI_BF16 : gemm::EPI_F32;
+  const int64_t es = bf ? 2 : 4;
+  int rc;
+  float* scores = scores_out ? scores_out : f.scores;
+  int32_t* idx = idx_out ? idx_out : f.idx;
+  float* w = w_out ? w_out : f.w;
+  int32_t* info = info_out ? info_out : f.info;
+
+  // 1. router: s = sigmoid(x W_r^T + p)
+  {
+  prof::Scope sc(prof::ST_ROUTER, st);
+  if (scores_in) {
+    if (scores_out && T > 0)
+      hipLaunchKernelGGL(copy_f32, dim3(1024), dim3(256), 0, st, scores_in, scores_out,
+                         static_cast<int64_t>(T) * n);
+  } else if (T > 0) {
+    gemm::Params p{};
+    p.M = T;
+    p.N = n;
+    p.C = scores;
+    p.ldc = n;
+    p.col_add = wt.router_logit_offset;
+    if (bf) {
+      const int64_t cnt = static_cast<int64_t>(n) * d;
+      bf16_t* hi = f.wsplit;
+      hipLaunchKernelGGL(split3, dim3(2048), dim3(256), 0, st, wt.w_router, hi, hi + cnt,
+                         hi + 2 * cnt, cnt);
+      p.nseg = 3;
+      for (int q = 0; q < 3; ++q) p.seg[q] = seg(x, d, hi + q * cnt, d, d);
+    } else {
+      p.nseg = 1;
+      p.seg[0] = seg(x, d, wt.w_router, d, d);
+    }
+    if ((rc = gemm::launch(p, gemm::EPI_SIGMOID, gemm::B_DENSE, bf, 128, st)) != MOE_OK) return rc;
+  }
+  }
+  const float* route_scores = scores_in ? scores_in : scores;
+
+  // 2. shared branch (independent of routing): z = x W_down^T, hs = SiTU(x Wgs^T, x Wus^T)
+  if (T > 0) {
+    gemm::Params p{};
+    p.M = T;
+    p.N = L;
+    p.nseg = 1;
+    p.seg[0] = seg(x, d, wt.w_down, d, d);
+    p.C = f.z;
+    p.ldc = L;
+    {
+      prof::Scope sc(prof::ST_LATENT_DOWN, st);
+      if ((rc = gemm::launch(p, store_epi, gemm::B_DENSE, bf, 128, st)) != MOE_OK) return rc;
+    }
+    gemm::Params q{};
+    q.M = T;
+    q.N = ms;
+    q.nseg = 1;
+    q.seg[0] = seg(x, d, wt.ws_gate, d, d);
+    q.seg[0].B2 = wt.ws_up;
+    q.C = f.hs;
+    q.ldc = ms;
+    prof::Scope sc(prof::ST_SHARED_GATE_UP, st);
+    if ((rc = gemm::launch(q, gemm::EPI_SITU, gemm::B_DENSE, bf, 128, st)) != MOE_OK) return rc;
+  }
+
+  // 3. routing (QB or frozen bias)
+  {
+  prof::Scope sc(prof::ST_ROUTING, st);
+  if ((rc = route_run(route_scores, T, n, k, s.qb_mode, s.qb_max_rounds, bias, idx, w, f.loads,
+                      info, f.route, st)) != MOE_OK)
+    return rc;
+  }
+  if (loads_out)
+    MOE_HIP_CHECK(hipMemcpyAsync(loads_out, f.loads, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, st));
+  if (T == 0) return MOE_OK;
+
+  // 4. permutation: slots grouped by expert, tokens ascending inside a group
+  {
+  prof::Scope sc(prof::ST_PERMUTE, st);
+  hipLaunchKernelGGL(scan_and_tiles, dim3(1), dim3(1024), 0, st, f.loads, n, f.bm, f.offs,
+                     f.tiles, f.ntiles);
+  const int64_t selw = static_cast<int64_t>(align_up(static_cast<size_t>(n) * T, 4) / 4);
+  hipLaunchKernelGGL(fill_u32, dim3(1024), dim3(256), 0, st, reinterpret_cast<uint32_t*>(f.sel),
+                     0u, selw);
+  hipLaunchKernelGGL(scatter_sel, dim3(1024), dim3(256), 0, st, idx, T, k, f.sel);
+  hipLaunchKernelGGL(expert_slots, dim3(n), dim3(256), 0, st, f.sel, T, k, f.offs, f.perm, f.inv);
+  MOE_LAUNCH_CHECK();
+  }
+
+  const bool mx = s.routed_dtype == MOE_MXFP4;
+  const int bfmt = mx ? gemm::B_MXFP4 : gemm::B_DENSE;
+  // 5. routed gate/up with SiTU-GLU: h[slot] = SiTU(z[perm[slot]] Wg_e^T, z[perm[slot]] Wu_e^T)
+  {
+    gemm::Params p{};
+    p.N = m;
+    p.nseg = 1;
+    p.seg[0] = seg(f.z, L, wt.w_gate, mx ? L / 2 : L, L);
+    p.seg[0].B2 = wt.w_uproj;
+    p.seg[0].Bs = wt.s_gate;
+    p.seg[0].Bs2 = wt.s_uproj;
+    p.b_expert_stride = mx ? static_cast<int64_t>(m) * L / 2 : static_cast<int64_t>(m) * L;
+    p.bs_expert_stride = static_cast<int64_t>(m) * L / 32;
+    p.tiles = f.tiles;
+    p.ntiles = f.ntiles;
+    p.max_mtiles = f.max_mtiles;
+    p.a_rows = f.perm;
+    p.C = f.h;
+    p.ldc = m;
+    prof::Scope sc(prof::ST_ROUTED_GATE_UP, st);
+    if ((rc = gemm::launch(p, gemm::EPI_SITU, bfmt, bf, f.bm, st)) != MOE_OK) return rc;
+  }
+  // 6. routed down: yp[slot] = h[slot] Wd_e^T
+  {
+    gemm::Params p{};
+    p.N = L;
+    p.nseg = 1;
+    p.seg[0] = seg(f.h, m, wt.w_dn, mx ? m / 2 : m, m);
+    p.seg[0].Bs = wt.s_dn;
+    p.b_expert_stride = mx ? static_cast<int64_t>(L) * m / 2 : static_cast<int64_t>(L) * m;
+    p.bs_expert_stride = static_cast<int64_t>(L) * m / 32;
+    p.tiles = f.tiles;
+    p.ntiles = f.ntiles;
+    p.max_mtiles = f.max_mtiles;
+    p.C = f.yp;
+    p.ldc = L;
+    prof::Scope sc(prof::ST_ROUTED_DOWN, st);
+    if ((rc = gemm::launch(p, store_epi, bfmt, bf, f.bm, st)) != MOE_OK) return rc;
+  }
+  // 7. weighted combine in the latent space + RMSNorm
+  {
+  prof::Scope sc(prof::ST_COMBINE_RMSNORM, st);
+  if (bf)
+    hipLaunchKernelGGL(combine_rmsnorm<bf16_t>, dim3(T), dim3(256), 0, st,
+                       static_cast<const bf16_t*>(f.yp), f.inv, w, wt.rms_gamma, k, L, s.rms_eps,
+                       static_cast<bf16_t*>(f.yhat));
+  else
+    hipLaunchKernelGGL(combine_rmsnorm<float>, dim3(T), dim3(256), 0, st,
+                       static_cast<const float*>(f.yp), f.inv, w, wt.rms_gamma, k, L, s.rms_eps,
+                       static_cast<float*>(f.yhat));
+  MOE_LAUNCH_CHECK();
+  }
+  // 8. out = yhat W_up^T + hs Ws_down^T (one GEMM, K concatenated)
+  {
+    gemm::Params p{};
+    p.M = T;
+    p.N = d;
+    p.nseg = 2;
+    p.seg[0] = seg(f.yhat, L, wt.w_up, L, L);
+    p.seg[1] = seg(f.hs, ms, wt.ws_down, ms, ms);
+    p.C = out;
+    p.ldc = d;
+    prof::Scope sc(prof::ST_UP_SHARED_DOWN, st);
+    if ((rc = gemm::launch(p, store_epi, gemm::B_DENSE, bf, 128, st)) != MOE_OK) return rc;
+  }
+  (void)es;
+  return MOE_OK;
+}
+
+}  // namespace layer
+}  // namespace moe
+
+extern "C" size_t moe_forward_workspace_bytes(const moe_shape_t* shape) {
+  if (moe::layer::validate(shape, nullptr) != MOE_OK) return 0;
+  return moe::layer::forward_layout(*shape, nullptr, nullptr);
+}
+
+extern "C" int moe_latent_forward(const moe_shape_t* shape, const moe_weights_t* weights,
+                                  const void* x, void* out, double* bias, const float* scores_in,
+                                  float* scores_out, int32_t* topk_idx, float* topk_w,
+                                  int32_t* loads, int32_t* qb_info, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  int st = moe::layer::validate(shape, weights);
+  if (st != MOE_OK) return st;
+  if (!weights || !bias || !workspace) return MOE_EINVAL;
+  if (shape->T > 0 && (!x || !out)) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MOE_EINVAL;
+  moe::layer::ForwardWorkspace fw;
+  const size_t need = moe::layer::forward_layout(*shape, &fw, workspace);
+  if (workspace_bytes < need) return MOE_EWORKSPACE;
+  return moe::layer::forward(*shape, *weights, x, out, bias, scores_in, scores_out, topk_idx,
+                             topk_w, loads, qb_info, fw, static_cast<hipStream_t>(stream));
+}

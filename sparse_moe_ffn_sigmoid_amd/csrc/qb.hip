@@ -1,0 +1,849 @@
+// Quantile Balancing routing on gfx950.
+//
+// Routing rule (xhh.club "Kimi K3 模型结构（5）：宽度维度，Stable LatentMoE",
+// Q&A on routing): top-k of the biased sigmoid scores, mixture weights = the
+// chosen raw scores renormalised.  Balancing rule (same page, Q&A on
+// Quantile Balancing and 延伸解读 "Quantile Balancing与DeepSeek-V3路由的异同"):
+// each unbalanced expert's bias jumps to minus the (1 - C_e/T) quantile of
+// its margin -- the exact coordinate minimiser of the dual of the balanced
+// assignment problem -- and a common offset is removed at the end.
+//
+// Arithmetic is exact: scores and biases live on a 2^-40 fixed-point grid in
+// int64 and every comparison uses the packed key
+//     ((sfx + bias + 2^51) << 10) | (1023 - e),
+// so "higher biased score first, ties to the lower expert index".
+//
+// Coordinate rounds alone stall with a few experts off by one (the dual is
+// piecewise linear), so once the count of unbalanced experts stops reaching
+// new minima the balance is completed by shortest augmenting paths on the
+// same dual: Bellman-Ford over experts on a sparse edge list holding every
+// (token, chosen A, unchosen B) whose reduced cost is at most Delta; the
+// distances up to D* are exact whenever D* <= Delta, otherwise Delta grows.
+//
+// Control flow lives on the device: a step is [top-k pass, status, quantile
+// round, finish] and every kernel reads the phase word first, so the host
+// only launches batches of steps and polls the phase.
+#include "prof.hpp"
+#include "route.hpp"
+
+namespace moe {
+namespace qb {
+
+constexpr int FRAC_BITS = 40;
+constexpr int IDX_BITS = 10;
+constexpr int64_t KEY_OFFSET = int64_t(1) << 51;
+constexpr int64_t BIAS_LIMIT = int64_t(1) << 50;
+constexpr int64_t DIST_INF = int64_t(1) << 52;
+constexpr uint64_t PACKED_INF = uint64_t(DIST_INF) << IDX_BITS;
+constexpr int MAX_NJ = 16;            // keys per lane: n <= 1024
+constexpr int TOPK_BLOCK = 256;       // 4 waves, one token per wave at a time
+constexpr int TOPK_GRID_MAX = 512;
+constexpr int MAX_K = 64;
+constexpr int STALL_ROUNDS = 3;
+constexpr int MAX_SAP_MOVES = 4096;
+constexpr int EDGE_LIST_MAX = 64;     // per token: low chosen / high unchosen candidates
+constexpr int64_t DELTA_START = int64_t(1) << 30;
+constexpr int64_t DELTA_MAX = int64_t(1) << 44;
+constexpr int64_t DELTA_MIN = int64_t(1) << 16;
+
+enum Phase : int64_t { PH_ROUNDS = 0, PH_SAP = 1, PH_DONE = 2, PH_FAILED = 3, PH_FROZEN = 4 };
+enum Ctrl {
+  C_PHASE = 0, C_ROUNDS, C_BEST, C_SINCE, C_MOVES, C_IMB, C_RESID, C_STATUS, C_DELTA,
+  C_EDGES_VALID, C_CUR, C_SELECT_RAN, C_MAX_ROUNDS, C_LAST_D, C_LAST_HOPS, C_BF_PASSES,
+  C_COUNT = 32
+};
+enum Cnt { N_EDGES = 0, N_OVERFLOW, N_BIASRANGE, N_COUNT = 8 };
+
+__host__ __device__ __forceinline__ int64_t target(int64_t T, int64_t n, int64_t k, int64_t e) {
+  return (T * k) / n + (e < (T * k) % n ? 1 : 0);
+}
+
+__device__ __forceinline__ int64_t score_fixed(float s) {
+  return static_cast<int64_t>(rint(static_cast<double>(s) * 1099511627776.0));  // * 2^40
+}
+
+__device__ __forceinline__ uint64_t pack_key(int64_t sfx, int64_t b, int e) {
+  return (static_cast<uint64_t>(sfx + b + KEY_OFFSET) << IDX_BITS) |
+         static_cast<uint64_t>(1023 - e);
+}
+
+// floor((a + b) / 2^11) without overflowing int64.
+__device__ __forceinline__ int64_t floor_mid(int64_t a, int64_t b) {
+  return (a >> 11) + (b >> 11) + (((a & 2047) + (b & 2047)) >> 11);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+struct Args {
+  const float* scores;   // [T][n]
+  const float* scoresT;  // [n][T]
+  int T, n, k;
+  int64_t* bfx;          // [2][n] biases, ctrl[C_CUR] selects the live half
+  int64_t* th_k;         // [T]
+  int64_t* th_k1;        // [T]
+  int32_t* part_loads;   // [grid][n]
+  int32_t* loads;        // [n]
+  int64_t* ctrl;         // [C_COUNT]
+  int32_t* cnt;          // [N_COUNT]
+  uint64_t* edges;       // [edge_cap]
+  int32_t edge_cap;
+  int32_t* idx;          // [T][k] or null
+  float* w;              // [T][k] or null
+  int topk_grid;
+};
+
+// ---------------------------------------------------------------------------
+// Top-k pass: one wave per token.  Finds the k-th and (k+1)-th keys by k+1
+// rounds of wave-wide max extraction, counts loads per block, and (by flag)
+// writes the ordered outputs or the sparse edges of the augmenting-path phase.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
+  const int64_t phase = a.ctrl[C_PHASE];
+  if (phase == PH_DONE || phase == PH_FAILED) {
+    if (!emit_out) return;
+  }
+  const bool emit_edges = (phase == PH_SAP) && !emit_out;
+  extern __shared__ unsigned char smem_raw[];
+  int32_t* sload = reinterpret_cast<int32_t*>(smem_raw);                 // [n]
+  int64_t* lowKp = reinterpret_cast<int64_t*>(sload + 1024);             // [4][64]
+  int64_t* highKp = lowKp + 4 * EDGE_LIST_MAX;                           // [4][64]
+  int32_t* lowE = reinterpret_cast<int32_t*>(highKp + 4 * EDGE_LIST_MAX);  // [4][64]
+  int32_t* highE = lowE + 4 * EDGE_LIST_MAX;                             // [4][64]
+  int32_t* nList = highE + 4 * EDGE_LIST_MAX;                            // [4][2]
+  int64_t* oSfx = reinterpret_cast<int64_t*>(nList + 8);                 // [4][64]
+  float* oS = reinterpret_cast<float*>(oSfx + 4 * MAX_K);                // [4][64]
+  int32_t* oE = reinterpret_cast<int32_t*>(oS + 4 * MAX_K);              // [4][64]
+  float* oSorted = reinterpret_cast<float*>(oE + 4 * MAX_K);             // [4][64]
+
+  const int n = a.n, k = a.k, T = a.T;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) sload[e] = 0;
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nj = (n + 63) >> 6;
+  const int64_t* bias = a.bfx + (a.ctrl[C_CUR] & 1) * n;
+  const int64_t delta = a.ctrl[C_DELTA];
+  const int rounds = (k < n) ? k + 1 : k;
+
+  for (int t = blockIdx.x * 4 + wv; t < T; t += gridDim.x * 4) {
+    const float* row = a.scores + static_cast<size_t>(t) * n;
+    uint64_t key[MAX_NJ];
+    int64_t sfx[MAX_NJ];
+#pragma unroll
+    for (int j = 0; j < MAX_NJ; ++j) {
+      const int e = lane + 64 * j;
+      key[j] = 0;
+      sfx[j] = 0;
+      if (j < nj && e < n) {
+        sfx[j] = score_fixed(row[e]);
+        key[j] = pack_key(sfx[j], bias[e], e);
+      }
+    }
+    uint32_t taken = 0;
+    uint64_t thk = 0, thk1 = 0;
+    for (int r = 0; r < rounds; ++r) {
+      uint64_t lm = 0;
+#pragma unroll
+      for (int j = 0; j < MAX_NJ; ++j)
+        if (!((taken >> j) & 1u) && key[j] > lm) lm = key[j];
+      const uint64_t wm = wave_max_u64(lm);
+#pragma unroll
+      for (int j = 0; j < MAX_NJ; ++j)
+        if (key[j] == wm) taken |= 1u << j;
+      if (r == k - 1) thk = wm;
+      if (r == k) thk1 = wm;
+    }
+    if (lane == 0) {
+      a.th_k[t] = static_cast<int64_t>(thk);
+      a.th_k1[t] = static_cast<int64_t>(thk1);
+    }
+    uint32_t selmask = 0;
+#pragma unroll
+    for (int j = 0; j < MAX_NJ; ++j)
+      if (key[j] != 0 && key[j] >= thk) {
+        selmask |= 1u << j;
+        atomicAdd(&sload[lane + 64 * j], 1);
+      }
+
+    if (emit_out) {
+      // gather the k chosen (sfx, s, e) into this wave's LDS slots
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < MAX_NJ; ++j) {
+        const bool sel = (selmask >> j) & 1u;
+        const uint64_t bal = __ballot(sel);
+        if (sel) {
+          const int pos = base + __popcll(bal & ((uint64_t(1) << lane) - 1));
+          const int e = lane + 64 * j;
+          oSfx[wv * MAX_K + pos] = sfx[j];
+          oS[wv * MAX_K + pos] = row[e];
+          oE[wv * MAX_K + pos] = e;
+        }
+        base += __popcll(bal);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      int rank = 0;
+      int64_t my_sfx = 0;
+      int my_e = 0;
+      float my_s = 0.f;
+      if (lane < k) {
+        my_sfx = oSfx[wv * MAX_K + lane];
+        my_e = oE[wv * MAX_K + lane];
+        my_s = oS[wv * MAX_K + lane];
+        for (int i = 0; i < k; ++i) {
+          const int64_t si = oSfx[wv * MAX_K + i];
+          const int ei = oE[wv * MAX_K + i];
+          rank += (si > my_sfx) || (si == my_sfx && ei < my_e);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (lane < k) oSorted[wv * MAX_K + rank] = my_s;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      if (lane < k) {
+        float sum = 0.f;
+        for (int i = 0; i < k; ++i) sum += oSorted[wv * MAX_K + i];
+        a.idx[static_cast<size_t>(t) * k + rank] = my_e;
+        a.w[static_cast<size_t>(t) * k + rank] = my_s / sum;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    if (emit_edges) {
+      // reduced cost rho_t(A,B) = Kp_A - Kp_B - [A > B] with Kp = sfx + bias
+      const int64_t kpk = static_cast<int64_t>(thk >> IDX_BITS) - KEY_OFFSET;
+      const int64_t kpk1 = (k < n) ? static_cast<int64_t>(thk1 >> IDX_BITS) - KEY_OFFSET : 0;
+      if (k < n && kpk - kpk1 <= delta + 1) {
+        int nlow = 0, nhigh = 0;
+#pragma unroll
+        for (int j = 0; j < MAX_NJ; ++j) {
+          const int e = lane + 64 * j;
+          const bool valid = key[j] != 0;
+          const int64_t kp = sfx[j] + (valid ? bias[e] : 0);
+          const bool sel = (selmask >> j) & 1u;
+          const bool isLow = valid && sel && (kp - kpk <= delta + 1);
+          const bool isHigh = valid && !sel && (kpk1 - kp <= delta + 1);
+          const uint64_t bl = __ballot(isLow);
+          const uint64_t bh = __ballot(isHigh);
+          if (isLow) {
+            const int pos = nlow + __popcll(bl & ((uint64_t(1) << lane) - 1));
+            if (pos < EDGE_LIST_MAX) {
+              lowKp[wv * EDGE_LIST_MAX + pos] = kp;
+              lowE[wv * EDGE_LIST_MAX + pos] = e;
+            }
+          }
+          if (isHigh) {
+            const int pos = nhigh + __popcll(bh & ((uint64_t(1) << lane) - 1));
+            if (pos < EDGE_LIST_MAX) {
+              highKp[wv * EDGE_LIST_MAX + pos] = kp;
+              highE[wv * EDGE_LIST_MAX + pos] = e;
+            }
+          }
+          nlow += __popcll(bl);
+          nhigh += __popcll(bh);
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        if (nlow > EDGE_LIST_MAX || nhigh > EDGE_LIST_MAX) {
+          if (lane == 0) atomicOr(&a.cnt[N_OVERFLOW], 1);
+        } else {
+          const int P = nlow * nhigh;
+          for (int p = lane; p < P; p += 64) {
+            const int ia = p / nhigh, ib = p - ia * nhigh;
+            const int A = lowE[wv * EDGE_LIST_MAX + ia];
+            const int B = highE[wv * EDGE_LIST_MAX + ib];
+            const int64_t rho =
+                lowKp[wv * EDGE_LIST_MAX + ia] - highKp[wv * EDGE_LIST_MAX + ib] - (A > B ? 1 : 0);
+            if (rho <= delta) {
+              const int slot = atomicAdd(&a.cnt[N_EDGES], 1);
+              if (slot < a.edge_cap)
+                a.edges[slot] = (static_cast<uint64_t>(rho) << 20) |
+                                (static_cast<uint64_t>(A) << 10) | static_cast<uint64_t>(B);
+              else
+                atomicOr(&a.cnt[N_OVERFLOW], 1);
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+  __syncthreads();
+  int32_t* part = a.part_loads + static_cast<size_t>(blockIdx.x) * n;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) part[e] = sload[e];
+  if (emit_edges && blockIdx.x == 0 && threadIdx.x == 0) a.ctrl[C_EDGES_VALID] = 1;
+}
+
+// ---------------------------------------------------------------------------
+// Status: reduce the per-block loads, then decide the next phase exactly as
+// the schedule prescribes (rounds until the unbalanced count stalls, then
+// augmenting paths, then done).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void status_pass(Args a) {
+  __shared__ int32_t s_imb[1024], s_res[1024];
+  const int n = a.n;
+  int imb = 0, res = 0;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    int32_t L = 0;
+    for (int b = 0; b < a.topk_grid; ++b) L += a.part_loads[static_cast<size_t>(b) * n + e];
+    a.loads[e] = L;
+    const int64_t d = static_cast<int64_t>(L) - target(a.T, n, a.k, e);
+    imb += d != 0;
+    const int ad = static_cast<int>(d < 0 ? -d : d);
+    res = res > ad ? res : ad;
+  }
+  s_imb[threadIdx.x] = imb;
+  s_res[threadIdx.x] = res;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      s_imb[threadIdx.x] += s_imb[threadIdx.x + s];
+      s_res[threadIdx.x] = max(s_res[threadIdx.x], s_res[threadIdx.x + s]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  int64_t* c = a.ctrl;
+  imb = s_imb[0];
+  c[C_IMB] = imb;
+  c[C_RESID] = s_res[0];
+  const int64_t ph = c[C_PHASE];
+  if (ph == PH_ROUNDS) {
+    if (imb == 0) {
+      c[C_PHASE] = PH_DONE;
+    } else if (c[C_ROUNDS] >= c[C_MAX_ROUNDS]) {
+      c[C_PHASE] = PH_SAP;
+    } else if (c[C_BEST] < 0 || imb < c[C_BEST]) {
+      c[C_BEST] = imb;
+      c[C_SINCE] = 0;
+    } else if (++c[C_SINCE] >= STALL_ROUNDS) {
+      c[C_PHASE] = PH_SAP;
+    }
+  } else if (ph == PH_SAP) {
+    if (imb == 0) {
+      c[C_PHASE] = PH_DONE;
+    } else if (c[C_MOVES] >= MAX_SAP_MOVES) {
+      c[C_PHASE] = PH_FAILED;
+      c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One quantile round: every unbalanced expert computes the C-th and (C+1)-th
+// largest margins over all tokens by an exact MSB-first radix select (10-bit
+// digits on the order-preserving uint64 image of the int64 margin) and jumps
+// to minus their midpoint.  One block per expert, reading the transposed
+// scores so the column is contiguous.
+// ---------------------------------------------------------------------------
+constexpr int SEL_BLOCK = 256;
+constexpr int DIG = 10;
+constexpr int NBIN = 1 << DIG;
+
+__device__ __forceinline__ uint64_t margin_u(const Args& a, const int64_t* bias, int e,
+                                             int t) {
+  const int64_t sfx = score_fixed(a.scoresT[static_cast<size_t>(e) * a.T + t]);
+  const uint64_t key = pack_key(sfx, bias[e], e);
+  const int64_t thk = a.th_k[t];
+  const bool sel = static_cast<int64_t>(key) >= thk;
+  const int64_t base = static_cast<int64_t>(pack_key(sfx, 0, e));
+  const int64_t M = base - (sel ? a.th_k1[t] : thk);
+  return static_cast<uint64_t>(M) ^ (uint64_t(1) << 63);
+}
+
+__global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
+  if (a.ctrl[C_PHASE] != PH_ROUNDS) return;
+  const int e = blockIdx.x;
+  const int n = a.n, T = a.T;
+  const int cur = static_cast<int>(a.ctrl[C_CUR] & 1);
+  const int64_t* bias = a.bfx + cur * n;
+  int64_t* nb = a.bfx + (cur ^ 1) * n;
+  const int64_t C = target(T, n, a.k, e);
+  if (a.loads[e] == C) {
+    if (threadIdx.x == 0) nb[e] = bias[e];
+    return;
+  }
+  __shared__ int32_t h1[NBIN], h2[NBIN];
+  __shared__ uint64_t s_min[SEL_BLOCK], s_max[SEL_BLOCK];
+  __shared__ uint64_t s_pre[2];
+  __shared__ int64_t s_rem[2];
+  __shared__ int s_shift;
+
+  // ranks wanted (1-indexed, descending): r1 = C, r2 = C+1, with the edge cases
+  // C == 0 (only the maximum) and C == T (only the minimum).
+  int64_t r1 = C, r2 = C + 1;
+  if (C == 0) r1 = r2 = 1;
+  if (C == T) r1 = r2 = T;
+
+  uint64_t mn = ~uint64_t(0), mx = 0;
+  for (int t = threadIdx.x; t < T; t += SEL_BLOCK) {
+    const uint64_t u = margin_u(a, bias, e, t);
+    mn = u < mn ? u : mn;
+    mx = u > mx ? u : mx;
+  }
+  s_min[threadIdx.x] = mn;
+  s_max[threadIdx.x] = mx;
+  __syncthreads();
+  for (int s = SEL_BLOCK / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      s_min[threadIdx.x] = min(s_min[threadIdx.x], s_min[threadIdx.x + s]);
+      s_max[threadIdx.x] = max(s_max[threadIdx.x], s_max[threadIdx.x + s]);
+    }
+    __syncthreads();
+  }
+  mn = s_min[0];
+  mx = s_max[0];
+  // bits above `top` are shared by every margin
+  const int top = (mn == mx) ? 0 : 64 - __clzll(static_cast<long long>(mn ^ mx));
+  const uint64_t common = (top == 64) ? 0 : (mn >> top) << top;
+  if (threadIdx.x == 0) {
+    s_pre[0] = s_pre[1] = common;
+    s_rem[0] = r1;
+    s_rem[1] = r2;
+  }
+  uint64_t mask = (top == 64) ? 0 : ~((uint64_t(1) << top) - 1);
+  int shift = top;
+  __syncthreads();
+  while (shift > 0) {
+    const int nbits = shift >= DIG ? DIG : shift;
+    shift -= nbits;
+    for (int i = threadIdx.x; i < NBIN; i += SEL_BLOCK) h1[i] = h2[i] = 0;
+    __syncthreads();
+    const uint64_t p1 = s_pre[0], p2 = s_pre[1];
+    const uint64_t dmask = (uint64_t(1) << nbits) - 1;
+    for (int t = threadIdx.x; t < T; t += SEL_BLOCK) {
+      const uint64_t u = margin_u(a, bias, e, t);
+      const int dg = static_cast<int>((u >> shift) & dmask);
+      if ((u & mask) == p1) atomicAdd(&h1[dg], 1);
+      if ((u & mask) == p2) atomicAdd(&h2[dg], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      int32_t* h = threadIdx.x == 0 ? h1 : h2;
+      int64_t rem = s_rem[threadIdx.x];
+      int dsel = 0;
+      for (int dgt = static_cast<int>(dmask); dgt >= 0; --dgt) {
+        if (rem <= h[dgt]) {
+          dsel = dgt;
+          break;
+        }
+        rem -= h[dgt];
+      }
+      s_rem[threadIdx.x] = rem;
+      s_pre[threadIdx.x] |= static_cast<uint64_t>(dsel) << shift;
+    }
+    mask |= dmask << shift;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int64_t m1 = static_cast<int64_t>(s_pre[0] ^ (uint64_t(1) << 63));
+    const int64_t m2 = static_cast<int64_t>(s_pre[1] ^ (uint64_t(1) << 63));
+    int64_t b;
+    if (C == 0)
+      b = -(m1 >> IDX_BITS) - 1;
+    else if (C == T)
+      b = -(m1 >> IDX_BITS) + 1;
+    else
+      b = -floor_mid(m1, m2);
+    nb[e] = b;
+    if (b >= BIAS_LIMIT || b <= -BIAS_LIMIT) atomicOr(&a.cnt[N_BIASRANGE], 1);
+    a.ctrl[C_SELECT_RAN] = 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Finish a step (one block of 1024 threads): after a quantile round flip the
+// live bias buffer; in the augmenting-path phase solve one move on the
+// sparse edge list.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void finish_step(Args a) {
+  int64_t* c = a.ctrl;
+  const int n = a.n;
+  const int tid = threadIdx.x;
+  __shared__ uint64_t d[1024];
+  __shared__ uint64_t dprev[1024];
+  __shared__ int64_t s_red[1024];
+  __shared__ int s_flag;
+  __shared__ int s_path[1025];
+  __shared__ int s_len;
+
+  const int64_t ph = c[C_PHASE];
+  if (ph == PH_ROUNDS) {
+    if (tid == 0 && c[C_SELECT_RAN]) {
+      c[C_SELECT_RAN] = 0;
+      c[C_CUR] ^= 1;
+      c[C_ROUNDS] += 1;
+      if (a.cnt[N_BIASRANGE]) {
+        c[C_PHASE] = PH_FAILED;
+        c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
+      }
+    }
+    return;
+  }
+  if (ph != PH_SAP || c[C_EDGES_VALID] == 0) return;
+
+  const int cur = static_cast<int>(c[C_CUR] & 1);
+  int64_t* bias = a.bfx + cur * n;
+  const int64_t delta = c[C_DELTA];
+  const int nedges = a.cnt[N_EDGES];
+  const bool overflow = a.cnt[N_OVERFLOW] != 0 || nedges > a.edge_cap;
+  __syncthreads();
+  if (overflow) {
+    if (tid == 0) {
+      if (delta / 4 < DELTA_MIN) {
+        c[C_PHASE] = PH_FAILED;
+        c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
+      } else {
+        c[C_DELTA] = delta / 4;
+      }
+      c[C_EDGES_VALID] = 0;
+      a.cnt[N_EDGES] = 0;
+      a.cnt[N_OVERFLOW] = 0;
+    }
+    return;
+  }
+  // sources: overloaded experts at distance 0
+  bool over_e = false, under_e = false;
+  if (tid < n) {
+    const int64_t C = target(a.T, n, a.k, tid);
+    over_e = a.loads[tid] > C;
+    under_e = a.loads[tid] < C;
+    d[tid] = over_e ? static_cast<uint64_t>(tid) : PACKED_INF;
+  }
+  __syncthreads();
+  int64_t D = DIST_INF;
+  int passes = 0;
+  while (true) {
+    if (tid < n) dprev[tid] = d[tid];
+    __syncthreads();
+    for (int i = tid; i < nedges; i += blockDim.x) {
+      const uint64_t ed = a.edges[i];
+      const int B = static_cast<int>(ed & 1023);
+      const int A = static_cast<int>((ed >> 10) & 1023);
+      const int64_t rho = static_cast<int64_t>(ed >> 20);
+      const int64_t dA = static_cast<int64_t>(d[A] >> IDX_BITS);
+      if (dA >= DIST_INF) continue;
+      const int64_t cand = dA + rho;
+      if (cand >= DIST_INF) continue;
+      const uint64_t pk = (static_cast<uint64_t>(cand) << IDX_BITS) | static_cast<uint64_t>(A);
+      if (pk < d[B]) atomicMin(reinterpret_cast<unsigned long long*>(&d[B]), pk);
+    }
+    __syncthreads();
+    s_red[tid] = (tid < n && under_e) ? static_cast<int64_t>(d[tid] >> IDX_BITS) : DIST_INF;
+    __syncthreads();
+    for (int s = 512; s > 0; s >>= 1) {
+      if (tid < s) s_red[tid] = min(s_red[tid], s_red[tid + s]);
+      __syncthreads();
+    }
+    D = s_red[0];
+    if (tid == 0) s_flag = 0;
+    __syncthreads();
+    if (tid < n && d[tid] != dprev[tid] && static_cast<int64_t>(d[tid] >> IDX_BITS) <= D)
+      s_flag = 1;
+    __syncthreads();
+    ++passes;
+    const int go = s_flag;
+    __syncthreads();
+    if (!go || passes > 4 * 1024) break;
+  }
+  if (D >= DIST_INF || D > delta) {
+    if (tid == 0) {
+      if (delta >= DELTA_MAX) {
+        c[C_PHASE] = PH_FAILED;
+        c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
+      } else {
+        c[C_DELTA] = delta * 16;
+      }
+      c[C_EDGES_VALID] = 0;
+      a.cnt[N_EDGES] = 0;
+    }
+    return;
+  }
+  // u* = lowest underloaded expert at distance D
+  s_red[tid] = (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) == D) ? tid : 1 << 30;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if (tid < s) s_red[tid] = min(s_red[tid], s_red[tid + s]);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int v = static_cast<int>(s_red[0]);
+    int len = 0;
+    bool ok = true;
+    while (true) {
+      s_path[len++] = v;
+      const int64_t Cv = target(a.T, n, a.k, v);
+      if (a.loads[v] > Cv) break;
+      v = static_cast<int>(d[v] & 1023);
+      if (len > n) {
+        ok = false;
+        break;
+      }
+    }
+    s_len = ok ? len : -1;
+  }
+  __syncthreads();
+  if (s_len < 0) {
+    if (tid == 0) {
+      c[C_PHASE] = PH_FAILED;
+      c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
+    }
+    return;
+  }
+  if (tid < n) {
+    const int64_t dv = static_cast<int64_t>(d[tid] >> IDX_BITS);
+    bias[tid] += (dv < D ? dv : D) - D;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int len = s_len;  // s_path[len-1] is the source, s_path[0] = u*
+    for (int i = 0; i < len; ++i) bias[s_path[len - 1 - i]] += i;
+    bool bad = false;
+    for (int e = 0; e < n; ++e) bad |= (bias[e] >= BIAS_LIMIT || bias[e] <= -BIAS_LIMIT);
+    c[C_MOVES] += 1;
+    c[C_LAST_D] = D;
+    c[C_LAST_HOPS] = len - 1;
+    c[C_BF_PASSES] += passes;
+    if (bad) {
+      c[C_PHASE] = PH_FAILED;
+      c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
+    }
+    c[C_EDGES_VALID] = 0;
+    a.cnt[N_EDGES] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Small helpers: init, transposition, centring, bias conversion.
+// ---------------------------------------------------------------------------
+__global__ void init_ctrl(Args a, const double* bias_in, int mode, int max_rounds) {
+  const int n = a.n;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const double b = bias_in ? bias_in[e] : 0.0;
+    const double bf = rint(b * 1099511627776.0);
+    int64_t v = 0;
+    if (!(fabs(bf) < static_cast<double>(BIAS_LIMIT))) {
+      atomicOr(&a.cnt[N_BIASRANGE], 1);
+    } else {
+      v = static_cast<int64_t>(bf);
+    }
+    a.bfx[e] = v;
+    a.bfx[n + e] = v;
+  }
+  if (threadIdx.x == 0) {
+    int64_t* c = a.ctrl;
+    for (int i = 0; i < C_COUNT; ++i) c[i] = 0;
+    // an empty batch is balanced: every target is zero
+    c[C_PHASE] = mode == MOE_QB_BATCH ? (a.T > 0 ? PH_ROUNDS : PH_DONE) : PH_FROZEN;
+    c[C_BEST] = -1;
+    c[C_DELTA] = DELTA_START;
+    c[C_MAX_ROUNDS] = max_rounds;
+  }
+}
+
+__global__ void zero_cnt(Args a) {
+  if (threadIdx.x < N_COUNT) a.cnt[threadIdx.x] = 0;
+}
+
+__global__ void check_range(Args a) {
+  // bias given out of range: report instead of routing with a clamped bias
+  if (threadIdx.x == 0 && a.cnt[N_BIASRANGE]) {
+    a.ctrl[C_PHASE] = PH_FAILED;
+    a.ctrl[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
+  }
+}
+
+__global__ void transpose_scores(const float* __restrict__ in, float* __restrict__ out, int T,
+                                 int n) {
+  __shared__ float tile[64][65];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 256 threads: 64 x 4
+  for (int r = ty; r < 64; r += 4) {
+    const int t = t0 + r, e = e0 + tx;
+    tile[r][tx] = (t < T && e < n) ? in[static_cast<size_t>(t) * n + e] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int e = e0 + r, t = t0 + tx;
+    if (e < n && t < T) out[static_cast<size_t>(e) * T + t] = tile[tx][r];
+  }
+}
+
+__global__ void center_and_export(Args a, double* bias_out, int32_t* info) {
+  __shared__ long long s[1024];
+  const int n = a.n;
+  int64_t* c = a.ctrl;
+  const int cur = static_cast<int>(c[C_CUR] & 1);
+  int64_t* bias = a.bfx + cur * n;
+  const bool balanced = c[C_PHASE] == PH_DONE;
+  long long acc = 0;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) acc += bias[e];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = blockDim.x / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) s[threadIdx.x] += s[threadIdx.x + st];
+    __syncthreads();
+  }
+  long long sum = s[0];
+  long long off = sum / n;
+  if ((sum % n != 0) && (sum < 0)) off -= 1;  // floor division
+  if (!balanced) off = 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    bias[e] -= off;
+    if (bias_out) bias_out[e] = static_cast<double>(bias[e]) * (1.0 / 1099511627776.0);
+  }
+  if (threadIdx.x == 0 && c[C_PHASE] != PH_DONE && c[C_PHASE] != PH_FROZEN &&
+      c[C_STATUS] == MOE_QB_STATUS_OK)
+    c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;  // the host's step cap ended the loop
+  if (threadIdx.x == 0 && info) {
+    info[0] = static_cast<int32_t>(c[C_ROUNDS]);
+    info[1] = static_cast<int32_t>(c[C_STATUS]);
+    info[3] = static_cast<int32_t>(c[C_MOVES]);
+  }
+}
+
+__global__ void export_resid(Args a, int32_t* info) {
+  if (threadIdx.x == 0 && info) info[2] = static_cast<int32_t>(a.ctrl[C_RESID]);
+}
+
+size_t topk_smem_bytes() {
+  return 1024 * 4 + 4 * EDGE_LIST_MAX * (8 + 8 + 4 + 4) + 8 * 4 + 4 * MAX_K * (8 + 4 + 4 + 4);
+}
+
+}  // namespace qb
+
+// ---------------------------------------------------------------------------
+// Host driver shared by moe_route_qb and moe_latent_forward.
+// ---------------------------------------------------------------------------
+
+static int32_t edge_capacity(int32_t T) { return 16 * T + 65536; }
+
+size_t route_workspace_layout(int32_t T, int32_t n, RouteWorkspace* ws, void* base) {
+  Carver cv(base);
+  RouteWorkspace w;
+  w.scoresT = cv.take<float>(static_cast<size_t>(T) * n);
+  w.bfx = cv.take<int64_t>(2 * static_cast<size_t>(n));
+  w.th_k = cv.take<int64_t>(T);
+  w.th_k1 = cv.take<int64_t>(T);
+  w.part_loads = cv.take<int32_t>(static_cast<size_t>(qb::TOPK_GRID_MAX) * n);
+  w.loads = cv.take<int32_t>(n);
+  w.ctrl = cv.take<int64_t>(qb::C_COUNT);
+  w.cnt = cv.take<int32_t>(qb::N_COUNT);
+  w.edge_cap = edge_capacity(T);
+  w.edges = cv.take<uint64_t>(w.edge_cap);
+  if (ws) *ws = w;
+  return cv.bytes();
+}
+
+int route_validate(int32_t T, int32_t n, int32_t k) {
+  if (T < 0 || n < 1 || k < 1 || k > n) return MOE_EINVAL;
+  if (n > 1024 || k > qb::MAX_K) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// Routes T tokens from fp32 scores.  Outputs may be null except the internal
+// loads buffer; `loads_out` receives a copy when given.
+int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode,
+              int32_t max_rounds, double* bias, int32_t* idx, float* w, int32_t* loads_out,
+              int32_t* info, const RouteWorkspace& ws, hipStream_t stream) {
+  using namespace qb;
+  Args a{};
+  a.scores = scores;
+  a.scoresT = ws.scoresT;
+  a.T = T;
+  a.n = n;
+  a.k = k;
+  a.bfx = ws.bfx;
+  a.th_k = ws.th_k;
+  a.th_k1 = ws.th_k1;
+  a.part_loads = ws.part_loads;
+  a.loads = ws.loads;
+  a.ctrl = ws.ctrl;
+  a.cnt = ws.cnt;
+  a.edges = ws.edges;
+  a.edge_cap = ws.edge_cap;
+  a.idx = idx;
+  a.w = w;
+  const int grid = T > 0 ? ((T + 3) / 4 < TOPK_GRID_MAX ? (T + 3) / 4 : TOPK_GRID_MAX) : 1;
+  a.topk_grid = grid;
+  if (max_rounds <= 0) max_rounds = 64;
+  const size_t smem = topk_smem_bytes();
+
+  hipLaunchKernelGGL(zero_cnt, dim3(1), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(init_ctrl, dim3(1), dim3(1024), 0, stream, a,
+                     mode == MOE_QB_BATCH ? bias : static_cast<const double*>(bias), mode,
+                     max_rounds);
+  hipLaunchKernelGGL(check_range, dim3(1), dim3(64), 0, stream, a);
+  MOE_LAUNCH_CHECK();
+
+  if (mode == MOE_QB_BATCH && T > 0) {
+    dim3 tg((T + 63) / 64, (n + 63) / 64);
+    hipLaunchKernelGGL(transpose_scores, tg, dim3(256), 0, stream, scores, ws.scoresT, T, n);
+    MOE_LAUNCH_CHECK();
+    const int batch = 4;
+    const int max_steps = max_rounds + 8 * MAX_SAP_MOVES + 64;
+    int steps = 0;
+    while (true) {
+      for (int i = 0; i < batch; ++i) {
+        hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 0);
+        hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), 0, stream, a);
+        hipLaunchKernelGGL(quantile_round, dim3(n), dim3(SEL_BLOCK), 0, stream, a);
+        hipLaunchKernelGGL(finish_step, dim3(1), dim3(1024), 0, stream, a);
+      }
+      MOE_LAUNCH_CHECK();
+      steps += batch;
+      int64_t phase = 0;
+      MOE_HIP_CHECK(hipMemcpyAsync(&phase, ws.ctrl + C_PHASE, sizeof(int64_t),
+                                   hipMemcpyDeviceToHost, stream));
+      MOE_HIP_CHECK(hipStreamSynchronize(stream));
+      if (phase == PH_DONE || phase == PH_FAILED) break;
+      if (steps >= max_steps) break;
+    }
+  }
+  // final pass: centred bias, ordered outputs, loads
+  hipLaunchKernelGGL(center_and_export, dim3(1), dim3(1024), 0, stream, a,
+                     mode == MOE_QB_BATCH ? bias : nullptr, info);
+  // with T == 0 this still writes zero per-block loads for the status pass
+  hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 1);
+  hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(export_resid, dim3(1), dim3(64), 0, stream, a, info);
+  if (loads_out)
+    MOE_HIP_CHECK(hipMemcpyAsync(loads_out, ws.loads, sizeof(int32_t) * n,
+                                 hipMemcpyDeviceToDevice, stream));
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_route_workspace_bytes(int32_t T, int32_t n, int32_t k) {
+  if (moe::route_validate(T, n, k) != MOE_OK) return 0;
+  return moe::route_workspace_layout(T, n, nullptr, nullptr);
+}
+
+extern "C" int moe_route_qb(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode,
+                            int32_t max_rounds, double* bias, int32_t* topk_idx, float* topk_w,
+                            int32_t* loads, int32_t* qb_info, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int st = moe::route_validate(T, n, k);
+  if (st != MOE_OK) return st;
+  if (mode != MOE_QB_BATCH && mode != MOE_QB_FROZEN) return MOE_EINVAL;
+  if ((T > 0 && (!scores || !topk_idx || !topk_w)) || !bias || !workspace) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MOE_EINVAL;
+  moe::RouteWorkspace ws;
+  const size_t need = moe::route_workspace_layout(T, n, &ws, workspace);
+  if (workspace_bytes < need) return MOE_EWORKSPACE;
+  moe::prof::Scope sc(moe::prof::ST_ROUTING, static_cast<hipStream_t>(stream));
+  return moe::route_run(scores, T, n, k, mode, max_rounds, bias, topk_idx, topk_w, loads, qb_info,
+                        ws, static_cast<hipStream_t>(stream));
+}

@@ -1,0 +1,73 @@
+"""The C ABI library loads, exports every declared entry point and validates
+arguments on the host before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("moe_route_qb", "moe_latent_forward", "moe_route_workspace_bytes",
+                 "moe_forward_workspace_bytes", "moe_status_str"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(moe.EXPORTED) <= set(declared_functions())
+
+
+def test_status_strings():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    assert lib.moe_status_str(0) == b"ok"
+    assert b"workspace" in lib.moe_status_str(-3)
+    assert lib.moe_status_str(12345)
+
+
+def test_route_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    assert lib.moe_route_workspace_bytes(100, 0, 1) == 0
+    assert lib.moe_route_workspace_bytes(100, 8, 9) == 0
+    assert lib.moe_route_workspace_bytes(100, 2048, 4) == 0
+    need = lib.moe_route_workspace_bytes(100, 64, 4)
+    assert need > 0
+    args = lambda T, n, k, mode=1, ws=fake, wsb=need: (fake, T, n, k, mode, 64, fake, fake, fake,
+                                                       fake, fake, ws, wsb, None)
+    assert lib.moe_route_qb(*args(100, 64, 65)) == -1          # k > n
+    assert lib.moe_route_qb(*args(100, 64, 0)) == -1
+    assert lib.moe_route_qb(*args(-1, 64, 4)) == -1
+    assert lib.moe_route_qb(*args(100, 2048, 4)) == -2         # n > 1024
+    assert lib.moe_route_qb(*args(100, 128, 100)) == -2        # k > 64
+    assert lib.moe_route_qb(*args(100, 64, 4, mode=7)) == -1
+    assert lib.moe_route_qb(*args(100, 64, 4, ws=None)) == -1
+    assert lib.moe_route_qb(*args(100, 64, 4, ws=ctypes.c_void_p((1 << 20) + 8))) == -1
+    assert lib.moe_route_qb(*args(100, 64, 4, wsb=need - 1)) == -3
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "sparse_moe_ffn_sigmoid_amd")
+    dst = tmp_path / "sparse_moe_ffn_sigmoid_amd"
+    dst.mkdir()
+    (dst / "__init__.py").write_text(open(os.path.join(pkg, "__init__.py")).read())
+    r = subprocess.run([sys.executable, "-c", "import sparse_moe_ffn_sigmoid_amd"],
+                       cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0 and "libmoe_mi355x.so is missing" in r.stderr

@@ -1,0 +1,81 @@
+"""Parity of moe_latent_forward (HIP) with the float64 layer oracle.
+
+Protocol ("identical scores"): the oracle's fp32 router scores are passed to
+the HIP layer as ``scores_in``, so both sides route from the same numbers;
+indices, loads, bias and QB counters must then match bit for bit and the
+outputs within max|diff| / rms(ref) <= 2e-2 (bf16), 1e-1 (MXFP4 against the
+oracle on the decoded weights) or 1e-4 (fp32).  The HIP router is checked
+separately against the oracle's scores (max abs difference <= 1e-5).
+"""
+import numpy as np
+import pytest
+
+import workloads
+from layer_cases import announce, oracle_scores, rel_err, run_gpu
+from oracle import layer as olayer
+from oracle import qb
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 1e-1}
+
+
+def check_layer(shape, seed=0, qb_mode=qb.MODE_BATCH, bias=None, name=""):
+    import sparse_moe_ffn_sigmoid_amd as moe
+    announce(f"layer {name} {shape}")
+    inp = workloads.layer_inputs(shape, "cpu", seed=seed, random_gamma=True)
+    s = oracle_scores(inp)
+    ref = qb.route_qb(s, shape.k, bias=bias, mode=qb_mode)
+    got = run_gpu(moe, shape, inp, scores_in=s, bias=bias, qb_mode=qb_mode)
+    assert (got["idx"] == ref["idx"]).all()
+    assert (got["loads"] == ref["loads"]).all()
+    assert tuple(int(v) for v in got["info"]) == tuple(ref["info"])
+    if qb_mode == qb.MODE_BATCH:
+        assert (got["bias"] == ref["bias"]).all()
+    out_ref = olayer.layer_forward(inp, ref["idx"], ref["w"], shape.eps)
+    err = rel_err(got["out"], out_ref)
+    print(f"  max|diff|/rms = {err:.3e}", flush=True)
+    assert err <= TOL[shape.routed if shape.routed == "mxfp4" else shape.act], err
+    # the HIP router on its own
+    announce(f"router {name}")
+    own = run_gpu(moe, shape, inp, bias=bias, qb_mode=qb_mode)
+    assert np.abs(own["scores"] - s).max() <= 1e-5
+    return got, ref
+
+
+def test_tiny_fp32_layer():
+    check_layer(workloads.SHAPES["tiny"], name="tiny fp32")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                                   # several tiles, ragged rows
+    dict(T=37, n=24, k=3, d=448, latent=192, m=128, shared=192),
+    dict(T=16, n=64, k=4),                                     # ~1 row per expert (small-M tile)
+])
+def test_bf16_layer(kw):
+    check_layer(workloads.small_shape(**kw), seed=1, name=f"bf16 {kw}")
+
+
+def test_mxfp4_layer():
+    check_layer(workloads.small_shape(routed="mxfp4", T=300, k=4), seed=2, name="mxfp4 qb")
+
+
+def test_mxfp4_layer_frozen_zero_bias():
+    shape = workloads.small_shape(routed="mxfp4", T=300, k=4, offset_std=1.0)
+    check_layer(shape, seed=3, qb_mode=qb.MODE_FROZEN, bias=np.zeros(shape.n),
+                name="mxfp4 frozen")
+
+
+def test_bf16_layer_frozen_bias():
+    shape = workloads.small_shape(T=120)
+    bias = np.rint(np.random.default_rng(4).normal(0, 0.1, shape.n) * 2.0 ** 40) * 2.0 ** -40
+    check_layer(shape, seed=4, qb_mode=qb.MODE_FROZEN, bias=bias, name="bf16 frozen")
+
+
+def test_layer_empty_batch():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    shape = workloads.small_shape(T=0)
+    inp = workloads.layer_inputs(shape, "cpu", seed=0)
+    announce("layer T=0")
+    got = run_gpu(moe, shape, inp)
+    assert got["out"].shape == (0, shape.d) and (got["loads"] == 0).all()

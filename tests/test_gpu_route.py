@@ -1,0 +1,134 @@
+"""Parity of moe_route_qb (HIP) with the QB oracle, through the C ABI.
+
+Bit-exact on indices, loads, the returned bias and the round/move counts
+(the HIP path runs the same schedule); weights within (k+1) fp32 ulps of
+the float64 oracle.  Inputs: router logits N(0,1) plus a per-expert offset,
+turned into fp32 scores by the oracle's sigmoid and fed to both sides.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import layer as olayer
+from oracle import qb
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def scores(T, n, offset_std=0.5, seed=0):
+    return olayer.sigmoid(workloads.qb_logits(T, n, offset_std, seed)).astype(np.float32)
+
+
+def gpu_route(s, k, bias=None, mode=1, max_rounds=64):
+    import sparse_moe_ffn_sigmoid_amd as moe
+    b = None if bias is None else torch.from_numpy(np.asarray(bias, np.float64)).cuda()
+    r = moe.route_qb(torch.from_numpy(s).cuda(), k, b, mode, max_rounds)
+    torch.cuda.synchronize()
+    return {key: v.cpu().numpy() for key, v in r.items()}
+
+
+def announce(name):
+    print(f"\n[gpu case] {name}", flush=True)
+    sys.stdout.flush()
+
+
+def check(s, k, mode=qb.MODE_BATCH, bias=None, name=""):
+    announce(f"route {name} T={s.shape[0]} n={s.shape[1]} k={k} mode={mode}")
+    ref = qb.route_qb(s, k, bias=bias, mode=mode)
+    got = gpu_route(s, k, bias, mode)
+    assert (got["idx"] == ref["idx"]).all()
+    assert (got["loads"] == ref["loads"]).all()
+    assert tuple(int(v) for v in got["info"]) == tuple(ref["info"])
+    if mode == qb.MODE_BATCH:
+        assert (got["bias"] == ref["bias"]).all()
+    tol = (k + 1) * 2.0 ** -24
+    assert np.allclose(got["w"], ref["w"], rtol=tol, atol=0)
+    return ref, got
+
+
+CASES = [
+    ("tiny", 64, 32, 4, 0.3),
+    ("decode", 64, 896, 16, 0.5),
+    ("ragged", 1000, 100, 7, 1.0),
+    ("mid", 3000, 256, 8, 0.5),
+    ("max_n_k", 300, 1024, 64, 0.5),
+    ("k3_prefill_shape", 4096, 896, 16, 0.5),
+]
+
+
+@pytest.mark.parametrize("name,T,n,k,std", CASES)
+def test_route_batch_parity(name, T, n, k, std):
+    ref, got = check(scores(T, n, std), k, name=name)
+    assert ref["info"][1] == qb.STATUS_OK
+    assert (got["loads"] == qb.targets(T, n, k)).all()
+
+
+def test_route_frozen_parity():
+    s = scores(500, 64, 1.0, seed=3)
+    bias = np.random.default_rng(0).normal(0, 0.2, 64)
+    bias = np.rint(bias * 2.0 ** 40) * 2.0 ** -40
+    check(s, 6, mode=qb.MODE_FROZEN, bias=bias, name="frozen")
+
+
+def test_route_warm_start_is_fixed_point():
+    s = scores(2000, 128, 0.5, seed=5)
+    ref = qb.route_qb(s, 8)
+    announce("warm start")
+    got = gpu_route(s, 8, bias=ref["bias"])
+    assert tuple(int(v) for v in got["info"]) == (0, 0, 0, 0)
+    assert (got["bias"] == ref["bias"]).all() and (got["idx"] == ref["idx"]).all()
+
+
+def test_route_edge_cases():
+    check(scores(50, 1, 0.5), 1, name="n=1")
+    check(scores(20, 8, 0.5), 8, name="k=n")
+    announce("T=0")
+    got = gpu_route(np.zeros((0, 16), np.float32), 3)
+    assert got["idx"].shape == (0, 3) and (got["loads"] == 0).all() and got["info"][1] == 0
+
+
+def test_route_degenerate_reports_not_balanced():
+    s = np.tile(np.array([[0.7, 0.3]], np.float32), (4, 1))
+    announce("degenerate")
+    got = gpu_route(s, 1, max_rounds=8)
+    assert got["info"][1] == qb.STATUS_NOT_BALANCED
+    ref = qb.route_qb(s, 1, max_rounds=8, max_sap=8)
+    assert ref["info"][1] == qb.STATUS_NOT_BALANCED
+
+
+def test_route_bias_out_of_range_reported():
+    s = scores(100, 16, 0.5)
+    announce("bias range")
+    got = gpu_route(s, 2, bias=np.full(16, 2048.0), mode=qb.MODE_FROZEN)
+    assert got["info"][1] == qb.STATUS_BIAS_RANGE
+
+
+def test_route_qb_workload_full_size():
+    """T=57344, n=896, k=16: against the stored oracle result, plus the
+    optimality certificate (exact loads and a bias that reproduces the
+    selection) checked here with plain NumPy."""
+    path = os.path.join(GOLDEN, "qb_57344x896_k16.json")
+    cfg = workloads.QB_SHAPE
+    s = scores(cfg["T"], cfg["n"], cfg["offset_std"], seed=0)
+    announce("qb full size")
+    got = gpu_route(s, cfg["k"])
+    C = qb.targets(cfg["T"], cfg["n"], cfg["k"])
+    assert (got["loads"] == C).all() and got["info"][1] == 0
+    # certificate: top-k of fixed-point (score + returned bias) is the selection
+    sfx = np.rint(s.astype(np.float64) * 2.0 ** 40).astype(np.int64)
+    bfx = np.rint(got["bias"] * 2.0 ** 40).astype(np.int64)
+    key = ((sfx + bfx[None, :] + (1 << 51)) << 10) | (1023 - np.arange(cfg["n"]))
+    top = np.argpartition(-key, cfg["k"] - 1, axis=1)[:, :cfg["k"]]
+    assert (np.sort(top, 1) == np.sort(got["idx"], 1)).all()
+    if os.path.exists(path):
+        gold = json.load(open(path))
+        import hashlib
+        assert hashlib.sha256(got["idx"].astype("<i4").tobytes()).hexdigest() == gold["idx_sha256"]
+        assert [int(v) for v in np.rint(got["bias"] * 2.0 ** 40)] == gold["bias_fixed"]
+        assert [int(v) for v in got["info"]] == gold["info"]
