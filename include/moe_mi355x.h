@@ -22,8 +22,14 @@
  *
  * Conventions for every entry point:
  *   - Every pointer argument is a DEVICE pointer owned by the caller unless
- *     stated otherwise.  The library never frees or retains caller memory and
- *     keeps no state between calls apart from loaded code objects.
+ *     stated otherwise.  The library never frees or retains caller memory.
+ *     State kept between calls: loaded code objects; per device, one
+ *     auxiliary non-blocking stream (default priority) with two events,
+ *     created on first use, on which moe_latent_forward runs the
+ *     routing-independent shared branch (forked from and joined back into
+ *     `stream`, under a per-device mutex held for the call); per host thread,
+ *     one pinned 64-byte word the balancing loop polls; the opt-in
+ *     stage-timing records.
  *   - Matrices are row-major [out_features][in_features] (K contiguous);
  *     activations are [T][features].  bf16 values are passed as raw 16-bit
  *     patterns.  MXFP4 weights: codes uint8 [rows][K/2] (element 2i in the

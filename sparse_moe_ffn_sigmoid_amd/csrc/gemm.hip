@@ -316,6 +316,246 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined bf16 kernel for dense B operands.
+//
+// Tiles move from HBM straight into LDS with global_load_lds_dwordx4 (each
+// lane supplies its own global address -- row gathers included -- and the 64
+// lanes of an instruction fill 1 KB of LDS in lane order), through a ring of
+// three stages so that two tiles are in flight while the MFMAs consume the
+// third.  A stage holds BK = 64 or 32 K-elements per row (128- or 64-byte
+// rows); the 16-byte chunk index is XORed with a function of the row so that
+// both the lane-ordered fills and the 32-row fragment reads are free of bank
+// conflicts.  Each stage lives in its own __shared__ array, the waits count
+// only this wave's own loads (s_waitcnt vmcnt) and the barrier is fenced for
+// the compiler only, so loads stay in flight across barriers.  For SiTU-GLU
+// the gate and up rows of B alternate in groups of 32, so every wave holds
+// both halves of its outputs in registers; results are stored straight from
+// the accumulators.
+// ---------------------------------------------------------------------------
+constexpr int STAGES = 3;
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16-byte global -> LDS copy per lane (lane i fills bytes [16i, 16i+16) after
+// the wave-uniform LDS base).  The builtin exists only for the device pass;
+// the host pass of a template kernel that names it would drop its launch stub.
+__device__ __forceinline__ void load_lds16(const bf16_t* g, bf16_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#endif
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// chunk swizzle of a row: 128-byte rows XOR with r mod 8, 64-byte rows with
+// (r / 2) mod 4 (two rows share a 128-byte bank window)
+template <int BKP>
+__device__ __forceinline__ int swz(int r) {
+  return BKP == 64 ? (r & 7) : ((r >> 1) & 3);
+}
+
+template <int BM, int BN, int WM, int EPI, int BKP>
+__global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Params p) {
+  constexpr int WN = 4 / WM;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold 32x32 blocks");
+  static_assert(EPI != EPI_SITU || FN % 2 == 0, "SiTU needs gate/up fragment pairs");
+  static_assert(BKP == 64 || BKP == 32, "stage depth");
+  constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
+  constexpr int CH = BKP / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;       // rows per load instruction
+  constexpr int NA = BM / RPI, NB = BN / RPI;
+  static_assert(NA * RPI == BM && NB * RPI == BN, "tile rows per instruction");
+  constexpr int MA = (NA + 3) / 4, MB = (NB + 3) / 4;
+  // Every wave issues MA (MB) load instructions per stage; when 4 does not
+  // divide NA (NB) the surplus ones repeat instruction i-1 of the same wave's
+  // neighbour range (same source, same LDS bytes), so the per-wave count of
+  // outstanding loads is uniform and known at compile time.
+  auto a_ins = [](int w, int i) { const int x = w + 4 * i; return x < NA ? x : x - 4; };
+  auto b_ins = [](int w, int i) { const int x = w + 4 * i; return x < NB ? x : x - 4; };
+
+  __shared__ __attribute__((aligned(1024))) bf16_t sA0[BM * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA1[BM * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA2[BM * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB0[BN * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB1[BN * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB2[BN * BKP];
+
+  const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
+  Tile tile;
+  if (!locate_tile<BM>(p, ntn, BN_OUT, tile)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // rows this lane fills in each of its load instructions (clamped to valid
+  // rows; rows past the tile only feed outputs that are never stored)
+  const int lrow = lane / CH;
+  int64_t a_off[MA];  // row * lda + chunk * 8 is set per segment; here row and chunk
+  int a_chunk[MA];
+#pragma unroll
+  for (int i = 0; i < MA; ++i) {
+    const int ins = a_ins(wave, i);
+    int r = ins * RPI + lrow;
+    a_chunk[i] = (lane % CH) ^ swz<BKP>(r);
+    r = r < tile.rows ? r : 0;
+    const int slot = tile.row0 + r;
+    a_off[i] = p.a_rows ? p.a_rows[slot] : slot;
+  }
+  int64_t b_off[MB];
+  int b_chunk[MB];
+  bool b_up[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r = b_ins(wave, i) * RPI + lrow;
+    b_chunk[i] = (lane % CH) ^ swz<BKP>(r);
+    int row;
+    if (EPI == EPI_SITU) {
+      const int g = r >> 5;
+      b_up[i] = g & 1;
+      row = tile.n0 + (g >> 1) * 32 + (r & 31);
+    } else {
+      b_up[i] = false;
+      row = tile.n0 + r;
+    }
+    b_off[i] = row < p.N ? row : p.N - 1;
+  }
+
+  int ktot = 0;
+  for (int sg = 0; sg < p.nseg; ++sg) ktot += p.seg[sg].K / BKP;
+
+  // Per-lane source pointers of the next tile to issue; tiles are issued in
+  // order, so the pointers advance by BKP and are reset at segment starts.
+  const bf16_t* pa[MA];
+  const bf16_t* pb[MB];
+  int seg_i = -1, seg_end = 0, next_kt = 0;
+  auto start_segment = [&](int sg) {
+    const Seg& g = p.seg[sg];
+    const bf16_t* A = static_cast<const bf16_t*>(g.A);
+    const bf16_t* B = static_cast<const bf16_t*>(g.B) +
+                      static_cast<int64_t>(tile.expert) * p.b_expert_stride;
+    const bf16_t* B2 = static_cast<const bf16_t*>(g.B2) +
+                       static_cast<int64_t>(tile.expert) * p.b_expert_stride;
+#pragma unroll
+    for (int i = 0; i < MA; ++i) pa[i] = A + a_off[i] * g.lda + a_chunk[i] * 8;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) pb[i] = (b_up[i] ? B2 : B) + b_off[i] * g.ldb + b_chunk[i] * 8;
+  };
+  auto issue = [&](bf16_t* As, bf16_t* Bs) {
+    if (next_kt == seg_end) {
+      ++seg_i;
+      start_segment(seg_i);
+      seg_end += p.seg[seg_i].K / BKP;
+    }
+    ++next_kt;
+#pragma unroll
+    for (int i = 0; i < MA; ++i) {
+      load_lds16(pa[i], As + a_ins(wave, i) * 512);
+      pa[i] += BKP;
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      load_lds16(pb[i], Bs + b_ins(wave, i) * 512);
+      pb[i] += BKP;
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](const bf16_t* As, const bf16_t* Bs) {
+    const int hi = lane >> 5, sw = swz<BKP>(lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < BKP / 16; ++kk) {
+      const int ch = ((kk * 2 + hi) ^ sw) * 8;
+      bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WTM + i * 32 + (lane & 31)) * BKP + ch);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WTN + j * 32 + (lane & 31)) * BKP + ch);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // prologue: stages 0 and 1 in flight
+  if (ktot > 0) issue(sA0, sB0);
+  if (ktot > 1) issue(sA1, sB1);
+  // one ring step: wait for tile kt (tile kt+1 may stay in flight), refill the
+  // stage freed by tile kt-1 with tile kt+2, multiply tile kt
+  auto ring = [&](int kt, bf16_t* Ac, bf16_t* Bc, bf16_t* An, bf16_t* Bn) {
+    if (kt < ktot) {  // uniform across the block
+      if (kt + 1 < ktot)
+        wait_vmcnt<MA + MB>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + 2 < ktot) issue(An, Bn);
+      compute(Ac, Bc);
+    }
+  };
+  for (int kt = 0; kt < ktot; kt += STAGES) {
+    ring(kt, sA0, sB0, sA2, sB2);
+    ring(kt + 1, sA1, sB1, sA0, sB0);
+    ring(kt + 2, sA2, sB2, sA1, sB1);
+  }
+
+  // ---- epilogue straight from the accumulators ----
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      if (row >= tile.rows) continue;
+      const int64_t orow = tile.row0 + row;
+      if (EPI == EPI_SITU) {
+#pragma unroll
+        for (int j = 0; j < FN; j += 2) {
+          const int grp = wn * FN + j;  // even: gate group, odd: its up group
+          const int col = tile.n0 + (grp >> 1) * 32 + (lane & 31);
+          if (col < p.N)
+            static_cast<bf16_t*>(p.C)[orow * p.ldc + col] =
+                f32_to_bf16(situ_glu(acc[i][j][r], acc[i][j + 1][r]));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = tile.n0 + wn * WTN + j * 32 + (lane & 31);
+          if (col >= p.N) continue;
+          if (EPI == EPI_SIGMOID) {
+            float x = acc[i][j][r];
+            if (p.col_add) x += p.col_add[col];
+            static_cast<float*>(p.C)[orow * p.ldc + col] = 1.0f / (1.0f + expf(-x));
+          } else {
+            static_cast<bf16_t*>(p.C)[orow * p.ldc + col] = f32_to_bf16(acc[i][j][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (fp32 activations and weights): 64x64 tiles, 4x4 per thread,
 // BK = 16, same tile scheduling, segments, gather and epilogues.
 // ---------------------------------------------------------------------------
@@ -420,6 +660,31 @@ static int run_bf16(const Params& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+template <int BM, int BN, int WM, int EPI, int BKP>
+static int run_pipe(const Params& p, hipStream_t stream) {
+  constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
+  for (int s = 0; s < p.nseg; ++s)
+    if (p.seg[s].K % BKP != 0) return MOE_EUNSUPPORTED;
+  const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
+  const int mt = p.tiles ? p.max_mtiles : (p.M + BM - 1) / BM;
+  const int64_t G = static_cast<int64_t>(mt) * ntn;
+  if (G <= 0) return MOE_OK;
+  const int64_t G8 = (G + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP>), dim3(static_cast<unsigned>(G8)),
+                     dim3(NTHREADS), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+template <int BM, int BN, int WM, int BKP>
+static int dispatch_pipe(const Params& p, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_BF16: return run_pipe<BM, BN, WM, EPI_BF16, BKP>(p, s);
+    case EPI_SIGMOID: return run_pipe<BM, BN, WM, EPI_SIGMOID, BKP>(p, s);
+    case EPI_SITU: return run_pipe<BM, BN, WM, EPI_SITU, BKP>(p, s);
+    default: return MOE_EUNSUPPORTED;
+  }
+}
+
 template <int EPI>
 static int run_f32(const Params& p, hipStream_t stream) {
   constexpr int BN_OUT = (EPI == EPI_SITU) ? FB / 2 : FB;
@@ -454,12 +719,16 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
   }
   for (int s = 0; s < p.nseg; ++s)
     if (p.seg[s].K % BK != 0) return MOE_EUNSUPPORTED;
-  if (bm_hint <= 32) {
-    return bfmt == B_DENSE ? dispatch_epi<32, 256, 1, B_DENSE>(p, epi, stream)
-                           : dispatch_epi<32, 256, 1, B_MXFP4>(p, epi, stream);
+  if (bfmt == B_DENSE) {
+    // grouped problems stream expert weights: tiles as tall as the expected
+    // rows per expert and 256 columns wide (fewer re-reads of the gathered
+    // rows per weight byte); dense problems use square tiles
+    if (bm_hint <= 32) return dispatch_pipe<32, 256, 1, 64>(p, epi, stream);
+    if (p.tiles && bm_hint <= 96) return dispatch_pipe<96, 256, 1, 32>(p, epi, stream);
+    return dispatch_pipe<128, 128, 2, 32>(p, epi, stream);
   }
-  return bfmt == B_DENSE ? dispatch_epi<128, 128, 2, B_DENSE>(p, epi, stream)
-                         : dispatch_epi<128, 128, 2, B_MXFP4>(p, epi, stream);
+  if (bm_hint <= 32) return dispatch_epi<32, 256, 1, B_MXFP4>(p, epi, stream);
+  return dispatch_epi<128, 128, 2, B_MXFP4>(p, epi, stream);
 }
 
 }  // namespace gemm

@@ -10,6 +10,8 @@
 // latent aggregation, before the up-projection) and the shared expert (two
 // experts merged into one MLP of width 6144 at full width, added to the
 // routed output).
+#include <mutex>
+
 #include "common.hpp"
 #include "gemm.hpp"
 #include "prof.hpp"
@@ -191,9 +193,14 @@ struct ForwardWorkspace {
   int max_mtiles;
 };
 
+// Tile height of the grouped expert GEMMs, from the mean rows per expert
+// (exact under QB): 32 for decode-like batches, 96 up to 96 rows, else 128.
 static int grouped_bm(const moe_shape_t& s) {
   const int64_t avg = (static_cast<int64_t>(s.T) * s.top_k + s.n_experts - 1) / s.n_experts;
-  return (s.act_dtype == MOE_BF16 && avg <= 32) ? 32 : (s.act_dtype == MOE_BF16 ? 128 : 64);
+  if (s.act_dtype != MOE_BF16) return 64;
+  if (avg <= 32) return 32;
+  if (avg <= 96 && s.routed_dtype != MOE_MXFP4) return 96;
+  return 128;
 }
 
 static size_t forward_layout(const moe_shape_t& s, ForwardWorkspace* fw, void* base) {
@@ -247,6 +254,34 @@ static int validate(const moe_shape_t* sp, const moe_weights_t* w) {
     if (s.routed_dtype == MOE_MXFP4 && (!w->s_gate || !w->s_uproj || !w->s_dn)) return MOE_EINVAL;
   }
   return MOE_OK;
+}
+
+// Per-device side stream (default priority, non-blocking) on which the
+// routing-independent shared branch runs while the caller's stream does the
+// latency-bound routing; two events fork it from and join it back into the
+// caller's stream.  A per-device mutex is held for the whole forward call so
+// that concurrent calls on one device cannot interleave on the shared events.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false;
+};
+
+static SideStream* side_stream() {
+  static SideStream tab[64];
+  static std::mutex init_mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(init_mu);
+  SideStream& ss = tab[dev];
+  if (!ss.ok) {
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) return nullptr;
+    ss.ok = true;
+  }
+  return &ss;
 }
 
 static gemm::Seg seg(const void* A, int64_t lda, const void* B, int64_t ldb, int K) {
@@ -304,7 +339,17 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
   }
   const float* route_scores = scores_in ? scores_in : scores;
 
-  // 2. shared branch (independent of routing): z = x W_down^T, hs = SiTU(x Wgs^T, x Wus^T)
+  // 2. shared branch (independent of routing) on the side stream:
+  //    z = x W_down^T, hs = SiTU(x Wgs^T, x Wus^T)
+  SideStream* side = T > 0 ? side_stream() : nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  hipStream_t sst = st;
+  if (side) {
+    side_lock = std::unique_lock<std::mutex>(side->mu);
+    MOE_HIP_CHECK(hipEventRecord(side->fork, st));
+    MOE_HIP_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
+    sst = side->s;
+  }
   if (T > 0) {
     gemm::Params p{};
     p.M = T;
@@ -314,8 +359,8 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     p.C = f.z;
     p.ldc = L;
     {
-      prof::Scope sc(prof::ST_LATENT_DOWN, st);
-      if ((rc = gemm::launch(p, store_epi, gemm::B_DENSE, bf, 128, st)) != MOE_OK) return rc;
+      prof::Scope sc(prof::ST_LATENT_DOWN, sst);
+      if ((rc = gemm::launch(p, store_epi, gemm::B_DENSE, bf, 128, sst)) != MOE_OK) return rc;
     }
     gemm::Params q{};
     q.M = T;
@@ -325,9 +370,12 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     q.seg[0].B2 = wt.ws_up;
     q.C = f.hs;
     q.ldc = ms;
-    prof::Scope sc(prof::ST_SHARED_GATE_UP, st);
-    if ((rc = gemm::launch(q, gemm::EPI_SITU, gemm::B_DENSE, bf, 128, st)) != MOE_OK) return rc;
+    {
+      prof::Scope sc(prof::ST_SHARED_GATE_UP, sst);
+      if ((rc = gemm::launch(q, gemm::EPI_SITU, gemm::B_DENSE, bf, 128, sst)) != MOE_OK) return rc;
+    }
   }
+  if (side) MOE_HIP_CHECK(hipEventRecord(side->join, side->s));
 
   // 3. routing (QB or frozen bias)
   {
@@ -353,6 +401,7 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
   MOE_LAUNCH_CHECK();
   }
 
+  if (side) MOE_HIP_CHECK(hipStreamWaitEvent(st, side->join, 0));
   const bool mx = s.routed_dtype == MOE_MXFP4;
   const int bfmt = mx ? gemm::B_MXFP4 : gemm::B_DENSE;
   // 5. routed gate/up with SiTU-GLU: h[slot] = SiTU(z[perm[slot]] Wg_e^T, z[perm[slot]] Wu_e^T)

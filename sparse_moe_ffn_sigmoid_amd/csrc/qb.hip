@@ -37,7 +37,6 @@ constexpr int64_t DIST_INF = int64_t(1) << 52;
 constexpr uint64_t PACKED_INF = uint64_t(DIST_INF) << IDX_BITS;
 constexpr int MAX_NJ = 16;            // keys per lane: n <= 1024
 constexpr int TOPK_BLOCK = 256;       // 4 waves, one token per wave at a time
-constexpr int TOPK_GRID_MAX = 512;
 constexpr int MAX_K = 64;
 constexpr int STALL_ROUNDS = 3;
 constexpr int MAX_SAP_MOVES = 4096;
@@ -49,7 +48,7 @@ constexpr int64_t DELTA_MIN = int64_t(1) << 16;
 enum Phase : int64_t { PH_ROUNDS = 0, PH_SAP = 1, PH_DONE = 2, PH_FAILED = 3, PH_FROZEN = 4 };
 enum Ctrl {
   C_PHASE = 0, C_ROUNDS, C_BEST, C_SINCE, C_MOVES, C_IMB, C_RESID, C_STATUS, C_DELTA,
-  C_EDGES_VALID, C_CUR, C_SELECT_RAN, C_MAX_ROUNDS, C_LAST_D, C_LAST_HOPS, C_BF_PASSES,
+  C_EDGES_VALID, C_CUR, C_ROUND, C_MAX_ROUNDS, C_LAST_D, C_LAST_HOPS, C_BF_PASSES,
   C_COUNT = 32
 };
 enum Cnt { N_EDGES = 0, N_OVERFLOW, N_BIASRANGE, N_COUNT = 8 };
@@ -58,8 +57,22 @@ __host__ __device__ __forceinline__ int64_t target(int64_t T, int64_t n, int64_t
   return (T * k) / n + (e < (T * k) % n ? 1 : 0);
 }
 
+// rint(s * 2^40) for a score s in [0, 1] with integer operations only:
+// s = m * 2^(E-150) with m the 24-bit significand, so s * 2^40 = m * 2^(E-110);
+// a right shift rounds half to even.  Zero and subnormals give 0.
 __device__ __forceinline__ int64_t score_fixed(float s) {
-  return static_cast<int64_t>(rint(static_cast<double>(s) * 1099511627776.0));  // * 2^40
+  const uint32_t u = __float_as_uint(s);
+  const int E = static_cast<int>((u >> 23) & 255u);
+  if (E == 0) return 0;
+  const uint64_t m = (u & 0x7FFFFFu) | 0x800000u;
+  const int sh = E - 110;
+  if (sh >= 0) return static_cast<int64_t>(m << sh);
+  const int r = -sh;
+  if (r > 24) return 0;  // m < 2^24 <= 2^(r-1): below one half
+  const uint64_t q = m >> r;
+  const uint64_t rem = m & ((uint64_t(1) << r) - 1);
+  const uint64_t half = uint64_t(1) << (r - 1);
+  return static_cast<int64_t>(q + ((rem > half) || (rem == half && (q & 1))));
 }
 
 __device__ __forceinline__ uint64_t pack_key(int64_t sfx, int64_t b, int e) {
@@ -72,13 +85,34 @@ __device__ __forceinline__ int64_t floor_mid(int64_t a, int64_t b) {
   return (a >> 11) + (b >> 11) + (((a & 2047) + (b & 2047)) >> 11);
 }
 
+// Wave-wide maximum with DPP row operations fused into v_max_u32 (quad
+// swaps, row shifts, row broadcasts; lanes without a source read 0, neutral
+// for an unsigned max); lane 63 ends with the maximum, broadcast through a
+// scalar register.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t w =
+      static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
+  return v > w ? v : w;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x114>(v);  // row_shr:4
+  v = dpp_max_step<0x118>(v);  // row_shr:8
+  v = dpp_max_step<0x142>(v);  // row_bcast:15
+  v = dpp_max_step<0x143>(v);  // row_bcast:31
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// 64-bit maximum: the high words first, then the low words of the lanes that
+// hold the highest high word.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o);
-    v = v > w ? v : w;
-  }
-  return v;
+  const uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
+  const uint32_t H = wave_max_u32(hi);
+  const uint32_t L = wave_max_u32(hi == H ? lo : 0u);
+  return (static_cast<uint64_t>(H) << 32) | L;
 }
 
 struct Args {
@@ -88,15 +122,14 @@ struct Args {
   int64_t* bfx;          // [2][n] biases, ctrl[C_CUR] selects the live half
   int64_t* th_k;         // [T]
   int64_t* th_k1;        // [T]
-  int32_t* part_loads;   // [grid][n]
   int32_t* loads;        // [n]
+  int32_t* acc;          // [n] loads accumulated by the top-k pass
   int64_t* ctrl;         // [C_COUNT]
   int32_t* cnt;          // [N_COUNT]
   uint64_t* edges;       // [edge_cap]
   int32_t edge_cap;
   int32_t* idx;          // [T][k] or null
   float* w;              // [T][k] or null
-  int topk_grid;
 };
 
 // ---------------------------------------------------------------------------
@@ -111,7 +144,7 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
   }
   const bool emit_edges = (phase == PH_SAP) && !emit_out;
   extern __shared__ unsigned char smem_raw[];
-  int32_t* sload = reinterpret_cast<int32_t*>(smem_raw);                 // [n]
+  int32_t* sload = reinterpret_cast<int32_t*>(smem_raw);                 // [1024]
   int64_t* lowKp = reinterpret_cast<int64_t*>(sload + 1024);             // [4][64]
   int64_t* highKp = lowKp + 4 * EDGE_LIST_MAX;                           // [4][64]
   int32_t* lowE = reinterpret_cast<int32_t*>(highKp + 4 * EDGE_LIST_MAX);  // [4][64]
@@ -136,28 +169,39 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
   for (int t = blockIdx.x * 4 + wv; t < T; t += gridDim.x * 4) {
     const float* row = a.scores + static_cast<size_t>(t) * n;
     uint64_t key[MAX_NJ];
-    int64_t sfx[MAX_NJ];
 #pragma unroll
     for (int j = 0; j < MAX_NJ; ++j) {
       const int e = lane + 64 * j;
       key[j] = 0;
-      sfx[j] = 0;
-      if (j < nj && e < n) {
-        sfx[j] = score_fixed(row[e]);
-        key[j] = pack_key(sfx[j], bias[e], e);
-      }
+      if (j < nj && e < n) key[j] = pack_key(score_fixed(row[e]), bias[e], e);
     }
-    uint32_t taken = 0;
+    // Each lane sorts its keys (descending bitonic network); then every
+    // round takes the wave maximum of the lane heads and the winning lane
+    // (keys are distinct, so exactly one) pops its head.
+    uint64_t q[MAX_NJ];
+#pragma unroll
+    for (int j = 0; j < MAX_NJ; ++j) q[j] = key[j];
+#pragma unroll
+    for (int kk = 2; kk <= MAX_NJ; kk <<= 1)
+#pragma unroll
+      for (int jj = kk >> 1; jj > 0; jj >>= 1)
+#pragma unroll
+        for (int i = 0; i < MAX_NJ; ++i) {
+          const int l = i ^ jj;
+          if (l > i) {
+            const uint64_t x = q[i], y = q[l];
+            const bool sw = ((i & kk) == 0) ? (x < y) : (x > y);
+            q[i] = sw ? y : x;
+            q[l] = sw ? x : y;
+          }
+        }
     uint64_t thk = 0, thk1 = 0;
     for (int r = 0; r < rounds; ++r) {
-      uint64_t lm = 0;
+      const uint64_t wm = wave_max_u64(q[0]);
+      const bool win = q[0] == wm;
 #pragma unroll
-      for (int j = 0; j < MAX_NJ; ++j)
-        if (!((taken >> j) & 1u) && key[j] > lm) lm = key[j];
-      const uint64_t wm = wave_max_u64(lm);
-#pragma unroll
-      for (int j = 0; j < MAX_NJ; ++j)
-        if (key[j] == wm) taken |= 1u << j;
+      for (int j = 0; j < MAX_NJ - 1; ++j) q[j] = win ? q[j + 1] : q[j];
+      q[MAX_NJ - 1] = win ? 0 : q[MAX_NJ - 1];
       if (r == k - 1) thk = wm;
       if (r == k) thk1 = wm;
     }
@@ -183,8 +227,9 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
         if (sel) {
           const int pos = base + __popcll(bal & ((uint64_t(1) << lane) - 1));
           const int e = lane + 64 * j;
-          oSfx[wv * MAX_K + pos] = sfx[j];
-          oS[wv * MAX_K + pos] = row[e];
+          const float sv = row[e];
+          oSfx[wv * MAX_K + pos] = score_fixed(sv);
+          oS[wv * MAX_K + pos] = sv;
           oE[wv * MAX_K + pos] = e;
         }
         base += __popcll(bal);
@@ -228,7 +273,7 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
         for (int j = 0; j < MAX_NJ; ++j) {
           const int e = lane + 64 * j;
           const bool valid = key[j] != 0;
-          const int64_t kp = sfx[j] + (valid ? bias[e] : 0);
+          const int64_t kp = static_cast<int64_t>(key[j] >> IDX_BITS) - KEY_OFFSET;  // sfx + bias
           const bool sel = (selmask >> j) & 1u;
           const bool isLow = valid && sel && (kp - kpk <= delta + 1);
           const bool isHigh = valid && !sel && (kpk1 - kp <= delta + 1);
@@ -278,13 +323,13 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
     }
   }
   __syncthreads();
-  int32_t* part = a.part_loads + static_cast<size_t>(blockIdx.x) * n;
-  for (int e = threadIdx.x; e < n; e += blockDim.x) part[e] = sload[e];
+  for (int e = threadIdx.x; e < n; e += blockDim.x)
+    if (sload[e]) atomicAdd(&a.acc[e], sload[e]);
   if (emit_edges && blockIdx.x == 0 && threadIdx.x == 0) a.ctrl[C_EDGES_VALID] = 1;
 }
 
 // ---------------------------------------------------------------------------
-// Status: reduce the per-block loads, then decide the next phase exactly as
+// Status: take the accumulated loads (and clear the accumulator), then decide the next phase exactly as
 // the schedule prescribes (rounds until the unbalanced count stalls, then
 // augmenting paths, then done).
 // ---------------------------------------------------------------------------
@@ -293,8 +338,8 @@ __global__ __launch_bounds__(1024) void status_pass(Args a) {
   const int n = a.n;
   int imb = 0, res = 0;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    int32_t L = 0;
-    for (int b = 0; b < a.topk_grid; ++b) L += a.part_loads[static_cast<size_t>(b) * n + e];
+    const int32_t L = a.acc[e];
+    a.acc[e] = 0;
     a.loads[e] = L;
     const int64_t d = static_cast<int64_t>(L) - target(a.T, n, a.k, e);
     imb += d != 0;
@@ -318,6 +363,7 @@ __global__ __launch_bounds__(1024) void status_pass(Args a) {
   c[C_RESID] = s_res[0];
   const int64_t ph = c[C_PHASE];
   if (ph == PH_ROUNDS) {
+    bool round = false;
     if (imb == 0) {
       c[C_PHASE] = PH_DONE;
     } else if (c[C_ROUNDS] >= c[C_MAX_ROUNDS]) {
@@ -325,9 +371,13 @@ __global__ __launch_bounds__(1024) void status_pass(Args a) {
     } else if (c[C_BEST] < 0 || imb < c[C_BEST]) {
       c[C_BEST] = imb;
       c[C_SINCE] = 0;
+      round = true;
     } else if (++c[C_SINCE] >= STALL_ROUNDS) {
       c[C_PHASE] = PH_SAP;
+    } else {
+      round = true;
     }
+    c[C_ROUND] = round ? 1 : 0;  // the quantile kernel runs, the finish kernel commits
   } else if (ph == PH_SAP) {
     if (imb == 0) {
       c[C_PHASE] = PH_DONE;
@@ -339,89 +389,68 @@ __global__ __launch_bounds__(1024) void status_pass(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// One quantile round: every unbalanced expert computes the C-th and (C+1)-th
-// largest margins over all tokens by an exact MSB-first radix select (10-bit
-// digits on the order-preserving uint64 image of the int64 margin) and jumps
-// to minus their midpoint.  One block per expert, reading the transposed
-// scores so the column is contiguous.
+// One quantile round (one block per expert, reading the transposed scores so
+// the column is contiguous): an unbalanced expert finds the C-th and
+// (C+1)-th largest margins over all tokens exactly and jumps to minus their
+// midpoint.  New biases go to the idle bias buffer; the finish kernel makes
+// them live.
+//
+// Selection: one pass bins d = margin - cut (the cut is -1024*bias; d > 0 iff
+// the token currently picks the expert) into 2048 order-preserving buckets
+// that are exact near zero and ~6% wide far from it, a block scan finds the
+// buckets holding the two ranks, a second pass gathers those one or two
+// buckets into LDS and the ranks are resolved by exact counting.  A bucket
+// too large for LDS falls back to an MSB-first radix select.
 // ---------------------------------------------------------------------------
 constexpr int SEL_BLOCK = 256;
+constexpr int NBUCKET = 2048;
+constexpr int GATHER_CAP = 4096;
 constexpr int DIG = 10;
 constexpr int NBIN = 1 << DIG;
 
-__device__ __forceinline__ uint64_t margin_u(const Args& a, const int64_t* bias, int e,
-                                             int t) {
+__device__ __forceinline__ int64_t margin_of(const Args& a, const int64_t* bias, int e, int t) {
   const int64_t sfx = score_fixed(a.scoresT[static_cast<size_t>(e) * a.T + t]);
   const uint64_t key = pack_key(sfx, bias[e], e);
   const int64_t thk = a.th_k[t];
   const bool sel = static_cast<int64_t>(key) >= thk;
   const int64_t base = static_cast<int64_t>(pack_key(sfx, 0, e));
-  const int64_t M = base - (sel ? a.th_k1[t] : thk);
-  return static_cast<uint64_t>(M) ^ (uint64_t(1) << 63);
+  return base - (sel ? a.th_k1[t] : thk);
 }
 
-__global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
-  if (a.ctrl[C_PHASE] != PH_ROUNDS) return;
-  const int e = blockIdx.x;
-  const int n = a.n, T = a.T;
-  const int cur = static_cast<int>(a.ctrl[C_CUR] & 1);
-  const int64_t* bias = a.bfx + cur * n;
-  int64_t* nb = a.bfx + (cur ^ 1) * n;
-  const int64_t C = target(T, n, a.k, e);
-  if (a.loads[e] == C) {
-    if (threadIdx.x == 0) nb[e] = bias[e];
-    return;
-  }
-  __shared__ int32_t h1[NBIN], h2[NBIN];
-  __shared__ uint64_t s_min[SEL_BLOCK], s_max[SEL_BLOCK];
+__device__ __forceinline__ int log_code(uint64_t x) {
+  if (x < 16) return static_cast<int>(x);
+  const int msb = 63 - __clzll(static_cast<long long>(x));
+  return 16 + (msb - 4) * 16 + static_cast<int>((x >> (msb - 4)) & 15);
+}
+
+// order-preserving bucket of d: [0, 1024) for d <= 0, [1024, 2048) for d > 0
+__device__ __forceinline__ int bucket_of(int64_t d) {
+  return d > 0 ? 1024 + log_code(static_cast<uint64_t>(d - 1))
+               : 1023 - log_code(static_cast<uint64_t>(-d));
+}
+
+// Exact value of descending ranks r1 <= r2 among all margins (radix select on
+// the order-preserving uint64 image); used when a bucket overflows LDS.
+__device__ void radix_select2(const Args& a, const int64_t* bias, int e, int64_t r1, int64_t r2,
+                              int32_t* h1, int32_t* h2, int64_t* out) {
   __shared__ uint64_t s_pre[2];
   __shared__ int64_t s_rem[2];
-  __shared__ int s_shift;
-
-  // ranks wanted (1-indexed, descending): r1 = C, r2 = C+1, with the edge cases
-  // C == 0 (only the maximum) and C == T (only the minimum).
-  int64_t r1 = C, r2 = C + 1;
-  if (C == 0) r1 = r2 = 1;
-  if (C == T) r1 = r2 = T;
-
-  uint64_t mn = ~uint64_t(0), mx = 0;
-  for (int t = threadIdx.x; t < T; t += SEL_BLOCK) {
-    const uint64_t u = margin_u(a, bias, e, t);
-    mn = u < mn ? u : mn;
-    mx = u > mx ? u : mx;
-  }
-  s_min[threadIdx.x] = mn;
-  s_max[threadIdx.x] = mx;
-  __syncthreads();
-  for (int s = SEL_BLOCK / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
-      s_min[threadIdx.x] = min(s_min[threadIdx.x], s_min[threadIdx.x + s]);
-      s_max[threadIdx.x] = max(s_max[threadIdx.x], s_max[threadIdx.x + s]);
-    }
-    __syncthreads();
-  }
-  mn = s_min[0];
-  mx = s_max[0];
-  // bits above `top` are shared by every margin
-  const int top = (mn == mx) ? 0 : 64 - __clzll(static_cast<long long>(mn ^ mx));
-  const uint64_t common = (top == 64) ? 0 : (mn >> top) << top;
   if (threadIdx.x == 0) {
-    s_pre[0] = s_pre[1] = common;
+    s_pre[0] = s_pre[1] = 0;
     s_rem[0] = r1;
     s_rem[1] = r2;
   }
-  uint64_t mask = (top == 64) ? 0 : ~((uint64_t(1) << top) - 1);
-  int shift = top;
   __syncthreads();
-  while (shift > 0) {
+  uint64_t mask = 0;
+  for (int shift = 64; shift > 0;) {
     const int nbits = shift >= DIG ? DIG : shift;
     shift -= nbits;
     for (int i = threadIdx.x; i < NBIN; i += SEL_BLOCK) h1[i] = h2[i] = 0;
     __syncthreads();
     const uint64_t p1 = s_pre[0], p2 = s_pre[1];
     const uint64_t dmask = (uint64_t(1) << nbits) - 1;
-    for (int t = threadIdx.x; t < T; t += SEL_BLOCK) {
-      const uint64_t u = margin_u(a, bias, e, t);
+    for (int t = threadIdx.x; t < a.T; t += SEL_BLOCK) {
+      const uint64_t u = static_cast<uint64_t>(margin_of(a, bias, e, t)) ^ (uint64_t(1) << 63);
       const int dg = static_cast<int>((u >> shift) & dmask);
       if ((u & mask) == p1) atomicAdd(&h1[dg], 1);
       if ((u & mask) == p2) atomicAdd(&h2[dg], 1);
@@ -445,8 +474,107 @@ __global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const int64_t m1 = static_cast<int64_t>(s_pre[0] ^ (uint64_t(1) << 63));
-    const int64_t m2 = static_cast<int64_t>(s_pre[1] ^ (uint64_t(1) << 63));
+    out[0] = static_cast<int64_t>(s_pre[0] ^ (uint64_t(1) << 63));
+    out[1] = static_cast<int64_t>(s_pre[1] ^ (uint64_t(1) << 63));
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
+  if (a.ctrl[C_PHASE] != PH_ROUNDS || a.ctrl[C_ROUND] == 0) return;
+  const int e = blockIdx.x;
+  const int n = a.n, T = a.T;
+  const int cur = static_cast<int>(a.ctrl[C_CUR] & 1);
+  const int64_t* bias = a.bfx + cur * n;
+  int64_t* nb = a.bfx + (cur ^ 1) * n;
+  const int64_t C = target(T, n, a.k, e);
+  if (a.loads[e] == C) {  // the lazy rule: balanced experts keep their bias
+    if (threadIdx.x == 0) nb[e] = bias[e];
+    return;
+  }
+  __shared__ int32_t hist[NBUCKET];
+  __shared__ int64_t gat[GATHER_CAP];
+  __shared__ int32_t scan[SEL_BLOCK];
+  __shared__ int s_bucket[2];
+  __shared__ int64_t s_above[2];
+  __shared__ int s_cnt;
+  __shared__ int64_t s_val[2];
+  const int tid = threadIdx.x;
+  const int64_t cut = -bias[e] * 1024;
+
+  for (int i = tid; i < NBUCKET; i += SEL_BLOCK) hist[i] = 0;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  for (int t = tid; t < T; t += SEL_BLOCK)
+    atomicAdd(&hist[bucket_of(margin_of(a, bias, e, t) - cut)], 1);
+  __syncthreads();
+
+  // descending ranks: r1 = C, r2 = C+1, or a single rank at the edges
+  int64_t r1 = C, r2 = C + 1;
+  if (C == 0) r1 = r2 = 1;
+  if (C == T) r1 = r2 = T;
+  // thread i owns buckets [2048 - 8(i+1), 2048 - 8i): counts in descending order
+  constexpr int PER = NBUCKET / SEL_BLOCK;
+  int32_t own = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) own += hist[NBUCKET - 1 - (tid * PER + j)];
+  scan[tid] = own;
+  __syncthreads();
+  for (int off = 1; off < SEL_BLOCK; off <<= 1) {
+    const int32_t v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const int64_t before = scan[tid] - own;  // values in buckets above this thread's chunk
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t r = q == 0 ? r1 : r2;
+    if (before < r && r <= scan[tid]) {
+      int64_t acc = before;
+      for (int j = 0; j < PER; ++j) {
+        const int b = NBUCKET - 1 - (tid * PER + j);
+        if (acc + hist[b] >= r) {
+          s_bucket[q] = b;
+          s_above[q] = acc;
+          break;
+        }
+        acc += hist[b];
+      }
+    }
+  }
+  __syncthreads();
+  const int b1 = s_bucket[0], b2 = s_bucket[1];  // b2 <= b1
+  for (int t = tid; t < T; t += SEL_BLOCK) {
+    const int64_t M = margin_of(a, bias, e, t);
+    const int b = bucket_of(M - cut);
+    if (b <= b1 && b >= b2) {
+      const int pos = atomicAdd(&s_cnt, 1);
+      if (pos < GATHER_CAP) gat[pos] = M;
+    }
+  }
+  __syncthreads();
+  const int cnt = s_cnt;
+  if (cnt <= GATHER_CAP) {
+    // ranks inside the gathered set (everything in buckets above b1 is larger)
+    const int64_t q1 = r1 - s_above[0], q2 = r2 - s_above[0];
+    for (int i = tid; i < cnt; i += SEL_BLOCK) {
+      const int64_t v = gat[i];
+      int64_t g = 0, ge = 0;
+      for (int j = 0; j < cnt; ++j) {
+        const int64_t w = gat[j];
+        g += w > v;
+        ge += w >= v;
+      }
+      if (g < q1 && q1 <= ge) s_val[0] = v;
+      if (g < q2 && q2 <= ge) s_val[1] = v;
+    }
+    __syncthreads();
+  } else {
+    radix_select2(a, bias, e, r1, r2, hist, hist + NBIN, s_val);
+  }
+  if (tid == 0) {
+    const int64_t m1 = s_val[0], m2 = s_val[1];
     int64_t b;
     if (C == 0)
       b = -(m1 >> IDX_BITS) - 1;
@@ -456,14 +584,12 @@ __global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
       b = -floor_mid(m1, m2);
     nb[e] = b;
     if (b >= BIAS_LIMIT || b <= -BIAS_LIMIT) atomicOr(&a.cnt[N_BIASRANGE], 1);
-    a.ctrl[C_SELECT_RAN] = 1;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Finish a step (one block of 1024 threads): after a quantile round flip the
-// live bias buffer; in the augmenting-path phase solve one move on the
-// sparse edge list.
+// Finish a step (one block of 1024 threads): make a quantile round's biases
+// live, or make one augmenting-path move on this step's sparse edge list.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void finish_step(Args a) {
   int64_t* c = a.ctrl;
@@ -475,11 +601,13 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
   __shared__ int s_flag;
   __shared__ int s_path[1025];
   __shared__ int s_len;
+  constexpr int EDGE_CACHE = 8192;
+  __shared__ uint64_t s_edges[EDGE_CACHE];
 
   const int64_t ph = c[C_PHASE];
   if (ph == PH_ROUNDS) {
-    if (tid == 0 && c[C_SELECT_RAN]) {
-      c[C_SELECT_RAN] = 0;
+    if (tid == 0 && c[C_ROUND]) {
+      c[C_ROUND] = 0;
       c[C_CUR] ^= 1;
       c[C_ROUNDS] += 1;
       if (a.cnt[N_BIASRANGE]) {
@@ -519,14 +647,28 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
     under_e = a.loads[tid] < C;
     d[tid] = over_e ? static_cast<uint64_t>(tid) : PACKED_INF;
   }
+  const bool cached = nedges <= EDGE_CACHE;
+  if (cached)
+    for (int i = tid; i < nedges; i += blockDim.x) s_edges[i] = a.edges[i];
   __syncthreads();
-  int64_t D = DIST_INF;
+  // Relaxation passes.  s_D is the running minimum distance of an
+  // underloaded expert (it only decreases); a pass that lowers some distance
+  // to at most s_D asks for another pass.  Flagging against the running value
+  // flags a superset of "changed at or below the final D*", so the passes
+  // stop only when every distance <= D* and its predecessor is final.
+  __shared__ unsigned long long s_D;
+  __shared__ int s_under[1024];
+  if (tid < n) s_under[tid] = under_e;
+  if (tid == 0) s_D = static_cast<unsigned long long>(DIST_INF);
+  __syncthreads();
+  if (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) < DIST_INF)
+    atomicMin(&s_D, static_cast<unsigned long long>(d[tid] >> IDX_BITS));
   int passes = 0;
   while (true) {
-    if (tid < n) dprev[tid] = d[tid];
+    if (tid == 0) s_flag = 0;
     __syncthreads();
     for (int i = tid; i < nedges; i += blockDim.x) {
-      const uint64_t ed = a.edges[i];
+      const uint64_t ed = cached ? s_edges[i] : a.edges[i];
       const int B = static_cast<int>(ed & 1023);
       const int A = static_cast<int>((ed >> 10) & 1023);
       const int64_t rho = static_cast<int64_t>(ed >> 20);
@@ -535,26 +677,21 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
       const int64_t cand = dA + rho;
       if (cand >= DIST_INF) continue;
       const uint64_t pk = (static_cast<uint64_t>(cand) << IDX_BITS) | static_cast<uint64_t>(A);
-      if (pk < d[B]) atomicMin(reinterpret_cast<unsigned long long*>(&d[B]), pk);
+      if (pk < d[B]) {
+        const uint64_t old = atomicMin(reinterpret_cast<unsigned long long*>(&d[B]), pk);
+        if (pk < old) {
+          if (s_under[B]) atomicMin(&s_D, static_cast<unsigned long long>(cand));
+          if (static_cast<uint64_t>(cand) <= s_D) s_flag = 1;
+        }
+      }
     }
-    __syncthreads();
-    s_red[tid] = (tid < n && under_e) ? static_cast<int64_t>(d[tid] >> IDX_BITS) : DIST_INF;
-    __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
-      if (tid < s) s_red[tid] = min(s_red[tid], s_red[tid + s]);
-      __syncthreads();
-    }
-    D = s_red[0];
-    if (tid == 0) s_flag = 0;
-    __syncthreads();
-    if (tid < n && d[tid] != dprev[tid] && static_cast<int64_t>(d[tid] >> IDX_BITS) <= D)
-      s_flag = 1;
     __syncthreads();
     ++passes;
     const int go = s_flag;
     __syncthreads();
     if (!go || passes > 4 * 1024) break;
   }
+  const int64_t D = static_cast<int64_t>(s_D);
   if (D >= DIST_INF || D > delta) {
     if (tid == 0) {
       if (delta >= DELTA_MAX) {
@@ -638,6 +775,7 @@ __global__ void init_ctrl(Args a, const double* bias_in, int mode, int max_round
     }
     a.bfx[e] = v;
     a.bfx[n + e] = v;
+    a.acc[e] = 0;
   }
   if (threadIdx.x == 0) {
     int64_t* c = a.ctrl;
@@ -735,14 +873,26 @@ size_t route_workspace_layout(int32_t T, int32_t n, RouteWorkspace* ws, void* ba
   w.bfx = cv.take<int64_t>(2 * static_cast<size_t>(n));
   w.th_k = cv.take<int64_t>(T);
   w.th_k1 = cv.take<int64_t>(T);
-  w.part_loads = cv.take<int32_t>(static_cast<size_t>(qb::TOPK_GRID_MAX) * n);
   w.loads = cv.take<int32_t>(n);
+  w.acc = cv.take<int32_t>(n);
   w.ctrl = cv.take<int64_t>(qb::C_COUNT);
   w.cnt = cv.take<int32_t>(qb::N_COUNT);
   w.edge_cap = edge_capacity(T);
   w.edges = cv.take<uint64_t>(w.edge_cap);
   if (ws) *ws = w;
   return cv.bytes();
+}
+
+// Pinned host word the balancing loop polls (one per host thread, allocated
+// on first use and kept for the life of the process).
+static int64_t* phase_word() {
+  thread_local int64_t* word = nullptr;
+  if (!word) {
+    void* p = nullptr;
+    if (hipHostMalloc(&p, 64, hipHostMallocDefault) != hipSuccess) return nullptr;
+    word = static_cast<int64_t*>(p);
+  }
+  return word;
 }
 
 int route_validate(int32_t T, int32_t n, int32_t k) {
@@ -766,16 +916,15 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
   a.bfx = ws.bfx;
   a.th_k = ws.th_k;
   a.th_k1 = ws.th_k1;
-  a.part_loads = ws.part_loads;
   a.loads = ws.loads;
+  a.acc = ws.acc;
   a.ctrl = ws.ctrl;
   a.cnt = ws.cnt;
   a.edges = ws.edges;
   a.edge_cap = ws.edge_cap;
   a.idx = idx;
   a.w = w;
-  const int grid = T > 0 ? ((T + 3) / 4 < TOPK_GRID_MAX ? (T + 3) / 4 : TOPK_GRID_MAX) : 1;
-  a.topk_grid = grid;
+  const int grid = T > 0 ? (T + 3) / 4 : 1;  // one token per wave
   if (max_rounds <= 0) max_rounds = 64;
   const size_t smem = topk_smem_bytes();
 
@@ -790,6 +939,8 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
     dim3 tg((T + 63) / 64, (n + 63) / 64);
     hipLaunchKernelGGL(transpose_scores, tg, dim3(256), 0, stream, scores, ws.scoresT, T, n);
     MOE_LAUNCH_CHECK();
+  }
+  if (mode == MOE_QB_BATCH && T > 0) {
     const int batch = 4;
     const int max_steps = max_rounds + 8 * MAX_SAP_MOVES + 64;
     int steps = 0;
@@ -802,10 +953,12 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
       }
       MOE_LAUNCH_CHECK();
       steps += batch;
-      int64_t phase = 0;
-      MOE_HIP_CHECK(hipMemcpyAsync(&phase, ws.ctrl + C_PHASE, sizeof(int64_t),
+      int64_t* hp = phase_word();
+      if (!hp) return MOE_EHIP;
+      MOE_HIP_CHECK(hipMemcpyAsync(hp, ws.ctrl + C_PHASE, sizeof(int64_t),
                                    hipMemcpyDeviceToHost, stream));
       MOE_HIP_CHECK(hipStreamSynchronize(stream));
+      const int64_t phase = *hp;
       if (phase == PH_DONE || phase == PH_FAILED) break;
       if (steps >= max_steps) break;
     }
@@ -813,7 +966,6 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
   // final pass: centred bias, ordered outputs, loads
   hipLaunchKernelGGL(center_and_export, dim3(1), dim3(1024), 0, stream, a,
                      mode == MOE_QB_BATCH ? bias : nullptr, info);
-  // with T == 0 this still writes zero per-block loads for the status pass
   hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 1);
   hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), 0, stream, a);
   hipLaunchKernelGGL(export_resid, dim3(1), dim3(64), 0, stream, a, info);

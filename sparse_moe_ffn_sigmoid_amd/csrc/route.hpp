@@ -11,8 +11,8 @@ struct RouteWorkspace {
   int64_t* bfx;         // [2][n] fixed-point biases (live half chosen on the device)
   int64_t* th_k;        // [T] k-th largest key per token
   int64_t* th_k1;       // [T] (k+1)-th largest key per token
-  int32_t* part_loads;  // [blocks][n] per-block loads of the top-k pass
   int32_t* loads;       // [n]
+  int32_t* acc;         // [n] load accumulator of the top-k pass (cleared by the status pass)
   int64_t* ctrl;        // control words (phase, counters)
   int32_t* cnt;         // edge count and error flags
   uint64_t* edges;      // sparse edge list of the augmenting-path phase
