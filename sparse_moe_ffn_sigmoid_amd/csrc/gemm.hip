@@ -33,24 +33,34 @@ struct Tile {
 
 // Block -> tile, with consecutive tiles kept on one XCD (blocks are dealt to
 // the 8 XCDs round robin), M-tile-major so one XCD's L2 reuses the A rows.
+// Grouped problems launch for an upper bound on the tile count; the mapping
+// spreads only the tiles that exist (the device count) over the XCDs and the
+// surplus blocks exit.
 template <int BM>
 __device__ __forceinline__ bool locate_tile(const Params& p, int ntn, int bn_out, Tile& t) {
-  const int G = gridDim.x;
   const int b = blockIdx.x;
-  const int tau = (b & 7) * (G >> 3) + (b >> 3);
-  const int mt = tau / ntn, nt = tau - (tau / ntn) * ntn;
   if (p.tiles) {
-    if (mt >= *p.ntiles) return false;
+    const int nt_m = *p.ntiles;
+    const int gv = nt_m * ntn;
+    const int gv8 = (gv + 7) & ~7;
+    if (b >= gv8) return false;
+    const int tau = (b & 7) * (gv8 >> 3) + (b >> 3);
+    if (tau >= gv) return false;
+    const int mt = tau / ntn, nt = tau - mt * ntn;
     const int32_t* q = p.tiles + 4 * mt;
     t.expert = q[0];
     t.row0 = q[1];
     t.rows = q[2];
-  } else {
-    t.expert = 0;
-    t.row0 = mt * BM;
-    if (t.row0 >= p.M) return false;
-    t.rows = min(BM, p.M - t.row0);
+    t.n0 = nt * bn_out;
+    return true;
   }
+  const int G = gridDim.x;
+  const int tau = (b & 7) * (G >> 3) + (b >> 3);
+  const int mt = tau / ntn, nt = tau - mt * ntn;
+  t.expert = 0;
+  t.row0 = mt * BM;
+  if (t.row0 >= p.M) return false;
+  t.rows = min(BM, p.M - t.row0);
   t.n0 = nt * bn_out;
   return true;
 }
@@ -392,7 +402,22 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Param
 
   const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
   Tile tile;
-  if (!locate_tile<BM>(p, ntn, BN_OUT, tile)) return;
+  int ks = 0;  // K split of this block (dense problems with few tiles)
+  const int kn = p.ksplit > 1 ? p.ksplit : 1;
+  if (kn > 1) {
+    const int G = gridDim.x, b = blockIdx.x;
+    int tau = (b & 7) * (G >> 3) + (b >> 3);
+    ks = tau % kn;
+    tau /= kn;
+    const int mt = tau / ntn;
+    tile.expert = 0;
+    tile.row0 = mt * BM;
+    if (tile.row0 >= p.M) return;
+    tile.rows = min(BM, p.M - tile.row0);
+    tile.n0 = (tau - mt * ntn) * BN_OUT;
+  } else if (!locate_tile<BM>(p, ntn, BN_OUT, tile)) {
+    return;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -431,30 +456,42 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Param
     b_off[i] = row < p.N ? row : p.N - 1;
   }
 
-  int ktot = 0;
-  for (int sg = 0; sg < p.nseg; ++sg) ktot += p.seg[sg].K / BKP;
+  int kall = 0;
+  for (int sg = 0; sg < p.nseg; ++sg) kall += p.seg[sg].K / BKP;
+  // this block's K stages [k_begin, k_begin + ktot) of the concatenated segments
+  const int k_begin = (ks * kall) / kn;
+  const int ktot = ((ks + 1) * kall) / kn - k_begin;
 
   // Per-lane source pointers of the next tile to issue; tiles are issued in
   // order, so the pointers advance by BKP and are reset at segment starts.
   const bf16_t* pa[MA];
   const bf16_t* pb[MB];
-  int seg_i = -1, seg_end = 0, next_kt = 0;
-  auto start_segment = [&](int sg) {
+  int seg_i = -1, seg_end = 0, next_kt = k_begin;
+  auto start_segment = [&](int sg, int skip) {
     const Seg& g = p.seg[sg];
-    const bf16_t* A = static_cast<const bf16_t*>(g.A);
+    const bf16_t* A = static_cast<const bf16_t*>(g.A) + skip;
     const bf16_t* B = static_cast<const bf16_t*>(g.B) +
-                      static_cast<int64_t>(tile.expert) * p.b_expert_stride;
+                      static_cast<int64_t>(tile.expert) * p.b_expert_stride + skip;
     const bf16_t* B2 = static_cast<const bf16_t*>(g.B2) +
-                       static_cast<int64_t>(tile.expert) * p.b_expert_stride;
+                       static_cast<int64_t>(tile.expert) * p.b_expert_stride + skip;
 #pragma unroll
     for (int i = 0; i < MA; ++i) pa[i] = A + a_off[i] * g.lda + a_chunk[i] * 8;
 #pragma unroll
     for (int i = 0; i < MB; ++i) pb[i] = (b_up[i] ? B2 : B) + b_off[i] * g.ldb + b_chunk[i] * 8;
   };
+  if (ktot > 0) {  // position the walk at k_begin
+    int seg_start = 0;
+    do {
+      ++seg_i;
+      seg_start = seg_end;
+      seg_end += p.seg[seg_i].K / BKP;
+    } while (seg_end <= k_begin);
+    start_segment(seg_i, (k_begin - seg_start) * BKP);
+  }
   auto issue = [&](bf16_t* As, bf16_t* Bs) {
     if (next_kt == seg_end) {
       ++seg_i;
-      start_segment(seg_i);
+      start_segment(seg_i, 0);
       seg_end += p.seg[seg_i].K / BKP;
     }
     ++next_kt;
@@ -521,6 +558,21 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Param
   }
 
   // ---- epilogue straight from the accumulators ----
+  if (kn > 1) {  // fp32 partials, columns in B-row order of the tile
+    const int64_t nv = static_cast<int64_t>(ntn) * BN;
+    const int64_t cb = static_cast<int64_t>(tile.n0 / BN_OUT) * BN + wn * WTN + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (row >= tile.rows) continue;
+        float* dst = p.partial + (static_cast<int64_t>(ks) * p.M + tile.row0 + row) * nv + cb;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dst[j * 32] = acc[i][j][r];
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -546,9 +598,242 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Param
             float x = acc[i][j][r];
             if (p.col_add) x += p.col_add[col];
             static_cast<float*>(p.C)[orow * p.ldc + col] = 1.0f / (1.0f + expf(-x));
+          } else if (EPI == EPI_F32) {
+            static_cast<float*>(p.C)[orow * p.ldc + col] = acc[i][j][r];
           } else {
             static_cast<bf16_t*>(p.C)[orow * p.ldc + col] = f32_to_bf16(acc[i][j][r]);
           }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel with MXFP4 B operands (bf16 A).
+//
+// Same ring as gemm_pipe with 64 K-elements per stage; the B stage holds the
+// raw codes (32 bytes per row), copied straight to LDS.  The E8M0 scales of
+// the block's B rows for the whole K range (K/32 bytes per row) are copied to
+// an LDS panel once, before the ring starts.  The K order inside a stage is
+// permuted identically for A and B so that each lane's codes for a whole
+// stage are one 16-byte LDS read under a single scale byte: MFMA step kk of
+// lane half h uses the 8 elements of chunk 4h + kk.  Codes are decoded with
+// v_cvt_scalef32_pk_bf16_fp4 (two E2M1 values times the block scale per
+// instruction).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load_lds16_raw(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#endif
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 8 E2M1 codes (one word, element 0 in the low nibble) times the scale -> 8 bf16
+__device__ __forceinline__ bf16x8_t decode8_hw(uint32_t q, float scale) {
+  bf16x8_t out = {};
+#if defined(__HIP_DEVICE_COMPILE__)
+  const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 0);
+  const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 1);
+  const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 2);
+  const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 3);
+  out[0] = v0[0]; out[1] = v0[1]; out[2] = v1[0]; out[3] = v1[1];
+  out[4] = v2[0]; out[5] = v2[1]; out[6] = v3[0]; out[7] = v3[1];
+#endif
+  return out;
+}
+
+// E8M0 byte -> fp32 2^(e-127) (e = 0 gives the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+template <int BM, int BN, int WM, int EPI>
+__global__ __launch_bounds__(NTHREADS, 2) void gemm_pipe_fp4(Params p) {
+  constexpr int BKP = 64;
+  constexpr int WN = 4 / WM;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold 32x32 blocks");
+  static_assert(EPI != EPI_SITU || FN % 2 == 0, "SiTU needs gate/up fragment pairs");
+  constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
+  constexpr int NA = BM / 8, NQ = BN / 32;
+  static_assert(NA * 8 == BM && NQ * 32 == BN, "tile rows per instruction");
+  constexpr int MA = (NA + 3) / 4, MQ = (NQ + 3) / 4;
+  static_assert(NA % 4 == 0 && NQ % 4 == 0, "uniform load instructions per wave");
+
+  __shared__ __attribute__((aligned(1024))) bf16_t sA0[BM * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA1[BM * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA2[BM * BKP];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ0[BN * 32];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ1[BN * 32];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ2[BN * 32];
+  // scale panel [BN][K/32], sized by the launch
+  extern __shared__ __attribute__((aligned(16))) uint8_t sP[];
+
+  const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
+  Tile tile;
+  if (!locate_tile<BM>(p, ntn, BN_OUT, tile)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const Seg& g = p.seg[0];  // one K segment (checked by the launcher)
+
+  // tile row -> B row (gate/up groups of 32 for SiTU), clamped below N
+  auto b_row_of = [&](int r, bool& up) {
+    int row;
+    if (EPI == EPI_SITU) {
+      const int grp = r >> 5;
+      up = grp & 1;
+      row = tile.n0 + (grp >> 1) * 32 + (r & 31);
+    } else {
+      up = false;
+      row = tile.n0 + r;
+    }
+    return static_cast<int64_t>(row < p.N ? row : p.N - 1);
+  };
+
+  // scale panel: 16-byte pieces of each B row's K/32 scale bytes
+  const int sp = static_cast<int>(g.ldb >> 4);  // scale bytes per row (multiple of 16)
+  {
+    const uint8_t* S = g.Bs + static_cast<int64_t>(tile.expert) * p.bs_expert_stride;
+    const uint8_t* S2 = g.Bs2 + static_cast<int64_t>(tile.expert) * p.bs_expert_stride;
+    const int per_row = sp >> 4;
+    const int total = BN * per_row;
+    for (int f = tid; f < total; f += NTHREADS) {
+      const int r = f / per_row, c = f - (f / per_row) * per_row;
+      bool up;
+      const int64_t row = b_row_of(r, up);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>((up ? S2 : S) + row * sp + c * 16);
+      *reinterpret_cast<u32x4_t*>(sP + r * sp + c * 16) = v;
+    }
+  }
+
+  int64_t a_off[MA];
+  int a_chunk[MA];
+#pragma unroll
+  for (int i = 0; i < MA; ++i) {
+    int r = (wave + 4 * i) * 8 + (lane >> 3);
+    a_chunk[i] = (lane & 7) ^ (r & 7);
+    r = r < tile.rows ? r : 0;
+    const int slot = tile.row0 + r;
+    a_off[i] = p.a_rows ? p.a_rows[slot] : slot;
+  }
+  const uint8_t* pq[MQ];
+  const bf16_t* pa[MA];
+  {
+    const bf16_t* A = static_cast<const bf16_t*>(g.A);
+    const uint8_t* Q = static_cast<const uint8_t*>(g.B) + static_cast<int64_t>(tile.expert) * p.b_expert_stride;
+    const uint8_t* Q2 = static_cast<const uint8_t*>(g.B2) + static_cast<int64_t>(tile.expert) * p.b_expert_stride;
+#pragma unroll
+    for (int i = 0; i < MA; ++i) pa[i] = A + a_off[i] * g.lda + a_chunk[i] * 8;
+#pragma unroll
+    for (int i = 0; i < MQ; ++i) {
+      const int r = (wave + 4 * i) * 32 + (lane >> 1);
+      const int half = (lane & 1) ^ ((r >> 2) & 1);
+      bool up;
+      const int64_t row = b_row_of(r, up);
+      pq[i] = (up ? Q2 : Q) + row * g.ldb + half * 16;
+    }
+  }
+  const int ktot = g.K / BKP;
+
+  auto issue = [&](bf16_t* As, uint8_t* Qs) {
+#pragma unroll
+    for (int i = 0; i < MA; ++i) {
+      load_lds16_raw(pa[i], As + (wave + 4 * i) * 512);
+      pa[i] += BKP;
+    }
+#pragma unroll
+    for (int i = 0; i < MQ; ++i) {
+      load_lds16_raw(pq[i], Qs + (wave + 4 * i) * 1024);
+      pq[i] += BKP / 2;
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](int kt, const bf16_t* As, const uint8_t* Qs) {
+    const int hi = lane >> 5, sw = lane & 7;
+    u32x4_t q[FN];
+    float sc[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int rb = wn * WTN + j * 32 + (lane & 31);
+      q[j] = *reinterpret_cast<const u32x4_t*>(Qs + rb * 32 + ((hi ^ ((rb >> 2) & 1)) * 16));
+      sc[j] = e8m0_to_f32(sP[rb * sp + kt * 2 + hi]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BKP / 16; ++kk) {
+      const int ch = ((hi * 4 + kk) ^ sw) * 8;
+      bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WTM + i * 32 + (lane & 31)) * BKP + ch);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = decode8_hw(q[j][kk], sc[j]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // the panel's LDS writes complete before the first barrier of the ring
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  if (ktot > 0) issue(sA0, sQ0);
+  if (ktot > 1) issue(sA1, sQ1);
+  auto ring = [&](int kt, bf16_t* Ac, uint8_t* Qc, bf16_t* An, uint8_t* Qn) {
+    if (kt < ktot) {
+      if (kt + 1 < ktot)
+        wait_vmcnt<MA + MQ>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + 2 < ktot) issue(An, Qn);
+      compute(kt, Ac, Qc);
+    }
+  };
+  for (int kt = 0; kt < ktot; kt += STAGES) {
+    ring(kt, sA0, sQ0, sA2, sQ2);
+    ring(kt + 1, sA1, sQ1, sA0, sQ0);
+    ring(kt + 2, sA2, sQ2, sA1, sQ1);
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      if (row >= tile.rows) continue;
+      const int64_t orow = tile.row0 + row;
+      if (EPI == EPI_SITU) {
+#pragma unroll
+        for (int j = 0; j < FN; j += 2) {
+          const int grp = wn * FN + j;
+          const int col = tile.n0 + (grp >> 1) * 32 + (lane & 31);
+          if (col < p.N)
+            static_cast<bf16_t*>(p.C)[orow * p.ldc + col] =
+                f32_to_bf16(situ_glu(acc[i][j][r], acc[i][j + 1][r]));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = tile.n0 + wn * WTN + j * 32 + (lane & 31);
+          if (col >= p.N) continue;
+          if (EPI == EPI_F32)
+            static_cast<float*>(p.C)[orow * p.ldc + col] = acc[i][j][r];
+          else
+            static_cast<bf16_t*>(p.C)[orow * p.ldc + col] = f32_to_bf16(acc[i][j][r]);
         }
       }
     }
@@ -636,6 +921,98 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f32(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Split-K reduction: C = epilogue(sum over splits of the fp32 partials).  The
+// partial columns follow the B-row order of a BN-wide tile; for SiTU-GLU the
+// gate and up rows of an output column are 32 apart inside its 64-row group.
+// ---------------------------------------------------------------------------
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ part, int kn, int M,
+                                                      int N, int64_t nv, int bn, void* C,
+                                                      int64_t ldc, const float* col_add) {
+  const int64_t total = static_cast<int64_t>(M) * N;
+  const int64_t plane = static_cast<int64_t>(M) * nv;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t row = i / N;
+    const int c = static_cast<int>(i - row * N);
+    const float* pr = part + row * nv;
+    if (EPI == EPI_SITU) {
+      const int half = bn / 2;
+      const int64_t vg = static_cast<int64_t>(c / half) * bn + ((c % half) / 32) * 64 + (c % 32);
+      float g = 0.f, u = 0.f;
+      for (int q = 0; q < kn; ++q) {
+        g += pr[q * plane + vg];
+        u += pr[q * plane + vg + 32];
+      }
+      static_cast<bf16_t*>(C)[row * ldc + c] = f32_to_bf16(situ_glu(g, u));
+    } else {
+      float x = 0.f;
+      for (int q = 0; q < kn; ++q) x += pr[q * plane + c];
+      if (EPI == EPI_SIGMOID) {
+        if (col_add) x += col_add[c];
+        static_cast<float*>(C)[row * ldc + c] = 1.0f / (1.0f + expf(-x));
+      } else if (EPI == EPI_F32) {
+        static_cast<float*>(C)[row * ldc + c] = x;
+      } else {
+        static_cast<bf16_t*>(C)[row * ldc + c] = f32_to_bf16(x);
+      }
+    }
+  }
+}
+
+// Tile shape and K split of a bf16 dense problem.  Row tiles follow M (32,
+// 64, else 128 x 128); when the output tiles cannot fill the chip the K
+// range is split so that about one wave of blocks runs, each split keeping
+// at least 4 stages.
+struct DensePlan {
+  int cfg;  // 0: 32x256 BKP 64, 1: 64x256 BKP 64, 2: 128x128 BKP 32
+  int bm, bn, bkp;
+  int ntn, mt;
+  int ks;
+  size_t bytes;
+};
+
+static DensePlan plan_dense(int M, int N, int K, int epi) {
+  DensePlan d{};
+  int target;
+  if (M <= 32) {
+    d.cfg = 0; d.bm = 32; d.bn = 256; d.bkp = 64; target = 256;
+  } else if (M <= 64) {
+    d.cfg = 1; d.bm = 64; d.bn = 256; d.bkp = 64; target = 256;
+  } else {
+    d.cfg = 2; d.bm = 128; d.bn = 128; d.bkp = 32; target = 512;
+  }
+  const int bn_out = epi == EPI_SITU ? d.bn / 2 : d.bn;
+  d.ntn = (N + bn_out - 1) / bn_out;
+  d.mt = (M + d.bm - 1) / d.bm;
+  const int64_t tiles = static_cast<int64_t>(d.mt) * d.ntn;
+  const int kall = K / d.bkp;
+  d.ks = 1;
+  if (tiles > 0 && tiles < target / 2 && kall >= 8) {
+    int ks = static_cast<int>((target + tiles - 1) / tiles);
+    ks = ks < kall / 4 ? ks : kall / 4;
+    d.ks = ks > 1 ? ks : 1;
+  }
+  d.bytes = d.ks > 1 ? static_cast<size_t>(d.ks) * M * d.ntn * d.bn * sizeof(float) : 0;
+  return d;
+}
+
+size_t splitk_bytes(int M, int N, int K, int epi) {
+  if (M <= 0 || N <= 0) return 0;
+  return plan_dense(M, N, K, epi).bytes;
+}
+
+template <int EPI>
+static int run_reduce(const Params& p, const DensePlan& d, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(p.M) * p.N;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)),
+                     dim3(256), 0, stream, p.partial, d.ks, p.M, p.N,
+                     static_cast<int64_t>(d.ntn) * d.bn, d.bn, p.C, p.ldc, p.col_add);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int EPI, int BFMT>
 static int run_bf16(const Params& p, hipStream_t stream) {
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
@@ -667,7 +1044,7 @@ static int run_pipe(const Params& p, hipStream_t stream) {
     if (p.seg[s].K % BKP != 0) return MOE_EUNSUPPORTED;
   const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
   const int mt = p.tiles ? p.max_mtiles : (p.M + BM - 1) / BM;
-  const int64_t G = static_cast<int64_t>(mt) * ntn;
+  const int64_t G = static_cast<int64_t>(mt) * ntn * (p.ksplit > 1 ? p.ksplit : 1);
   if (G <= 0) return MOE_OK;
   const int64_t G8 = (G + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP>), dim3(static_cast<unsigned>(G8)),
@@ -679,10 +1056,51 @@ template <int BM, int BN, int WM, int BKP>
 static int dispatch_pipe(const Params& p, int epi, hipStream_t s) {
   switch (epi) {
     case EPI_BF16: return run_pipe<BM, BN, WM, EPI_BF16, BKP>(p, s);
+    case EPI_F32: return run_pipe<BM, BN, WM, EPI_F32, BKP>(p, s);
     case EPI_SIGMOID: return run_pipe<BM, BN, WM, EPI_SIGMOID, BKP>(p, s);
     case EPI_SITU: return run_pipe<BM, BN, WM, EPI_SITU, BKP>(p, s);
     default: return MOE_EUNSUPPORTED;
   }
+}
+
+// Panel bytes of the MXFP4 kernel and the largest panel it takes (two blocks
+// per CU within 160 KB of LDS).
+template <int BM, int BN>
+constexpr size_t fp4_static_lds() {
+  return static_cast<size_t>(3) * (BM * 64 * 2 + BN * 32);
+}
+
+// Returns 1 when the shape does not fit the pipelined MXFP4 kernel (the caller
+// then uses the register-staged kernel).
+template <int BM, int BN, int WM, int EPI>
+static int run_pipe_fp4(const Params& p, hipStream_t stream) {
+  constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
+  if (p.nseg != 1 || p.seg[0].K % 512 != 0) return 1;
+  const Seg& g = p.seg[0];
+  const uintptr_t align = reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B) |
+                          reinterpret_cast<uintptr_t>(g.B2) | reinterpret_cast<uintptr_t>(g.Bs) |
+                          reinterpret_cast<uintptr_t>(g.Bs2) |
+                          static_cast<uintptr_t>(g.lda * 2) | static_cast<uintptr_t>(p.b_expert_stride) |
+                          static_cast<uintptr_t>(p.bs_expert_stride);
+  if (align % 16 != 0) return 1;
+  const size_t panel = static_cast<size_t>(BN) * (p.seg[0].K / 32);
+  if (fp4_static_lds<BM, BN>() + panel > 80 * 1024) return 1;
+  const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
+  const int mt = p.tiles ? p.max_mtiles : (p.M + BM - 1) / BM;
+  const int64_t G = static_cast<int64_t>(mt) * ntn;
+  if (G <= 0) return MOE_OK;
+  const int64_t G8 = (G + 7) / 8 * 8;
+  static bool configured = false;
+  if (!configured) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(80 * 1024 - fp4_static_lds<BM, BN>())) != hipSuccess)
+      return MOE_EHIP;
+    configured = true;
+  }
+  hipLaunchKernelGGL((gemm_pipe_fp4<BM, BN, WM, EPI>), dim3(static_cast<unsigned>(G8)),
+                     dim3(NTHREADS), panel, stream, p);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 template <int EPI>
@@ -701,6 +1119,7 @@ template <int BM, int BN, int WM, int BFMT>
 static int dispatch_epi(const Params& p, int epi, hipStream_t s) {
   switch (epi) {
     case EPI_BF16: return run_bf16<BM, BN, WM, EPI_BF16, BFMT>(p, s);
+    case EPI_F32: return run_bf16<BM, BN, WM, EPI_F32, BFMT>(p, s);
     case EPI_SIGMOID: return run_bf16<BM, BN, WM, EPI_SIGMOID, BFMT>(p, s);
     case EPI_SITU: return run_bf16<BM, BN, WM, EPI_SITU, BFMT>(p, s);
     default: return MOE_EUNSUPPORTED;
@@ -719,14 +1138,55 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
   }
   for (int s = 0; s < p.nseg; ++s)
     if (p.seg[s].K % BK != 0) return MOE_EUNSUPPORTED;
-  if (bfmt == B_DENSE) {
+  if (bfmt == B_DENSE && p.tiles) {
     // grouped problems stream expert weights: tiles as tall as the expected
     // rows per expert and 256 columns wide (fewer re-reads of the gathered
-    // rows per weight byte); dense problems use square tiles
-    if (bm_hint <= 32) return dispatch_pipe<32, 256, 1, 64>(p, epi, stream);
-    if (p.tiles && bm_hint <= 96) return dispatch_pipe<96, 256, 1, 32>(p, epi, stream);
-    return dispatch_pipe<128, 128, 2, 32>(p, epi, stream);
+    // rows per weight byte)
+    Params q = p;
+    q.ksplit = 1;
+    if (bm_hint <= 32) return dispatch_pipe<32, 256, 1, 64>(q, epi, stream);
+    if (bm_hint <= 96)  // gate/up: 128-byte row pieces per stage measure faster
+      return epi == EPI_SITU ? dispatch_pipe<96, 256, 1, 64>(q, epi, stream)
+                             : dispatch_pipe<96, 256, 1, 32>(q, epi, stream);
+    return dispatch_pipe<128, 128, 2, 32>(q, epi, stream);
   }
+  if (bfmt == B_DENSE) {
+    int K = 0;
+    for (int s = 0; s < p.nseg; ++s) K += p.seg[s].K;
+    const DensePlan d = plan_dense(p.M, p.N, K, epi);
+    Params q = p;
+    q.ksplit = 1;
+    if (d.ks > 1 && p.partial && p.partial_bytes >= d.bytes) q.ksplit = d.ks;
+    int rc;
+    if (d.cfg == 0)
+      rc = dispatch_pipe<32, 256, 1, 64>(q, epi, stream);
+    else if (d.cfg == 1)
+      rc = dispatch_pipe<64, 256, 1, 64>(q, epi, stream);
+    else
+      rc = dispatch_pipe<128, 128, 2, 32>(q, epi, stream);
+    if (rc != MOE_OK || q.ksplit == 1) return rc;
+    switch (epi) {
+      case EPI_BF16: return run_reduce<EPI_BF16>(q, d, stream);
+      case EPI_F32: return run_reduce<EPI_F32>(q, d, stream);
+      case EPI_SIGMOID: return run_reduce<EPI_SIGMOID>(q, d, stream);
+      case EPI_SITU: return run_reduce<EPI_SITU>(q, d, stream);
+      default: return MOE_EUNSUPPORTED;
+    }
+  }
+  // MXFP4 routed experts: codes straight to LDS, scales in a per-block panel,
+  // decoded per fragment; shapes outside that kernel's limits use the
+  // register-staged kernel that decodes while writing LDS
+  int rc = 1;
+  if (epi == EPI_SITU)
+    rc = bm_hint <= 32 ? run_pipe_fp4<32, 256, 1, EPI_SITU>(p, stream)
+                       : run_pipe_fp4<128, 128, 2, EPI_SITU>(p, stream);
+  else if (epi == EPI_BF16)
+    rc = bm_hint <= 32 ? run_pipe_fp4<32, 256, 1, EPI_BF16>(p, stream)
+                       : run_pipe_fp4<128, 128, 2, EPI_BF16>(p, stream);
+  else if (epi == EPI_F32)
+    rc = bm_hint <= 32 ? run_pipe_fp4<32, 256, 1, EPI_F32>(p, stream)
+                       : run_pipe_fp4<128, 128, 2, EPI_F32>(p, stream);
+  if (rc != 1) return rc;
   if (bm_hint <= 32) return dispatch_epi<32, 256, 1, B_MXFP4>(p, epi, stream);
   return dispatch_epi<128, 128, 2, B_MXFP4>(p, epi, stream);
 }

@@ -43,7 +43,16 @@ struct Params {
   void* C;
   int64_t ldc;
   const float* col_add;      // EPI_SIGMOID: per-column logit offset or null
+  // Split-K for dense problems with few output tiles: fp32 partial sums
+  // [ksplit][M][tiles_n * BN] (set by launch(), room given by partial_bytes),
+  // reduced with the epilogue by a second kernel.  Null: no split.
+  float* partial;
+  size_t partial_bytes;
+  int ksplit;
 };
+
+// Bytes of fp32 partials launch() uses for a bf16 dense problem (0: no split).
+size_t splitk_bytes(int M, int N, int K, int epi);
 
 // Launch helpers (defined in gemm.hip).  `act_bf16` selects the bf16 MFMA
 // kernels, otherwise the fp32 kernels run.

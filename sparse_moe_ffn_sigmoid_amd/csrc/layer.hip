@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void expert_slots(const uint8_t* sel, int T, i
 // y_t = sum_j w[t][j] * yp[inv[t][j]] in fp32 (j ascending), then
 // RMSNorm: y * rsqrt(mean(y^2) + eps) * gamma.  One block per token.
 template <typename ACT>
-__global__ __launch_bounds__(256) void combine_rmsnorm(const ACT* __restrict__ yp,
+__global__ __launch_bounds__(256) void combine_rmsnorm(const float* __restrict__ yp,
                                                        const int32_t* __restrict__ inv,
                                                        const float* __restrict__ w,
                                                        const float* __restrict__ gamma, int k,
@@ -146,11 +146,11 @@ __global__ __launch_bounds__(256) void combine_rmsnorm(const ACT* __restrict__ y
   for (int i = 0; i < MAXV; ++i) acc[i] = 0.f;
   for (int j = 0; j < k; ++j) {
     const float wj = w[static_cast<int64_t>(t) * k + j];
-    const ACT* src = yp + static_cast<int64_t>(inv[static_cast<int64_t>(t) * k + j]) * L;
+    const float* src = yp + static_cast<int64_t>(inv[static_cast<int64_t>(t) * k + j]) * L;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       const int c = threadIdx.x + 256 * i;
-      if (c < L) acc[i] = fmaf(wj, to_f32<ACT>(src[c]), acc[i]);
+      if (c < L) acc[i] = fmaf(wj, src[c], acc[i]);
     }
   }
   float ss = 0.f;
@@ -191,6 +191,8 @@ struct ForwardWorkspace {
   void* yhat;         // [T][latent]
   int bm;
   int max_mtiles;
+  float* partial;     // split-K partial sums of the dense GEMMs (used one at a time)
+  size_t partial_bytes;
 };
 
 // Tile height of the grouped expert GEMMs, from the mean rows per expert
@@ -228,8 +230,22 @@ static size_t forward_layout(const moe_shape_t& s, ForwardWorkspace* fw, void* b
   f.perm = cv.take<int32_t>(T * k);
   f.inv = cv.take<int32_t>(T * k);
   f.h = cv.take<char>(T * k * s.inter * es);
-  f.yp = cv.take<char>(T * k * s.latent * es);
+  f.yp = cv.take<float>(T * k * s.latent);  // fp32: the combine sums unrounded products
   f.yhat = cv.take<char>(T * s.latent * es);
+  // The dense GEMMs that may split K never overlap in time: the router runs
+  // before the shared branch forks, the two shared-branch products run in
+  // order on one stream, and the up-projection runs after the join.
+  size_t pb = 0;
+  if (s.act_dtype == MOE_BF16) {
+    const int epi_store = gemm::EPI_BF16;
+    const size_t c[4] = {gemm::splitk_bytes(s.T, s.n_experts, 3 * s.d, gemm::EPI_SIGMOID),
+                         gemm::splitk_bytes(s.T, s.latent, s.d, epi_store),
+                         gemm::splitk_bytes(s.T, s.shared_inter, s.d, gemm::EPI_SITU),
+                         gemm::splitk_bytes(s.T, s.d, s.latent + s.shared_inter, epi_store)};
+    for (size_t v : c) pb = v > pb ? v : pb;
+  }
+  f.partial = cv.take<float>(pb / sizeof(float));
+  f.partial_bytes = pb;
   if (fw) *fw = f;
   return cv.bytes();
 }
@@ -323,6 +339,8 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     p.C = scores;
     p.ldc = n;
     p.col_add = wt.router_logit_offset;
+    p.partial = f.partial;
+    p.partial_bytes = f.partial_bytes;
     if (bf) {
       const int64_t cnt = static_cast<int64_t>(n) * d;
       bf16_t* hi = f.wsplit;
@@ -358,6 +376,8 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     p.seg[0] = seg(x, d, wt.w_down, d, d);
     p.C = f.z;
     p.ldc = L;
+    p.partial = f.partial;
+    p.partial_bytes = f.partial_bytes;
     {
       prof::Scope sc(prof::ST_LATENT_DOWN, sst);
       if ((rc = gemm::launch(p, store_epi, gemm::B_DENSE, bf, 128, sst)) != MOE_OK) return rc;
@@ -370,6 +390,8 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     q.seg[0].B2 = wt.ws_up;
     q.C = f.hs;
     q.ldc = ms;
+    q.partial = f.partial;
+    q.partial_bytes = f.partial_bytes;
     {
       prof::Scope sc(prof::ST_SHARED_GATE_UP, sst);
       if ((rc = gemm::launch(q, gemm::EPI_SITU, gemm::B_DENSE, bf, 128, sst)) != MOE_OK) return rc;
@@ -439,14 +461,14 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     p.C = f.yp;
     p.ldc = L;
     prof::Scope sc(prof::ST_ROUTED_DOWN, st);
-    if ((rc = gemm::launch(p, store_epi, bfmt, bf, f.bm, st)) != MOE_OK) return rc;
+    if ((rc = gemm::launch(p, gemm::EPI_F32, bfmt, bf, f.bm, st)) != MOE_OK) return rc;
   }
   // 7. weighted combine in the latent space + RMSNorm
   {
   prof::Scope sc(prof::ST_COMBINE_RMSNORM, st);
   if (bf)
     hipLaunchKernelGGL(combine_rmsnorm<bf16_t>, dim3(T), dim3(256), 0, st,
-                       static_cast<const bf16_t*>(f.yp), f.inv, w, wt.rms_gamma, k, L, s.rms_eps,
+                       static_cast<const float*>(f.yp), f.inv, w, wt.rms_gamma, k, L, s.rms_eps,
                        static_cast<bf16_t*>(f.yhat));
   else
     hipLaunchKernelGGL(combine_rmsnorm<float>, dim3(T), dim3(256), 0, st,
@@ -464,6 +486,8 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     p.seg[1] = seg(f.hs, ms, wt.ws_down, ms, ms);
     p.C = out;
     p.ldc = d;
+    p.partial = f.partial;
+    p.partial_bytes = f.partial_bytes;
     prof::Scope sc(prof::ST_UP_SHARED_DOWN, st);
     if ((rc = gemm::launch(p, store_epi, gemm::B_DENSE, bf, 128, st)) != MOE_OK) return rc;
   }

@@ -596,12 +596,11 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
   const int n = a.n;
   const int tid = threadIdx.x;
   __shared__ uint64_t d[1024];
-  __shared__ uint64_t dprev[1024];
   __shared__ int64_t s_red[1024];
   __shared__ int s_flag;
   __shared__ int s_path[1025];
   __shared__ int s_len;
-  constexpr int EDGE_CACHE = 8192;
+  constexpr int EDGE_CACHE = 12288;
   __shared__ uint64_t s_edges[EDGE_CACHE];
 
   const int64_t ph = c[C_PHASE];
@@ -640,26 +639,31 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
     return;
   }
   // sources: overloaded experts at distance 0
-  bool over_e = false, under_e = false;
+  __shared__ int s_over[1024], s_under[1024], s_pos[1024];
+  __shared__ int s_bad;
+  bool under_e = false;
   if (tid < n) {
     const int64_t C = target(a.T, n, a.k, tid);
-    over_e = a.loads[tid] > C;
-    under_e = a.loads[tid] < C;
-    d[tid] = over_e ? static_cast<uint64_t>(tid) : PACKED_INF;
+    const int32_t L = a.loads[tid];
+    s_over[tid] = L > C;
+    under_e = L < C;
+    s_under[tid] = under_e;
+    s_pos[tid] = 0;
+    d[tid] = L > C ? static_cast<uint64_t>(tid) : PACKED_INF;
   }
   const bool cached = nedges <= EDGE_CACHE;
   if (cached)
     for (int i = tid; i < nedges; i += blockDim.x) s_edges[i] = a.edges[i];
-  __syncthreads();
   // Relaxation passes.  s_D is the running minimum distance of an
   // underloaded expert (it only decreases); a pass that lowers some distance
   // to at most s_D asks for another pass.  Flagging against the running value
   // flags a superset of "changed at or below the final D*", so the passes
   // stop only when every distance <= D* and its predecessor is final.
   __shared__ unsigned long long s_D;
-  __shared__ int s_under[1024];
-  if (tid < n) s_under[tid] = under_e;
-  if (tid == 0) s_D = static_cast<unsigned long long>(DIST_INF);
+  if (tid == 0) {
+    s_D = static_cast<unsigned long long>(DIST_INF);
+    s_bad = 0;
+  }
   __syncthreads();
   if (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) < DIST_INF)
     atomicMin(&s_D, static_cast<unsigned long long>(d[tid] >> IDX_BITS));
@@ -708,18 +712,18 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
   // u* = lowest underloaded expert at distance D
   s_red[tid] = (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) == D) ? tid : 1 << 30;
   __syncthreads();
-  for (int s = 512; s > 0; s >>= 1) {
-    if (tid < s) s_red[tid] = min(s_red[tid], s_red[tid + s]);
+  for (int st = 512; st > 0; st >>= 1) {
+    if (tid < st) s_red[tid] = min(s_red[tid], s_red[tid + st]);
     __syncthreads();
   }
+  // the path from u* back to its source (an overloaded expert), in LDS
   if (tid == 0) {
     int v = static_cast<int>(s_red[0]);
     int len = 0;
     bool ok = true;
     while (true) {
       s_path[len++] = v;
-      const int64_t Cv = target(a.T, n, a.k, v);
-      if (a.loads[v] > Cv) break;
+      if (s_over[v]) break;
       v = static_cast<int>(d[v] & 1023);
       if (len > n) {
         ok = false;
@@ -729,28 +733,32 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
     s_len = ok ? len : -1;
   }
   __syncthreads();
-  if (s_len < 0) {
+  const int len = s_len;
+  if (len < 0) {
     if (tid == 0) {
       c[C_PHASE] = PH_FAILED;
       c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
     }
     return;
   }
+  // the i-th expert from the source gains i grid units (s_path[len-1] is the
+  // source, s_path[0] = u*); a vertex appears once on a predecessor path
+  if (tid < len) s_pos[s_path[len - 1 - tid]] = tid;
+  __syncthreads();
+  // every expert drops by D - min(d, D), then the path shift is added
   if (tid < n) {
     const int64_t dv = static_cast<int64_t>(d[tid] >> IDX_BITS);
-    bias[tid] += (dv < D ? dv : D) - D;
+    const int64_t nbv = bias[tid] + ((dv < D ? dv : D) - D) + s_pos[tid];
+    bias[tid] = nbv;
+    if (nbv >= BIAS_LIMIT || nbv <= -BIAS_LIMIT) s_bad = 1;
   }
   __syncthreads();
   if (tid == 0) {
-    const int len = s_len;  // s_path[len-1] is the source, s_path[0] = u*
-    for (int i = 0; i < len; ++i) bias[s_path[len - 1 - i]] += i;
-    bool bad = false;
-    for (int e = 0; e < n; ++e) bad |= (bias[e] >= BIAS_LIMIT || bias[e] <= -BIAS_LIMIT);
     c[C_MOVES] += 1;
     c[C_LAST_D] = D;
     c[C_LAST_HOPS] = len - 1;
     c[C_BF_PASSES] += passes;
-    if (bad) {
+    if (s_bad) {
       c[C_PHASE] = PH_FAILED;
       c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
     }

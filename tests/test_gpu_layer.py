@@ -60,6 +60,19 @@ def test_mxfp4_layer():
     check_layer(workloads.small_shape(routed="mxfp4", T=300, k=4), seed=2, name="mxfp4 qb")
 
 
+# Widths that are multiples of 512 take the pipelined MXFP4 kernel (scale
+# panel in LDS); the others take the register-staged one.  Cases cover both
+# tile shapes (few / many rows per expert) and column tails.
+@pytest.mark.parametrize("kw", [
+    dict(T=300, k=4, d=1024, latent=512, m=512),              # 32x256 tiles, both GEMMs
+    dict(T=300, k=4, d=1024, latent=512, m=576),              # gate/up column tail
+    dict(T=300, k=4, d=1024, latent=640, m=512),              # down column tail
+    dict(T=640, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 128x128 tiles
+])
+def test_mxfp4_layer_pipelined(kw):
+    check_layer(workloads.small_shape(routed="mxfp4", **kw), seed=5, name=f"mxfp4 {kw}")
+
+
 def test_mxfp4_layer_frozen_zero_bias():
     shape = workloads.small_shape(routed="mxfp4", T=300, k=4, offset_std=1.0)
     check_layer(shape, seed=3, qb_mode=qb.MODE_FROZEN, bias=np.zeros(shape.n),

@@ -1,0 +1,109 @@
+"""Full-size K3 layers, run exactly as the benchmark times them (seeded inputs
+generated on the device, QB on the batch from a zero bias, one workspace),
+checked against the float64 oracle:
+
+* router: the fp32 scores of sampled tokens against the oracle's router;
+* routing: exact target loads, the top-k certificate (the selection is the
+  top-k of the fixed-point biased scores under the returned bias) and the
+  renormalised weights for every token; bit-exact indices, bias and QB
+  counters against the oracle's QB on the same scores where the oracle
+  finishes in seconds (T <= 4096);
+* outputs: sampled tokens against the oracle layer on those tokens, with the
+  oracle's weights computed from the same scores (experts decoded one at a
+  time), max|diff| / rms(ref) within the bf16 / MXFP4 bounds.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from layer_cases import announce, rel_err
+from oracle import layer as olayer
+from oracle import qb
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "mxfp4": 1e-1}
+SCALES = {"w_gate": "s_gate", "w_uproj": "s_uproj", "w_dn": "s_dn"}
+
+
+def forward_as_benchmarked(shape, qb_mode):
+    import sparse_moe_ffn_sigmoid_amd as moe
+    dev = torch.device("cuda:0")
+    inp = workloads.layer_inputs(shape, dev, seed=0)
+    w = {}
+    for key, v in inp.items():
+        if key == "x" or v is None:
+            continue
+        if isinstance(v, tuple):
+            w[key], w[SCALES[key]] = v
+        else:
+            w[key] = v
+    w["router_logit_offset"] = w.pop("logit_offset")
+    routed = moe.MOE_MXFP4 if shape.routed == "mxfp4" else moe.MOE_BF16
+    sh = moe.make_shape(shape.T, shape.d, shape.latent, shape.n, shape.k, shape.m, shape.shared,
+                        moe.MOE_BF16, routed, shape.eps, qb_mode, 64)
+    ws = torch.empty(moe.forward_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+    bias0 = torch.zeros(shape.n, dtype=torch.float64, device=dev)
+    r = moe.latent_forward(sh, w, inp["x"], bias=bias0, workspace=ws, want_scores=True)
+    torch.cuda.synchronize()
+    return inp, {k: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy()
+                 for k, v in r.items()}
+
+
+def check_routing(shape, got, qb_mode):
+    s = got["scores"]
+    T, n, k = s.shape[0], shape.n, shape.k
+    # the selection is the top-k of the fixed-point biased keys (ties to the lower index)
+    sfx = qb.to_fixed(s)
+    bfx = np.rint(got["bias"] * 2.0 ** 40).astype(np.int64)
+    assert (bfx.astype(np.float64) * 2.0 ** -40 == got["bias"]).all()
+    key = qb.packed_keys(sfx, bfx)
+    top = np.argpartition(-key, k - 1, axis=1)[:, :k]
+    assert (np.sort(top, 1) == np.sort(got["idx"], 1)).all()
+    # ordered by raw score, weights = chosen raw scores renormalised
+    chosen = np.take_along_axis(s.astype(np.float64), got["idx"].astype(np.int64), 1)
+    assert (np.diff(chosen, axis=1) <= 0).all()
+    w_ref = chosen / chosen.sum(1, keepdims=True)
+    assert np.abs(got["w"] - w_ref).max() <= (k + 1) * 2.0 ** -24
+    if qb_mode == qb.MODE_BATCH:
+        assert (got["loads"] == qb.targets(T, n, k)).all()
+        assert got["info"][1] == qb.STATUS_OK
+        if T <= 4096:
+            ref = qb.route_qb(s, k)
+            assert (got["idx"] == ref["idx"]).all()
+            assert (got["bias"] == ref["bias"]).all()
+            assert tuple(int(v) for v in got["info"]) == tuple(ref["info"])
+    else:
+        assert (bfx == 0).all()
+        assert (got["loads"] == np.bincount(got["idx"].ravel(), minlength=n)).all()
+    return w_ref
+
+
+@pytest.mark.parametrize("wl,qb_mode", [
+    ("k3_decode", qb.MODE_BATCH),
+    ("k3_prefill", qb.MODE_BATCH),
+    ("k3_mxfp4", qb.MODE_BATCH),
+    ("k3_mxfp4", qb.MODE_FROZEN),
+])
+def test_full_size_layer_sampled(wl, qb_mode):
+    shape = workloads.SHAPES[wl]
+    announce(f"full-size layer {wl} qb_mode={qb_mode}")
+    inp, got = forward_as_benchmarked(shape, qb_mode)
+    T = shape.T
+    tokens = np.unique(np.array([0, T // 3, (2 * T) // 3, T - 1]))
+    # router on the sampled tokens
+    x_s = olayer.as_f64(inp["x"][torch.from_numpy(tokens).cuda()])
+    s_ref = olayer.router_scores(x_s, olayer.as_f64(inp["w_router"]),
+                                 olayer.as_f64(inp["logit_offset"]))
+    assert np.abs(got["scores"][tokens] - s_ref).max() <= 1e-5
+    w_ref = check_routing(shape, got, qb_mode)
+    # layer outputs of the sampled tokens, oracle weights from the same scores
+    sub = dict(inp)
+    sub["x"] = inp["x"][torch.from_numpy(tokens).cuda()]
+    out_ref = olayer.layer_forward(sub, got["idx"][tokens], w_ref[tokens], shape.eps)
+    err = rel_err(got["out"][tokens], out_ref)
+    print(f"  info={got['info'].tolist()} sampled max|diff|/rms = {err:.3e}", flush=True)
+    assert err <= TOL[shape.routed]
+    del inp, sub
+    torch.cuda.empty_cache()
