@@ -27,9 +27,10 @@
  *     auxiliary non-blocking stream (default priority) with two events,
  *     created on first use, on which moe_latent_forward runs the
  *     routing-independent shared branch (forked from and joined back into
- *     `stream`, under a per-device mutex held for the call); per host thread,
- *     one pinned 64-byte word the balancing loop polls; the opt-in
- *     stage-timing records.
+ *     `stream`, under a per-device mutex held for the call); per host thread
+ *     and device, two pinned 64-byte words and two events through which the
+ *     balancing loop reads the phase of the previous batch of steps while
+ *     the next batch runs; the opt-in stage-timing records.
  *   - Matrices are row-major [out_features][in_features] (K contiguous);
  *     activations are [T][features].  bf16 values are passed as raw 16-bit
  *     patterns.  MXFP4 weights: codes uint8 [rows][K/2] (element 2i in the

@@ -49,6 +49,8 @@ enum Phase : int64_t { PH_ROUNDS = 0, PH_SAP = 1, PH_DONE = 2, PH_FAILED = 3, PH
 enum Ctrl {
   C_PHASE = 0, C_ROUNDS, C_BEST, C_SINCE, C_MOVES, C_IMB, C_RESID, C_STATUS, C_DELTA,
   C_EDGES_VALID, C_CUR, C_ROUND, C_MAX_ROUNDS, C_LAST_D, C_LAST_HOPS, C_BF_PASSES,
+  C_PIVOT,  // th_k1 holds every token's (k+1)-th key of the last top-k pass
+  C_DROP,   // largest bias decrease (grid units) since that pass
   C_COUNT = 32
 };
 enum Cnt { N_EDGES = 0, N_OVERFLOW, N_BIASRANGE, N_COUNT = 8 };
@@ -155,14 +157,27 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
   int32_t* oE = reinterpret_cast<int32_t*>(oS + 4 * MAX_K);              // [4][64]
   float* oSorted = reinterpret_cast<float*>(oE + 4 * MAX_K);             // [4][64]
 
+  uint64_t* cand = reinterpret_cast<uint64_t*>(oSorted + 4 * MAX_K);      // [4][64]
+  uint64_t* thv = cand + 4 * 64;                                         // [4][2]
+  int64_t* sbias = reinterpret_cast<int64_t*>(thv + 4 * 2);              // [1024]
+
   const int n = a.n, k = a.k, T = a.T;
-  for (int e = threadIdx.x; e < n; e += blockDim.x) sload[e] = 0;
+  const int64_t* gbias = a.bfx + (a.ctrl[C_CUR] & 1) * n;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    sload[e] = 0;
+    sbias[e] = gbias[e];
+  }
   __syncthreads();
+  // Pivot: every key of the last pass's top k+1 has dropped by at most
+  // `drop`, so at least k+1 keys are >= th_k1 - drop; when at most 64 are,
+  // the k-th and (k+1)-th keys are found by ranking those candidates.
+  const bool use_pivot = a.ctrl[C_PIVOT] != 0 && k < n;
+  const uint64_t drop_key = static_cast<uint64_t>(a.ctrl[C_DROP]) << IDX_BITS;
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int nj = (n + 63) >> 6;
-  const int64_t* bias = a.bfx + (a.ctrl[C_CUR] & 1) * n;
+  const int64_t* bias = sbias;
   const int64_t delta = a.ctrl[C_DELTA];
   const int rounds = (k < n) ? k + 1 : k;
 
@@ -175,35 +190,67 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
       key[j] = 0;
       if (j < nj && e < n) key[j] = pack_key(score_fixed(row[e]), bias[e], e);
     }
-    // Each lane sorts its keys (descending bitonic network); then every
-    // round takes the wave maximum of the lane heads and the winning lane
-    // (keys are distinct, so exactly one) pops its head.
-    uint64_t q[MAX_NJ];
-#pragma unroll
-    for (int j = 0; j < MAX_NJ; ++j) q[j] = key[j];
-#pragma unroll
-    for (int kk = 2; kk <= MAX_NJ; kk <<= 1)
-#pragma unroll
-      for (int jj = kk >> 1; jj > 0; jj >>= 1)
-#pragma unroll
-        for (int i = 0; i < MAX_NJ; ++i) {
-          const int l = i ^ jj;
-          if (l > i) {
-            const uint64_t x = q[i], y = q[l];
-            const bool sw = ((i & kk) == 0) ? (x < y) : (x > y);
-            q[i] = sw ? y : x;
-            q[l] = sw ? x : y;
-          }
-        }
     uint64_t thk = 0, thk1 = 0;
-    for (int r = 0; r < rounds; ++r) {
-      const uint64_t wm = wave_max_u64(q[0]);
-      const bool win = q[0] == wm;
+    bool found = false;
+    if (use_pivot) {
+      const uint64_t prev = static_cast<uint64_t>(a.th_k1[t]);
+      const uint64_t P = prev > drop_key ? prev - drop_key : 1;
+      int c = 0;
 #pragma unroll
-      for (int j = 0; j < MAX_NJ - 1; ++j) q[j] = win ? q[j + 1] : q[j];
-      q[MAX_NJ - 1] = win ? 0 : q[MAX_NJ - 1];
-      if (r == k - 1) thk = wm;
-      if (r == k) thk1 = wm;
+      for (int j = 0; j < MAX_NJ; ++j) c += __popcll(__ballot(key[j] >= P));
+      if (c >= k + 1 && c <= 64) {
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < MAX_NJ; ++j) {
+          const bool in = key[j] >= P;
+          const uint64_t bal = __ballot(in);
+          if (in) cand[wv * 64 + base + __popcll(bal & ((uint64_t(1) << lane) - 1))] = key[j];
+          base += __popcll(bal);
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        if (lane < c) {
+          const uint64_t v = cand[wv * 64 + lane];
+          int rank = 0;
+          for (int i = 0; i < c; ++i) rank += cand[wv * 64 + i] > v;
+          if (rank == k - 1) thv[wv * 2] = v;
+          if (rank == k) thv[wv * 2 + 1] = v;
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        thk = thv[wv * 2];
+        thk1 = thv[wv * 2 + 1];
+        __builtin_amdgcn_wave_barrier();
+        found = true;
+      }
+    }
+    if (!found) {
+      // k+1 rounds of wave-wide maximum: each lane offers its largest
+      // remaining key, the winner (keys are distinct) removes it; removed
+      // keys are rebuilt afterwards.
+      uint32_t removed = 0;
+      for (int r = 0; r < rounds; ++r) {
+        uint64_t lm = key[0];
+#pragma unroll
+        for (int j = 1; j < MAX_NJ; ++j) lm = key[j] > lm ? key[j] : lm;
+        const uint64_t wm = wave_max_u64(lm);
+        if (lm == wm) {
+#pragma unroll
+          for (int j = 0; j < MAX_NJ; ++j)
+            if (key[j] == wm) {
+              key[j] = 0;
+              removed |= 1u << j;
+            }
+        }
+        if (r == k - 1) thk = wm;
+        if (r == k) thk1 = wm;
+      }
+#pragma unroll
+      for (int j = 0; j < MAX_NJ; ++j)
+        if ((removed >> j) & 1u) {
+          const int e = lane + 64 * j;
+          key[j] = pack_key(score_fixed(row[e]), bias[e], e);
+        }
     }
     if (lane == 0) {
       a.th_k[t] = static_cast<int64_t>(thk);
@@ -361,6 +408,8 @@ __global__ __launch_bounds__(1024) void status_pass(Args a) {
   imb = s_imb[0];
   c[C_IMB] = imb;
   c[C_RESID] = s_res[0];
+  c[C_PIVOT] = 1;  // th_k1 now holds this pass's keys; biases unchanged so far
+  c[C_DROP] = 0;
   const int64_t ph = c[C_PHASE];
   if (ph == PH_ROUNDS) {
     bool round = false;
@@ -403,6 +452,7 @@ __global__ __launch_bounds__(1024) void status_pass(Args a) {
 // too large for LDS falls back to an MSB-first radix select.
 // ---------------------------------------------------------------------------
 constexpr int SEL_BLOCK = 256;
+constexpr int QREG = 16;  // margins kept in registers per thread (T <= 4096)
 constexpr int NBUCKET = 2048;
 constexpr int GATHER_CAP = 4096;
 constexpr int DIG = 10;
@@ -505,7 +555,15 @@ __global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
   for (int i = tid; i < NBUCKET; i += SEL_BLOCK) hist[i] = 0;
   if (tid == 0) s_cnt = 0;
   __syncthreads();
-  for (int t = tid; t < T; t += SEL_BLOCK)
+  // the first QREG margins of each thread stay in registers for the gather
+  int64_t mreg[QREG];
+#pragma unroll
+  for (int i = 0; i < QREG; ++i) {
+    const int t = tid + i * SEL_BLOCK;
+    mreg[i] = t < T ? margin_of(a, bias, e, t) : 0;
+    if (t < T) atomicAdd(&hist[bucket_of(mreg[i] - cut)], 1);
+  }
+  for (int t = tid + QREG * SEL_BLOCK; t < T; t += SEL_BLOCK)
     atomicAdd(&hist[bucket_of(margin_of(a, bias, e, t) - cut)], 1);
   __syncthreads();
 
@@ -545,14 +603,17 @@ __global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
   }
   __syncthreads();
   const int b1 = s_bucket[0], b2 = s_bucket[1];  // b2 <= b1
-  for (int t = tid; t < T; t += SEL_BLOCK) {
-    const int64_t M = margin_of(a, bias, e, t);
+  auto gather = [&](int64_t M) {
     const int b = bucket_of(M - cut);
     if (b <= b1 && b >= b2) {
       const int pos = atomicAdd(&s_cnt, 1);
       if (pos < GATHER_CAP) gat[pos] = M;
     }
-  }
+  };
+#pragma unroll
+  for (int i = 0; i < QREG; ++i)
+    if (tid + i * SEL_BLOCK < T) gather(mreg[i]);
+  for (int t = tid + QREG * SEL_BLOCK; t < T; t += SEL_BLOCK) gather(margin_of(a, bias, e, t));
   __syncthreads();
   const int cnt = s_cnt;
   if (cnt <= GATHER_CAP) {
@@ -605,10 +666,24 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
 
   const int64_t ph = c[C_PHASE];
   if (ph == PH_ROUNDS) {
-    if (tid == 0 && c[C_ROUND]) {
+    if (c[C_ROUND] == 0) return;
+    // commit the round: largest bias decrease for the next top-k pivot
+    const int cur = static_cast<int>(c[C_CUR] & 1);
+    const int64_t* ob = a.bfx + cur * n;
+    const int64_t* nb = a.bfx + (cur ^ 1) * n;
+    int64_t dmax = 0;
+    for (int e = tid; e < n; e += blockDim.x) dmax = max(dmax, ob[e] - nb[e]);
+    s_red[tid] = dmax;
+    __syncthreads();
+    for (int st = 512; st > 0; st >>= 1) {
+      if (tid < st) s_red[tid] = max(s_red[tid], s_red[tid + st]);
+      __syncthreads();
+    }
+    if (tid == 0) {
       c[C_ROUND] = 0;
       c[C_CUR] ^= 1;
       c[C_ROUNDS] += 1;
+      c[C_DROP] = s_red[0];
       if (a.cnt[N_BIASRANGE]) {
         c[C_PHASE] = PH_FAILED;
         c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
@@ -755,6 +830,7 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
   __syncthreads();
   if (tid == 0) {
     c[C_MOVES] += 1;
+    c[C_DROP] = D;  // no bias fell by more than D
     c[C_LAST_D] = D;
     c[C_LAST_HOPS] = len - 1;
     c[C_BF_PASSES] += passes;
@@ -844,6 +920,7 @@ __global__ void center_and_export(Args a, double* bias_out, int32_t* info) {
   if ((sum % n != 0) && (sum < 0)) off -= 1;  // floor division
   if (!balanced) off = 0;
   __syncthreads();
+  if (threadIdx.x == 0) c[C_DROP] = off > 0 ? off : 0;  // every bias moves by -off
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     bias[e] -= off;
     if (bias_out) bias_out[e] = static_cast<double>(bias[e]) * (1.0 / 1099511627776.0);
@@ -863,7 +940,8 @@ __global__ void export_resid(Args a, int32_t* info) {
 }
 
 size_t topk_smem_bytes() {
-  return 1024 * 4 + 4 * EDGE_LIST_MAX * (8 + 8 + 4 + 4) + 8 * 4 + 4 * MAX_K * (8 + 4 + 4 + 4);
+  return 1024 * 4 + 4 * EDGE_LIST_MAX * (8 + 8 + 4 + 4) + 8 * 4 + 4 * MAX_K * (8 + 4 + 4 + 4) +
+         4 * 64 * 8 + 4 * 2 * 8 + 1024 * 8;
 }
 
 }  // namespace qb
@@ -891,16 +969,33 @@ size_t route_workspace_layout(int32_t T, int32_t n, RouteWorkspace* ws, void* ba
   return cv.bytes();
 }
 
-// Pinned host word the balancing loop polls (one per host thread, allocated
-// on first use and kept for the life of the process).
-static int64_t* phase_word() {
-  thread_local int64_t* word = nullptr;
-  if (!word) {
-    void* p = nullptr;
-    if (hipHostMalloc(&p, 64, hipHostMallocDefault) != hipSuccess) return nullptr;
-    word = static_cast<int64_t*>(p);
+// Pinned host words and events of the balancing loop (per host thread and
+// device, created on first use and kept for the life of the process): batch
+// i copies the phase word into slot i % 2 and records event i % 2.
+struct PollState {
+  int64_t* word = nullptr;  // [2][8] (one 64-byte line per slot)
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  bool ok = false;
+};
+
+static PollState* poll_state() {
+  constexpr int MAX_DEVICES = 64;
+  thread_local PollState st[MAX_DEVICES];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  PollState& p = st[dev];
+  if (!p.ok) {
+    if (!p.word) {
+      void* w = nullptr;
+      if (hipHostMalloc(&w, 128, hipHostMallocDefault) != hipSuccess) return nullptr;
+      p.word = static_cast<int64_t*>(w);
+    }
+    for (int i = 0; i < 2; ++i)
+      if (!p.ev[i] && hipEventCreateWithFlags(&p.ev[i], hipEventDisableTiming) != hipSuccess)
+        return nullptr;
+    p.ok = true;
   }
-  return word;
+  return &p;
 }
 
 int route_validate(int32_t T, int32_t n, int32_t k) {
@@ -949,10 +1044,16 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
     MOE_LAUNCH_CHECK();
   }
   if (mode == MOE_QB_BATCH && T > 0) {
+    // Batches of steps; while batch i runs the host waits for the phase word
+    // of batch i-1, so the queue never drains for a poll.  Steps launched
+    // after the loop has ended return at once.
     const int batch = 4;
     const int max_steps = max_rounds + 8 * MAX_SAP_MOVES + 64;
-    int steps = 0;
+    PollState* ps = poll_state();
+    if (!ps) return MOE_EHIP;
+    int steps = 0, launched = 0;
     while (true) {
+      const int slot = launched & 1;
       for (int i = 0; i < batch; ++i) {
         hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 0);
         hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), 0, stream, a);
@@ -960,14 +1061,17 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
         hipLaunchKernelGGL(finish_step, dim3(1), dim3(1024), 0, stream, a);
       }
       MOE_LAUNCH_CHECK();
-      steps += batch;
-      int64_t* hp = phase_word();
-      if (!hp) return MOE_EHIP;
-      MOE_HIP_CHECK(hipMemcpyAsync(hp, ws.ctrl + C_PHASE, sizeof(int64_t),
+      MOE_HIP_CHECK(hipMemcpyAsync(ps->word + 8 * slot, ws.ctrl + C_PHASE, sizeof(int64_t),
                                    hipMemcpyDeviceToHost, stream));
-      MOE_HIP_CHECK(hipStreamSynchronize(stream));
-      const int64_t phase = *hp;
-      if (phase == PH_DONE || phase == PH_FAILED) break;
+      MOE_HIP_CHECK(hipEventRecord(ps->ev[slot], stream));
+      ++launched;
+      steps += batch;
+      if (launched >= 2) {
+        const int prev = slot ^ 1;
+        MOE_HIP_CHECK(hipEventSynchronize(ps->ev[prev]));
+        const int64_t phase = ps->word[8 * prev];
+        if (phase == PH_DONE || phase == PH_FAILED) break;
+      }
       if (steps >= max_steps) break;
     }
   }
