@@ -24,6 +24,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+# HBM bytes per launch of the routed gate/up kernel, from rocprofv3 FETCH_SIZE
+# and WRITE_SIZE runs scaled by a 1 GiB device copy (profiles/
+# routed_gate_up_hbm_traffic.txt); None where not measured for the current
+# kernel.
+TRAFFIC = {"k3_prefill": None, "k3_decode": None, "k3_mxfp4": None}
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
 
 
@@ -109,6 +114,9 @@ def main():
     ap.add_argument("--qb", default="batch", choices=["batch", "frozen"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the run, one plain device-to-device copy of this many bytes "
+                         "(the reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -174,7 +182,16 @@ def main():
     gu_ms, gu_n = stages["routed_gate_up"]
     gu_avg_ms = gu_ms / max(gu_n, 1)
     gu_bytes = gate_up_bytes(shape, touched, shape.T)
-    achieved = gu_bytes / (gu_avg_ms / 1e3) / 1e9
+    gu_flops = 2.0 * shape.T * shape.k * (2 * shape.m) * shape.latent
+    if shape.routed == "mxfp4":
+        # codes are decoded to bf16 for the MFMA: compute-bound, bf16 dense peak
+        roof = {"bound": "mfma", "achieved": gu_flops / (gu_avg_ms / 1e3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": gu_bytes / (gu_avg_ms / 1e3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = TRAFFIC.get(args.workload)
     rec = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -193,10 +210,8 @@ def main():
                    "T": shape.T, "d": shape.d, "latent": shape.latent, "experts": shape.n,
                    "top_k": shape.k, "inter": shape.m, "shared_inter": shape.shared,
                    "routed_weights": shape.routed, "qb": args.qb},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "routed gate/up grouped GEMM + SiTU-GLU",
-                     "bytes_per_launch": gu_bytes, "avg_ms": gu_avg_ms},
+        "roofline": dict(roof, kernel="routed gate/up grouped GEMM + SiTU-GLU",
+                         bytes_per_launch=gu_bytes, flops_per_launch=gu_flops, avg_ms=gu_avg_ms),
         "layer": {
             "hbm_gbs": (wb_routed + wb_dense) / (ms_per_step / 1e3) / 1e9,
             "weight_bytes": wb_routed + wb_dense,
@@ -207,6 +222,12 @@ def main():
             "wall_s": wall,
         },
     }
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, shape, args.cpu_sample_tokens)
     print(json.dumps(rec), flush=True)

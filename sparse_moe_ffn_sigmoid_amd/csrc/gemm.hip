@@ -351,13 +351,24 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // 16-byte global -> LDS copy per lane (lane i fills bytes [16i, 16i+16) after
-// the wave-uniform LDS base).  The builtin exists only for the device pass;
-// the host pass of a template kernel that names it would drop its launch stub.
-__device__ __forceinline__ void load_lds16(const bf16_t* g, bf16_t* lds) {
+// the wave-uniform LDS base in M0).  Issued as inline assembly so that the
+// compiler does not track these LDS writes: it would otherwise wait for every
+// load in flight (vmcnt(0)) before the LDS reads of another stage, which
+// drains the ring.  The kernels order them explicitly (vmcnt waits, then a
+// barrier) and no other instruction in them uses M0.
+__device__ __forceinline__ void load_lds16_asm(const void* g, void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+  const uint32_t m =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m)
+               : "memory", "m0");
+#pragma clang diagnostic pop
 #endif
 }
+
+__device__ __forceinline__ void load_lds16(const bf16_t* g, bf16_t* lds) { load_lds16_asm(g, lds); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -372,7 +383,7 @@ __device__ __forceinline__ int swz(int r) {
   return BKP == 64 ? (r & 7) : ((r >> 1) & 3);
 }
 
-template <int BM, int BN, int WM, int EPI, int BKP>
+template <int BM, int BN, int WM, int EPI, int BKP, int NST>
 __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Params p) {
   constexpr int WN = 4 / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -393,12 +404,16 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Param
   auto a_ins = [](int w, int i) { const int x = w + 4 * i; return x < NA ? x : x - 4; };
   auto b_ins = [](int w, int i) { const int x = w + 4 * i; return x < NB ? x : x - 4; };
 
-  __shared__ __attribute__((aligned(1024))) bf16_t sA0[BM * BKP];
-  __shared__ __attribute__((aligned(1024))) bf16_t sA1[BM * BKP];
-  __shared__ __attribute__((aligned(1024))) bf16_t sA2[BM * BKP];
-  __shared__ __attribute__((aligned(1024))) bf16_t sB0[BN * BKP];
-  __shared__ __attribute__((aligned(1024))) bf16_t sB1[BN * BKP];
-  __shared__ __attribute__((aligned(1024))) bf16_t sB2[BN * BKP];
+  static_assert(NST == 3 || NST == 4, "ring depth");
+  // One LDS variable per stage (A rows, then B rows): the compiler tracks
+  // direct-to-LDS loads per variable, so reads of one stage do not wait for
+  // loads still in flight into another.
+  constexpr int SW = (BM + BN) * BKP;
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[SW];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[SW];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[SW];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST == 4 ? SW : 8];
+  bf16_t* const stg[4] = {st0, st1, st2, st3};
 
   const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
   Tile tile;
@@ -535,26 +550,34 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Param
     }
   };
 
-  // prologue: stages 0 and 1 in flight
-  if (ktot > 0) issue(sA0, sB0);
-  if (ktot > 1) issue(sA1, sB1);
-  // one ring step: wait for tile kt (tile kt+1 may stay in flight), refill the
-  // stage freed by tile kt-1 with tile kt+2, multiply tile kt
+  // prologue: tiles 0 .. NST-2 in flight
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < ktot) issue(stg[s], stg[s] + BM * BKP);
+  // one ring step: wait for tile kt (tiles kt+1 .. kt+NST-2 may stay in
+  // flight), refill the stage freed by tile kt-1 with tile kt+NST-1, multiply
+  // tile kt
   auto ring = [&](int kt, bf16_t* Ac, bf16_t* Bc, bf16_t* An, bf16_t* Bn) {
     if (kt < ktot) {  // uniform across the block
-      if (kt + 1 < ktot)
+      const int ahead = min(NST - 2, ktot - 1 - kt);  // tiles issued after tile kt
+      if (ahead >= 2)
+        wait_vmcnt<2 * (MA + MB)>();
+      else if (ahead == 1)
         wait_vmcnt<MA + MB>();
       else
         wait_vmcnt<0>();
       lds_barrier();
-      if (kt + 2 < ktot) issue(An, Bn);
+      if (kt + NST - 1 < ktot) issue(An, Bn);
       compute(Ac, Bc);
     }
   };
-  for (int kt = 0; kt < ktot; kt += STAGES) {
-    ring(kt, sA0, sB0, sA2, sB2);
-    ring(kt + 1, sA1, sB1, sA0, sB0);
-    ring(kt + 2, sA2, sB2, sA1, sB1);
+  for (int kt = 0; kt < ktot; kt += NST) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+      bf16_t* cur = stg[s];
+      bf16_t* nxt = stg[(s + NST - 1) % NST];
+      ring(kt + s, cur, cur + BM * BKP, nxt, nxt + BM * BKP);
+    }
   }
 
   // ---- epilogue straight from the accumulators ----
@@ -622,11 +645,7 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Param
 // v_cvt_scalef32_pk_bf16_fp4 (two E2M1 values times the block scale per
 // instruction).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void load_lds16_raw(const void* g, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-#endif
-}
+__device__ __forceinline__ void load_lds16_raw(const void* g, void* lds) { load_lds16_asm(g, lds); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -1037,7 +1056,7 @@ static int run_bf16(const Params& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-template <int BM, int BN, int WM, int EPI, int BKP>
+template <int BM, int BN, int WM, int EPI, int BKP, int NST>
 static int run_pipe(const Params& p, hipStream_t stream) {
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   for (int s = 0; s < p.nseg; ++s)
@@ -1047,18 +1066,26 @@ static int run_pipe(const Params& p, hipStream_t stream) {
   const int64_t G = static_cast<int64_t>(mt) * ntn * (p.ksplit > 1 ? p.ksplit : 1);
   if (G <= 0) return MOE_OK;
   const int64_t G8 = (G + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP>), dim3(static_cast<unsigned>(G8)),
+  hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP, NST>), dim3(static_cast<unsigned>(G8)),
                      dim3(NTHREADS), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+// Ring depth: 3 stages (a fourth measured no faster on the weight-streaming
+// 32-row tiles once the loads stay in flight across the LDS reads).
+template <int BM, int BN, int BKP>
+constexpr int pipe_stages() {
+  return 3;
+}
+
 template <int BM, int BN, int WM, int BKP>
 static int dispatch_pipe(const Params& p, int epi, hipStream_t s) {
+  constexpr int NST = pipe_stages<BM, BN, BKP>();
   switch (epi) {
-    case EPI_BF16: return run_pipe<BM, BN, WM, EPI_BF16, BKP>(p, s);
-    case EPI_F32: return run_pipe<BM, BN, WM, EPI_F32, BKP>(p, s);
-    case EPI_SIGMOID: return run_pipe<BM, BN, WM, EPI_SIGMOID, BKP>(p, s);
-    case EPI_SITU: return run_pipe<BM, BN, WM, EPI_SITU, BKP>(p, s);
+    case EPI_BF16: return run_pipe<BM, BN, WM, EPI_BF16, BKP, NST>(p, s);
+    case EPI_F32: return run_pipe<BM, BN, WM, EPI_F32, BKP, NST>(p, s);
+    case EPI_SIGMOID: return run_pipe<BM, BN, WM, EPI_SIGMOID, BKP, NST>(p, s);
+    case EPI_SITU: return run_pipe<BM, BN, WM, EPI_SITU, BKP, NST>(p, s);
     default: return MOE_EUNSUPPORTED;
   }
 }
@@ -1145,9 +1172,8 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
     Params q = p;
     q.ksplit = 1;
     if (bm_hint <= 32) return dispatch_pipe<32, 256, 1, 64>(q, epi, stream);
-    if (bm_hint <= 96)  // gate/up: 128-byte row pieces per stage measure faster
-      return epi == EPI_SITU ? dispatch_pipe<96, 256, 1, 64>(q, epi, stream)
-                             : dispatch_pipe<96, 256, 1, 32>(q, epi, stream);
+    if (bm_hint <= 96)  // 128-byte row pieces per stage, one block per CU
+      return dispatch_pipe<96, 256, 1, 64>(q, epi, stream);
     return dispatch_pipe<128, 128, 2, 32>(q, epi, stream);
   }
   if (bfmt == B_DENSE) {
