@@ -356,19 +356,25 @@ __device__ __forceinline__ void lds_barrier() {
 // load in flight (vmcnt(0)) before the LDS reads of another stage, which
 // drains the ring.  The kernels order them explicitly (vmcnt waits, then a
 // barrier) and no other instruction in them uses M0.
-__device__ __forceinline__ void load_lds16_asm(const void* g, void* lds) {
+__device__ __forceinline__ void load_lds16_asm(const void* g, void* lds, bool nt = false) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t m =
       __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m)
-               : "memory", "m0");
+  if (nt)  // read once: non-temporal cache policy
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(m)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m)
+                 : "memory", "m0");
 #pragma clang diagnostic pop
 #endif
 }
 
-__device__ __forceinline__ void load_lds16(const bf16_t* g, bf16_t* lds) { load_lds16_asm(g, lds); }
+__device__ __forceinline__ void load_lds16(const bf16_t* g, bf16_t* lds, bool nt = false) {
+  load_lds16_asm(g, lds, nt);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -383,7 +389,7 @@ __device__ __forceinline__ int swz(int r) {
   return BKP == 64 ? (r & 7) : ((r >> 1) & 3);
 }
 
-template <int BM, int BN, int WM, int EPI, int BKP, int NST>
+template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT>
 __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Params p) {
   constexpr int WN = 4 / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -517,7 +523,7 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Param
     }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      load_lds16(pb[i], Bs + b_ins(wave, i) * 512);
+      load_lds16(pb[i], Bs + b_ins(wave, i) * 512, BNT);
       pb[i] += BKP;
     }
   };
@@ -1056,7 +1062,7 @@ static int run_bf16(const Params& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-template <int BM, int BN, int WM, int EPI, int BKP, int NST>
+template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT>
 static int run_pipe(const Params& p, hipStream_t stream) {
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   for (int s = 0; s < p.nseg; ++s)
@@ -1066,7 +1072,7 @@ static int run_pipe(const Params& p, hipStream_t stream) {
   const int64_t G = static_cast<int64_t>(mt) * ntn * (p.ksplit > 1 ? p.ksplit : 1);
   if (G <= 0) return MOE_OK;
   const int64_t G8 = (G + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP, NST>), dim3(static_cast<unsigned>(G8)),
+  hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT>), dim3(static_cast<unsigned>(G8)),
                      dim3(NTHREADS), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -1078,14 +1084,16 @@ constexpr int pipe_stages() {
   return 3;
 }
 
-template <int BM, int BN, int WM, int BKP>
+// BNT: B rows are read by exactly one block (grouped problems with one row
+// tile per expert), so they are streamed with the non-temporal policy.
+template <int BM, int BN, int WM, int BKP, bool BNT = false>
 static int dispatch_pipe(const Params& p, int epi, hipStream_t s) {
   constexpr int NST = pipe_stages<BM, BN, BKP>();
   switch (epi) {
-    case EPI_BF16: return run_pipe<BM, BN, WM, EPI_BF16, BKP, NST>(p, s);
-    case EPI_F32: return run_pipe<BM, BN, WM, EPI_F32, BKP, NST>(p, s);
-    case EPI_SIGMOID: return run_pipe<BM, BN, WM, EPI_SIGMOID, BKP, NST>(p, s);
-    case EPI_SITU: return run_pipe<BM, BN, WM, EPI_SITU, BKP, NST>(p, s);
+    case EPI_BF16: return run_pipe<BM, BN, WM, EPI_BF16, BKP, NST, BNT>(p, s);
+    case EPI_F32: return run_pipe<BM, BN, WM, EPI_F32, BKP, NST, BNT>(p, s);
+    case EPI_SIGMOID: return run_pipe<BM, BN, WM, EPI_SIGMOID, BKP, NST, BNT>(p, s);
+    case EPI_SITU: return run_pipe<BM, BN, WM, EPI_SITU, BKP, NST, BNT>(p, s);
     default: return MOE_EUNSUPPORTED;
   }
 }
@@ -1171,9 +1179,10 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
     // rows per weight byte)
     Params q = p;
     q.ksplit = 1;
-    if (bm_hint <= 32) return dispatch_pipe<32, 256, 1, 64>(q, epi, stream);
+    // about one row tile per expert: each weight byte is read once
+    if (bm_hint <= 32) return dispatch_pipe<32, 256, 1, 64, true>(q, epi, stream);
     if (bm_hint <= 96)  // 128-byte row pieces per stage, one block per CU
-      return dispatch_pipe<96, 256, 1, 64>(q, epi, stream);
+      return dispatch_pipe<96, 256, 1, 64, true>(q, epi, stream);
     return dispatch_pipe<128, 128, 2, 32>(q, epi, stream);
   }
   if (bfmt == B_DENSE) {

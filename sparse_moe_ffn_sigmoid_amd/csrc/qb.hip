@@ -65,16 +65,16 @@ __host__ __device__ __forceinline__ int64_t target(int64_t T, int64_t n, int64_t
 __device__ __forceinline__ int64_t score_fixed(float s) {
   const uint32_t u = __float_as_uint(s);
   const int E = static_cast<int>((u >> 23) & 255u);
-  if (E == 0) return 0;
-  const uint64_t m = (u & 0x7FFFFFu) | 0x800000u;
+  const uint32_t m = (u & 0x7FFFFFu) | 0x800000u;
   const int sh = E - 110;
-  if (sh >= 0) return static_cast<int64_t>(m << sh);
+  if (sh >= 0) return static_cast<int64_t>(static_cast<uint64_t>(m) << sh);  // s >= 2^-17: exact
+  if (E == 0) return 0;
   const int r = -sh;
   if (r > 24) return 0;  // m < 2^24 <= 2^(r-1): below one half
-  const uint64_t q = m >> r;
-  const uint64_t rem = m & ((uint64_t(1) << r) - 1);
-  const uint64_t half = uint64_t(1) << (r - 1);
-  return static_cast<int64_t>(q + ((rem > half) || (rem == half && (q & 1))));
+  const uint32_t q = m >> r;                       // r <= 24: 32-bit arithmetic suffices
+  const uint32_t rem = m & ((1u << r) - 1u);
+  const uint32_t half = 1u << (r - 1);
+  return static_cast<int64_t>(q + ((rem > half) || (rem == half && (q & 1u))));
 }
 
 __device__ __forceinline__ uint64_t pack_key(int64_t sfx, int64_t b, int e) {
@@ -162,6 +162,21 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
   int64_t* sbias = reinterpret_cast<int64_t*>(thv + 4 * 2);              // [1024]
 
   const int n = a.n, k = a.k, T = a.T;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nj = (n + 63) >> 6;
+  // this wave's first token: its scores are requested before the block
+  // waits for the bias staging, so the two memory trips overlap
+  const int t_first = blockIdx.x * 4 + wv;
+  float sv[MAX_NJ];
+  auto load_scores = [&](int t) {
+    const float* row = a.scores + static_cast<size_t>(t) * n;
+#pragma unroll
+    for (int j = 0; j < MAX_NJ; ++j) {
+      const int e = lane + 64 * j;
+      sv[j] = (j < nj && e < n) ? row[e] : 0.f;
+    }
+  };
   const int64_t* gbias = a.bfx + (a.ctrl[C_CUR] & 1) * n;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     sload[e] = 0;
@@ -174,21 +189,19 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
   const bool use_pivot = a.ctrl[C_PIVOT] != 0 && k < n;
   const uint64_t drop_key = static_cast<uint64_t>(a.ctrl[C_DROP]) << IDX_BITS;
 
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int nj = (n + 63) >> 6;
   const int64_t* bias = sbias;
   const int64_t delta = a.ctrl[C_DELTA];
   const int rounds = (k < n) ? k + 1 : k;
 
-  for (int t = blockIdx.x * 4 + wv; t < T; t += gridDim.x * 4) {
+  for (int t = t_first; t < T; t += gridDim.x * 4) {
     const float* row = a.scores + static_cast<size_t>(t) * n;
+    load_scores(t);
     uint64_t key[MAX_NJ];
 #pragma unroll
     for (int j = 0; j < MAX_NJ; ++j) {
       const int e = lane + 64 * j;
       key[j] = 0;
-      if (j < nj && e < n) key[j] = pack_key(score_fixed(row[e]), bias[e], e);
+      if (j < nj && e < n) key[j] = pack_key(score_fixed(sv[j]), bias[e], e);
     }
     uint64_t thk = 0, thk1 = 0;
     bool found = false;
@@ -211,8 +224,13 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         if (lane < c) {
           const uint64_t v = cand[wv * 64 + lane];
-          int rank = 0;
-          for (int i = 0; i < c; ++i) rank += cand[wv * 64 + i] > v;
+          const uint64_t* cw = cand + wv * 64;
+          int rank = 0, i = 0;
+          for (; i + 8 <= c; i += 8) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) rank += cw[i + q] > v;
+          }
+          for (; i < c; ++i) rank += cw[i] > v;
           if (rank == k - 1) thv[wv * 2] = v;
           if (rank == k) thv[wv * 2 + 1] = v;
         }
@@ -274,9 +292,9 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
         if (sel) {
           const int pos = base + __popcll(bal & ((uint64_t(1) << lane) - 1));
           const int e = lane + 64 * j;
-          const float sv = row[e];
-          oSfx[wv * MAX_K + pos] = score_fixed(sv);
-          oS[wv * MAX_K + pos] = sv;
+          const float sval = row[e];
+          oSfx[wv * MAX_K + pos] = score_fixed(sval);
+          oS[wv * MAX_K + pos] = sval;
           oE[wv * MAX_K + pos] = e;
         }
         base += __popcll(bal);
@@ -369,6 +387,7 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
       }
     }
   }
+  // per-block counts, one global atomic per expert the block selected
   __syncthreads();
   for (int e = threadIdx.x; e < n; e += blockDim.x)
     if (sload[e]) atomicAdd(&a.acc[e], sload[e]);
