@@ -28,7 +28,9 @@ PEAK_BF16_TFLOPS = 2500.0
 # and WRITE_SIZE runs scaled by a 1 GiB device copy (profiles/
 # routed_gate_up_hbm_traffic.txt); None where not measured for the current
 # kernel.
-TRAFFIC = {"k3_prefill": None, "k3_decode": None, "k3_mxfp4": None}
+TRAFFIC = {"k3_prefill": 27.020e9,   # gemm_pipe<96, 256, 1, SITU, 64, 3, nt>
+           "k3_decode": 26.313e9,    # gemm_pipe<32, 256, 1, SITU, 64, 3, nt>
+           "k3_mxfp4": 23.495e9}     # gemm_pipe_fp4<128, 128, 2, SITU>
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
 
 
