@@ -390,7 +390,7 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT>
-__global__ __launch_bounds__(NTHREADS, (BKP == 32 ? 2 : 1)) void gemm_pipe(Params p) {
+__global__ __launch_bounds__(NTHREADS, (BKP == 32 && BM * BN <= 128 * 256) ? 2 : 1) void gemm_pipe(Params p) {
   constexpr int WN = 4 / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -990,12 +990,18 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
 // range is split so that about one wave of blocks runs, each split keeping
 // at least 4 stages.
 struct DensePlan {
-  int cfg;  // 0: 32x256 BKP 64, 1: 64x256 BKP 64, 2: 128x128 BKP 32
+  int cfg;  // 0: 32x256 BKP 64, 1: 64x256 BKP 64, 2: 128x128 BKP 32,
+            // 3: 256x128 BKP 32, 4: 256x256 BKP 32
   int bm, bn, bkp;
   int ntn, mt;
   int ks;
   size_t bytes;
 };
+
+static int tiles_of(int M, int N, int bm, int bn, int epi) {
+  const int bn_out = epi == EPI_SITU ? bn / 2 : bn;
+  return ((M + bm - 1) / bm) * ((N + bn_out - 1) / bn_out);
+}
 
 static DensePlan plan_dense(int M, int N, int K, int epi) {
   DensePlan d{};
@@ -1004,6 +1010,11 @@ static DensePlan plan_dense(int M, int N, int K, int epi) {
     d.cfg = 0; d.bm = 32; d.bn = 256; d.bkp = 64; target = 256;
   } else if (M <= 64) {
     d.cfg = 1; d.bm = 64; d.bn = 256; d.bkp = 64; target = 256;
+  } else if (M >= 256 && epi != EPI_SIGMOID && tiles_of(M, N, 256, 256, epi) >= 256) {
+    // large products: 128 x 128 per wave (0.5 KB of LDS reads per MFMA)
+    d.cfg = 4; d.bm = 256; d.bn = 256; d.bkp = 32; target = 256;
+  } else if (M >= 256 && tiles_of(M, N, 256, 128, epi) >= 256) {
+    d.cfg = 3; d.bm = 256; d.bn = 128; d.bkp = 32; target = 512;
   } else {
     d.cfg = 2; d.bm = 128; d.bn = 128; d.bkp = 32; target = 512;
   }
@@ -1197,6 +1208,10 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
       rc = dispatch_pipe<32, 256, 1, 64>(q, epi, stream);
     else if (d.cfg == 1)
       rc = dispatch_pipe<64, 256, 1, 64>(q, epi, stream);
+    else if (d.cfg == 4)
+      rc = dispatch_pipe<256, 256, 2, 32>(q, epi, stream);
+    else if (d.cfg == 3)
+      rc = dispatch_pipe<256, 128, 2, 32>(q, epi, stream);
     else
       rc = dispatch_pipe<128, 128, 2, 32>(q, epi, stream);
     if (rc != MOE_OK || q.ksplit == 1) return rc;
