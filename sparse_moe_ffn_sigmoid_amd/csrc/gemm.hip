@@ -675,7 +675,7 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 }
 
 template <int BM, int BN, int WM, int EPI>
-__global__ __launch_bounds__(NTHREADS, 2) void gemm_pipe_fp4(Params p) {
+__global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Params p) {
   constexpr int BKP = 64;
   constexpr int WN = 4 / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -1109,11 +1109,20 @@ static int dispatch_pipe(const Params& p, int epi, hipStream_t s) {
   }
 }
 
-// Panel bytes of the MXFP4 kernel and the largest panel it takes (two blocks
-// per CU within 160 KB of LDS).
+// Static LDS of the MXFP4 kernel, and the LDS a block may use in all (two
+// blocks per CU up to 128-row tiles, one block per CU for taller tiles).
 template <int BM, int BN>
 constexpr size_t fp4_static_lds() {
   return static_cast<size_t>(3) * (BM * 64 * 2 + BN * 32);
+}
+template <int BM>
+constexpr size_t fp4_lds_budget() {
+  return BM >= 160 ? 160 * 1024 : 80 * 1024;
+}
+
+size_t fp4_tall_tile_fits(int K) {
+  return K % 512 == 0 && fp4_static_lds<160, 256>() + static_cast<size_t>(256) * (K / 32) <=
+                             fp4_lds_budget<160>();
 }
 
 // Returns 1 when the shape does not fit the pipelined MXFP4 kernel (the caller
@@ -1130,7 +1139,7 @@ static int run_pipe_fp4(const Params& p, hipStream_t stream) {
                           static_cast<uintptr_t>(p.bs_expert_stride);
   if (align % 16 != 0) return 1;
   const size_t panel = static_cast<size_t>(BN) * (p.seg[0].K / 32);
-  if (fp4_static_lds<BM, BN>() + panel > 80 * 1024) return 1;
+  if (fp4_static_lds<BM, BN>() + panel > fp4_lds_budget<BM>()) return 1;
   const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
   const int mt = p.tiles ? p.max_mtiles : (p.M + BM - 1) / BM;
   const int64_t G = static_cast<int64_t>(mt) * ntn;
@@ -1140,7 +1149,8 @@ static int run_pipe_fp4(const Params& p, hipStream_t stream) {
   if (!configured) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(80 * 1024 - fp4_static_lds<BM, BN>())) != hipSuccess)
+                            static_cast<int>(fp4_lds_budget<BM>() - fp4_static_lds<BM, BN>())) !=
+        hipSuccess)
       return MOE_EHIP;
     configured = true;
   }
@@ -1227,6 +1237,16 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
   // decoded per fragment; shapes outside that kernel's limits use the
   // register-staged kernel that decodes while writing LDS
   int rc = 1;
+  if (bm_hint == 160) {
+    // tiles were cut 160 rows tall: only the pipelined kernel takes them
+    if (epi == EPI_SITU)
+      rc = run_pipe_fp4<160, 256, 1, EPI_SITU>(p, stream);
+    else if (epi == EPI_BF16)
+      rc = run_pipe_fp4<160, 256, 1, EPI_BF16>(p, stream);
+    else if (epi == EPI_F32)
+      rc = run_pipe_fp4<160, 256, 1, EPI_F32>(p, stream);
+    return rc == 1 ? MOE_EUNSUPPORTED : rc;
+  }
   if (epi == EPI_SITU)
     rc = bm_hint <= 32 ? run_pipe_fp4<32, 256, 1, EPI_SITU>(p, stream)
                        : run_pipe_fp4<128, 128, 2, EPI_SITU>(p, stream);

@@ -54,6 +54,9 @@ struct Params {
 // Bytes of fp32 partials launch() uses for a bf16 dense problem (0: no split).
 size_t splitk_bytes(int M, int N, int K, int epi);
 
+// Whether the pipelined MXFP4 kernel takes 160-row tiles for this K.
+size_t fp4_tall_tile_fits(int K);
+
 // Launch helpers (defined in gemm.hip).  `act_bf16` selects the bf16 MFMA
 // kernels, otherwise the fp32 kernels run.
 int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipStream_t stream);

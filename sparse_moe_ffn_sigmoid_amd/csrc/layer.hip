@@ -201,7 +201,13 @@ static int grouped_bm(const moe_shape_t& s) {
   const int64_t avg = (static_cast<int64_t>(s.T) * s.top_k + s.n_experts - 1) / s.n_experts;
   if (s.act_dtype != MOE_BF16) return 64;
   if (avg <= 32) return 32;
-  if (avg <= 96 && s.routed_dtype != MOE_MXFP4) return 96;
+  if (s.routed_dtype == MOE_MXFP4) {
+    // MFMA-bound: 160-row tiles (5 x 2 fragments per wave) when the
+    // pipelined MXFP4 kernel takes both K widths
+    if (gemm::fp4_tall_tile_fits(s.latent) && gemm::fp4_tall_tile_fits(s.inter)) return 160;
+    return 128;
+  }
+  if (avg <= 96) return 96;
   return 128;
 }
 

@@ -61,13 +61,15 @@ def test_mxfp4_layer():
 
 
 # Widths that are multiples of 512 take the pipelined MXFP4 kernel (scale
-# panel in LDS); the others take the register-staged one.  Cases cover both
-# tile shapes (few / many rows per expert) and column tails.
+# panel in LDS); the others take the register-staged one.  Cases cover the
+# tile shapes (few rows per expert: 32 x 256; many: 160 x 256), row and
+# column tails.
 @pytest.mark.parametrize("kw", [
     dict(T=300, k=4, d=1024, latent=512, m=512),              # 32x256 tiles, both GEMMs
     dict(T=300, k=4, d=1024, latent=512, m=576),              # gate/up column tail
     dict(T=300, k=4, d=1024, latent=640, m=512),              # down column tail
-    dict(T=640, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 128x128 tiles
+    dict(T=640, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 160-row tiles, full
+    dict(T=700, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 160-row tiles + 15-row tail
 ])
 def test_mxfp4_layer_pipelined(kw):
     check_layer(workloads.small_shape(routed="mxfp4", **kw), seed=5, name=f"mxfp4 {kw}")
