@@ -30,7 +30,8 @@ PEAK_BF16_TFLOPS = 2500.0
 # kernel.
 TRAFFIC = {"k3_prefill": 27.020e9,   # gemm_pipe<96, 256, 1, SITU, 64, 3, nt>
            "k3_decode": 26.313e9,    # gemm_pipe<32, 256, 1, SITU, 64, 3, nt>
-           "k3_mxfp4": 23.495e9}     # gemm_pipe_fp4<128, 128, 2, SITU>
+           "k3_mxfp4": None,         # kernel changed since measured
+           "k3_prefill_16k": None}
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
 
 
@@ -112,7 +113,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="k3_prefill",
-                    choices=["k3_prefill", "k3_decode", "k3_mxfp4"])
+                    choices=["k3_prefill", "k3_decode", "k3_mxfp4", "k3_prefill_16k"])
     ap.add_argument("--qb", default="batch", choices=["batch", "frozen"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -185,8 +186,9 @@ def main():
     gu_avg_ms = gu_ms / max(gu_n, 1)
     gu_bytes = gate_up_bytes(shape, touched, shape.T)
     gu_flops = 2.0 * shape.T * shape.k * (2 * shape.m) * shape.latent
-    if shape.routed == "mxfp4":
-        # codes are decoded to bf16 for the MFMA: compute-bound, bf16 dense peak
+    if shape.routed == "mxfp4" or shape.T * shape.k >= 32 * shape.n * 8:
+        # codes decoded to bf16, or hundreds of rows per expert: compute-bound,
+        # bf16 dense MFMA peak
         roof = {"bound": "mfma", "achieved": gu_flops / (gu_avg_ms / 1e3) / 1e12,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     else:
@@ -208,7 +210,8 @@ def main():
         "dtype": "bf16" if shape.act == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights, skewed router offsets)",
         "config": {"workload": {"k3_prefill": "k3_prefill_bf16", "k3_decode": "k3_decode_bf16",
-                                "k3_mxfp4": "k3_prefill_mxfp4"}[args.workload],
+                                "k3_mxfp4": "k3_prefill_mxfp4",
+                                "k3_prefill_16k": "k3_prefill_bf16_16k"}[args.workload],
                    "T": shape.T, "d": shape.d, "latent": shape.latent, "experts": shape.n,
                    "top_k": shape.k, "inter": shape.m, "shared_inter": shape.shared,
                    "routed_weights": shape.routed, "qb": args.qb},

@@ -35,7 +35,8 @@ struct Tile {
 // the 8 XCDs round robin), M-tile-major so one XCD's L2 reuses the A rows.
 // Grouped problems launch for an upper bound on the tile count; the mapping
 // spreads only the tiles that exist (the device count) over the XCDs and the
-// surplus blocks exit.
+// surplus blocks exit.  Grouped tiles are ordered in pairs of row tiles per
+// column tile.
 template <int BM>
 __device__ __forceinline__ bool locate_tile(const Params& p, int ntn, int bn_out, Tile& t) {
   const int b = blockIdx.x;
@@ -46,7 +47,18 @@ __device__ __forceinline__ bool locate_tile(const Params& p, int ntn, int bn_out
     if (b >= gv8) return false;
     const int tau = (b & 7) * (gv8 >> 3) + (b >> 3);
     if (tau >= gv) return false;
-    const int mt = tau / ntn, nt = tau - mt * ntn;
+    // pairs of row tiles per column tile: the two row tiles of a tall expert
+    // read the same weight rows side by side (one XCD's L2)
+    int mt, nt;
+    const int pair = tau / (2 * ntn);
+    if (2 * pair + 1 < nt_m) {
+      const int r = tau - pair * 2 * ntn;
+      nt = r >> 1;
+      mt = 2 * pair + (r & 1);
+    } else {  // an odd last row tile
+      mt = 2 * pair;
+      nt = tau - pair * 2 * ntn;
+    }
     const int32_t* q = p.tiles + 4 * mt;
     t.expert = q[0];
     t.row0 = q[1];
@@ -1204,6 +1216,9 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
     if (bm_hint <= 32) return dispatch_pipe<32, 256, 1, 64, true>(q, epi, stream);
     if (bm_hint <= 96)  // 128-byte row pieces per stage, one block per CU
       return dispatch_pipe<96, 256, 1, 64, true>(q, epi, stream);
+    // tall experts (MFMA-bound): 160 x 64 or 128 x 128 per wave
+    if (bm_hint == 160) return dispatch_pipe<160, 256, 1, 64>(q, epi, stream);
+    if (bm_hint == 256) return dispatch_pipe<256, 256, 2, 32>(q, epi, stream);
     return dispatch_pipe<128, 128, 2, 32>(q, epi, stream);
   }
   if (bfmt == B_DENSE) {

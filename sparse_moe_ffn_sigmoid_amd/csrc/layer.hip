@@ -196,7 +196,9 @@ struct ForwardWorkspace {
 };
 
 // Tile height of the grouped expert GEMMs, from the mean rows per expert
-// (exact under QB): 32 for decode-like batches, 96 up to 96 rows, else 128.
+// (exact under QB): 32 for decode-like batches, 96 up to 96 rows, 160 up to
+// 320 rows (one or two tiles per expert), else 256; MXFP4 takes 160 when its
+// pipelined kernel applies, else 128.
 static int grouped_bm(const moe_shape_t& s) {
   const int64_t avg = (static_cast<int64_t>(s.T) * s.top_k + s.n_experts - 1) / s.n_experts;
   if (s.act_dtype != MOE_BF16) return 64;
@@ -208,7 +210,8 @@ static int grouped_bm(const moe_shape_t& s) {
     return 128;
   }
   if (avg <= 96) return 96;
-  return 128;
+  if (avg <= 320) return 160;  // one or two 160-row tiles per expert
+  return 256;
 }
 
 static size_t forward_layout(const moe_shape_t& s, ForwardWorkspace* fw, void* base) {

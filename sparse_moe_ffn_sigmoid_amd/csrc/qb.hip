@@ -678,9 +678,10 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
   __shared__ uint64_t d[1024];
   __shared__ int64_t s_red[1024];
   __shared__ int s_flag;
-  __shared__ int s_path[1025];
+  __shared__ int16_t s_path[1032];
   __shared__ int s_len;
-  constexpr int EDGE_CACHE = 12288;
+  // 16384 cached edges (128 KB) + the state above and below: about 150 KB
+  constexpr int EDGE_CACHE = 16384;
   __shared__ uint64_t s_edges[EDGE_CACHE];
 
   const int64_t ph = c[C_PHASE];
@@ -733,7 +734,8 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
     return;
   }
   // sources: overloaded experts at distance 0
-  __shared__ int s_over[1024], s_under[1024], s_pos[1024];
+  __shared__ uint8_t s_over[1024], s_under[1024];
+  __shared__ int16_t s_pos[1024];
   __shared__ int s_bad;
   bool under_e = false;
   if (tid < n) {
@@ -816,7 +818,7 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
     int len = 0;
     bool ok = true;
     while (true) {
-      s_path[len++] = v;
+      s_path[len++] = static_cast<int16_t>(v);
       if (s_over[v]) break;
       v = static_cast<int>(d[v] & 1023);
       if (len > n) {
@@ -837,7 +839,7 @@ __global__ __launch_bounds__(1024) void finish_step(Args a) {
   }
   // the i-th expert from the source gains i grid units (s_path[len-1] is the
   // source, s_path[0] = u*); a vertex appears once on a predecessor path
-  if (tid < len) s_pos[s_path[len - 1 - tid]] = tid;
+  if (tid < len) s_pos[s_path[len - 1 - tid]] = static_cast<int16_t>(tid);
   __syncthreads();
   // every expert drops by D - min(d, D), then the path shift is added
   if (tid < n) {

@@ -51,6 +51,7 @@ def test_tiny_fp32_layer():
     dict(),                                                   # several tiles, ragged rows
     dict(T=37, n=24, k=3, d=448, latent=192, m=128, shared=192),
     dict(T=16, n=64, k=4),                                     # ~1 row per expert (small-M tile)
+    dict(T=600, n=16, k=4),                                    # 150 rows per expert: one 160-row tile
 ])
 def test_bf16_layer(kw):
     check_layer(workloads.small_shape(**kw), seed=1, name=f"bf16 {kw}")

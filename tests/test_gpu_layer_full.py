@@ -12,6 +12,8 @@ checked against the float64 oracle:
   oracle's weights computed from the same scores (experts decoded one at a
   time), max|diff| / rms(ref) within the bf16 / MXFP4 bounds.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -85,10 +87,22 @@ def check_routing(shape, got, qb_mode):
     ("k3_prefill", qb.MODE_BATCH),
     ("k3_mxfp4", qb.MODE_BATCH),
     ("k3_mxfp4", qb.MODE_FROZEN),
+    ("k3_prefill_16k", qb.MODE_BATCH),
 ])
 def test_full_size_layer_sampled(wl, qb_mode):
-    shape = workloads.SHAPES[wl]
-    announce(f"full-size layer {wl} qb_mode={qb_mode}")
+    check_sampled(workloads.SHAPES[wl], qb_mode, wl)
+
+
+# K3 widths with fewer experts, so that each expert holds 150, 300 or 512 rows:
+# one 160-row tile, two 160-row tiles (ragged), two 256 x 256 tiles.
+@pytest.mark.parametrize("T,n", [(600, 64), (1200, 64), (2048, 64)])
+def test_tall_expert_tiles_k3_width(T, n):
+    shape = dataclasses.replace(workloads.SHAPES["k3_prefill"], T=T, n=n)
+    check_sampled(shape, qb.MODE_BATCH, f"T={T} n={n}")
+
+
+def check_sampled(shape, qb_mode, name):
+    announce(f"layer {name} qb_mode={qb_mode}")
     inp, got = forward_as_benchmarked(shape, qb_mode)
     T = shape.T
     tokens = np.unique(np.array([0, T // 3, (2 * T) // 3, T - 1]))

@@ -58,6 +58,10 @@ SHAPES = {
                             7168 ** -0.5, 0.5),
     "k3_mxfp4": LayerShape(16384, 7168, 3584, 896, 16, 2048, 6144, "bf16", "mxfp4",
                            7168 ** -0.5, 1.0),
+    # the bf16 prefill layer at 16384 tokens: compute-bound (MFMA) instead of
+    # bound by streaming the routed weights
+    "k3_prefill_16k": LayerShape(16384, 7168, 3584, 896, 16, 2048, 6144, "bf16", "bf16",
+                                 7168 ** -0.5, 0.5),
 }
 
 QB_SHAPE = dict(T=57344, n=896, k=16, offset_std=0.5)
