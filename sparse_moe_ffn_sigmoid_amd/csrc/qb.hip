@@ -21,8 +21,11 @@
 // distances up to D* are exact whenever D* <= Delta, otherwise Delta grows.
 //
 // Control flow lives on the device: a step is [top-k pass, status, quantile
-// round, finish] and every kernel reads the phase word first, so the host
-// only launches batches of steps and polls the phase.
+// round] and every kernel reads the phase word first, so the host only
+// launches batches of steps and polls the phase.  A quantile round becomes
+// live in the next step: the top-k pass reads its biases from the idle
+// buffer, the status pass commits it; an augmenting-path move is made by the
+// status pass itself.
 #include "prof.hpp"
 #include "route.hpp"
 
@@ -44,16 +47,25 @@ constexpr int EDGE_LIST_MAX = 64;     // per token: low chosen / high unchosen c
 constexpr int64_t DELTA_START = int64_t(1) << 30;
 constexpr int64_t DELTA_MAX = int64_t(1) << 44;
 constexpr int64_t DELTA_MIN = int64_t(1) << 16;
+// The top-k pass adds its per-block loads into one of ACC_COPIES copies of
+// the load counters (chosen by block index), so that the device-wide atomics
+// on one counter do not serialise across every block; the status pass sums
+// the copies.
+constexpr int ACC_COPIES = 32;
+constexpr int TOPK_MAX_GRID = 768;    // top-k blocks: three resident per CU; waves loop over tokens
 
 enum Phase : int64_t { PH_ROUNDS = 0, PH_SAP = 1, PH_DONE = 2, PH_FAILED = 3, PH_FROZEN = 4 };
 enum Ctrl {
   C_PHASE = 0, C_ROUNDS, C_BEST, C_SINCE, C_MOVES, C_IMB, C_RESID, C_STATUS, C_DELTA,
   C_EDGES_VALID, C_CUR, C_ROUND, C_MAX_ROUNDS, C_LAST_D, C_LAST_HOPS, C_BF_PASSES,
-  C_PIVOT,  // th_k1 holds every token's (k+1)-th key of the last top-k pass
+  C_PIVOT,  // th[].k1 holds every token's (k+1)-th key of the last top-k pass
   C_DROP,   // largest bias decrease (grid units) since that pass
   C_COUNT = 32
 };
-enum Cnt { N_EDGES = 0, N_OVERFLOW, N_BIASRANGE, N_COUNT = 8 };
+// The edge list is split into EDGE_SEGS segments with one counter each
+// (chosen by block index), for the same reason as the load counters.
+constexpr int EDGE_SEGS = 32;
+enum Cnt { N_OVERFLOW = 1, N_BIASRANGE = 2, N_SEG0 = 8, N_COUNT = N_SEG0 + EDGE_SEGS };
 
 __host__ __device__ __forceinline__ int64_t target(int64_t T, int64_t n, int64_t k, int64_t e) {
   return (T * k) / n + (e < (T * k) % n ? 1 : 0);
@@ -122,13 +134,12 @@ struct Args {
   const float* scoresT;  // [n][T]
   int T, n, k;
   int64_t* bfx;          // [2][n] biases, ctrl[C_CUR] selects the live half
-  int64_t* th_k;         // [T]
-  int64_t* th_k1;        // [T]
+  KeyPair* th;           // [T]
   int32_t* loads;        // [n]
-  int32_t* acc;          // [n] loads accumulated by the top-k pass
+  int32_t* acc;          // [ACC_COPIES][n] loads accumulated by the top-k pass
   int64_t* ctrl;         // [C_COUNT]
   int32_t* cnt;          // [N_COUNT]
-  uint64_t* edges;       // [edge_cap]
+  uint64_t* edges;       // [EDGE_SEGS][edge_cap / EDGE_SEGS]
   int32_t edge_cap;
   int32_t* idx;          // [T][k] or null
   float* w;              // [T][k] or null
@@ -165,8 +176,8 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int nj = (n + 63) >> 6;
-  // this wave's first token: its scores are requested before the block
-  // waits for the bias staging, so the two memory trips overlap
+  // this wave's tokens: t_first, t_first + 4 * gridDim.x, ...; each token's
+  // scores are requested while the previous token is ranked
   const int t_first = blockIdx.x * 4 + wv;
   float sv[MAX_NJ];
   auto load_scores = [&](int t) {
@@ -177,25 +188,53 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
       sv[j] = (j < nj && e < n) ? row[e] : 0.f;
     }
   };
-  const int64_t* gbias = a.bfx + (a.ctrl[C_CUR] & 1) * n;
+  if (t_first < T) load_scores(t_first);  // in flight during the bias staging
+  // A quantile round of the previous step is committed by the status pass
+  // that follows this one; until then its biases (in the idle buffer) are
+  // the live ones, and the largest bias decrease is taken here.
+  const bool pending = a.ctrl[C_PHASE] == PH_ROUNDS && a.ctrl[C_ROUND] != 0;
+  const int cur = static_cast<int>(a.ctrl[C_CUR] & 1) ^ (pending ? 1 : 0);
+  const int64_t* gbias = a.bfx + cur * n;
+  const int64_t* obias = a.bfx + (cur ^ 1) * n;
+  uint64_t dmax = 0;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     sload[e] = 0;
-    sbias[e] = gbias[e];
+    const int64_t b = gbias[e];
+    sbias[e] = b;
+    if (pending) {
+      const int64_t dec = obias[e] - b;
+      dmax = dec > static_cast<int64_t>(dmax) ? static_cast<uint64_t>(dec) : dmax;
+    }
+  }
+  __shared__ uint64_t s_dmax[TOPK_BLOCK / 64];
+  if (pending) {
+    const uint64_t m = wave_max_u64(dmax);
+    if (lane == 0) s_dmax[wv] = m;
   }
   __syncthreads();
   // Pivot: every key of the last pass's top k+1 has dropped by at most
-  // `drop`, so at least k+1 keys are >= th_k1 - drop; when at most 64 are,
+  // `drop`, so at least k+1 keys are >= th.k1 - drop; when at most 64 are,
   // the k-th and (k+1)-th keys are found by ranking those candidates.
   const bool use_pivot = a.ctrl[C_PIVOT] != 0 && k < n;
-  const uint64_t drop_key = static_cast<uint64_t>(a.ctrl[C_DROP]) << IDX_BITS;
+  uint64_t drop = static_cast<uint64_t>(a.ctrl[C_DROP]);
+  if (pending) {
+    drop = 0;
+    for (int i = 0; i < TOPK_BLOCK / 64; ++i) drop = s_dmax[i] > drop ? s_dmax[i] : drop;
+  }
+  const uint64_t drop_key = drop << IDX_BITS;
 
   const int64_t* bias = sbias;
   const int64_t delta = a.ctrl[C_DELTA];
+  const int seg = blockIdx.x & (EDGE_SEGS - 1);
+  const int seg_cap = a.edge_cap / EDGE_SEGS;
   const int rounds = (k < n) ? k + 1 : k;
 
-  for (int t = t_first; t < T; t += gridDim.x * 4) {
+  const int stride = gridDim.x * 4;
+  for (int t = t_first; t < T; t += stride) {
     const float* row = a.scores + static_cast<size_t>(t) * n;
-    load_scores(t);
+    // the pivot is requested before the next token's scores, so waiting for
+    // it leaves that prefetch in flight
+    const uint64_t prev = use_pivot ? static_cast<uint64_t>(a.th[t].k1) : 0;
     uint64_t key[MAX_NJ];
 #pragma unroll
     for (int j = 0; j < MAX_NJ; ++j) {
@@ -203,10 +242,10 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
       key[j] = 0;
       if (j < nj && e < n) key[j] = pack_key(score_fixed(sv[j]), bias[e], e);
     }
+    if (t + stride < T) load_scores(t + stride);
     uint64_t thk = 0, thk1 = 0;
     bool found = false;
     if (use_pivot) {
-      const uint64_t prev = static_cast<uint64_t>(a.th_k1[t]);
       const uint64_t P = prev > drop_key ? prev - drop_key : 1;
       int c = 0;
 #pragma unroll
@@ -270,10 +309,7 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
           key[j] = pack_key(score_fixed(row[e]), bias[e], e);
         }
     }
-    if (lane == 0) {
-      a.th_k[t] = static_cast<int64_t>(thk);
-      a.th_k1[t] = static_cast<int64_t>(thk1);
-    }
+    if (lane == 0) a.th[t] = KeyPair{static_cast<int64_t>(thk), static_cast<int64_t>(thk1)};
     uint32_t selmask = 0;
 #pragma unroll
     for (int j = 0; j < MAX_NJ; ++j)
@@ -374,10 +410,11 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
             const int64_t rho =
                 lowKp[wv * EDGE_LIST_MAX + ia] - highKp[wv * EDGE_LIST_MAX + ib] - (A > B ? 1 : 0);
             if (rho <= delta) {
-              const int slot = atomicAdd(&a.cnt[N_EDGES], 1);
-              if (slot < a.edge_cap)
-                a.edges[slot] = (static_cast<uint64_t>(rho) << 20) |
-                                (static_cast<uint64_t>(A) << 10) | static_cast<uint64_t>(B);
+              const int slot = atomicAdd(&a.cnt[N_SEG0 + seg], 1);
+              if (slot < seg_cap)
+                a.edges[static_cast<size_t>(seg) * seg_cap + slot] =
+                    (static_cast<uint64_t>(rho) << 20) | (static_cast<uint64_t>(A) << 10) |
+                    static_cast<uint64_t>(B);
               else
                 atomicOr(&a.cnt[N_OVERFLOW], 1);
             }
@@ -389,79 +426,305 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
   }
   // per-block counts, one global atomic per expert the block selected
   __syncthreads();
+  int32_t* acc = a.acc + (blockIdx.x & (ACC_COPIES - 1)) * n;
   for (int e = threadIdx.x; e < n; e += blockDim.x)
-    if (sload[e]) atomicAdd(&a.acc[e], sload[e]);
+    if (sload[e]) atomicAdd(&acc[e], sload[e]);
   if (emit_edges && blockIdx.x == 0 && threadIdx.x == 0) a.ctrl[C_EDGES_VALID] = 1;
 }
 
 // ---------------------------------------------------------------------------
-// Status: take the accumulated loads (and clear the accumulator), then decide the next phase exactly as
-// the schedule prescribes (rounds until the unbalanced count stalls, then
-// augmenting paths, then done).
+// One augmenting-path move (all 1024 threads of the status block): shortest
+// distances from the overloaded experts over this step's sparse edge list,
+// then every expert drops by D - min(d, D) and the path to the nearest
+// underloaded expert is shifted by one grid unit per hop.
+// ---------------------------------------------------------------------------
+__device__ void sap_move(const Args& a) {
+  int64_t* c = a.ctrl;
+  const int n = a.n;
+  const int tid = threadIdx.x;
+  __shared__ uint64_t d[1024];
+  __shared__ int64_t s_red[1024];
+  __shared__ int s_flag;
+  __shared__ int16_t s_path[1032];
+  __shared__ int s_len;
+  // 16384 cached edges (128 KB) + the state above and below: about 150 KB
+  constexpr int EDGE_CACHE = 16384;
+  __shared__ uint64_t s_edges[EDGE_CACHE];
+  __shared__ int s_seg_off[EDGE_SEGS + 1];
+
+
+  const int cur = static_cast<int>(c[C_CUR] & 1);
+  int64_t* bias = a.bfx + cur * n;
+  const int64_t delta = c[C_DELTA];
+  const int seg_cap = a.edge_cap / EDGE_SEGS;
+  if (tid == 0) {
+    int tot = 0;
+    for (int sg = 0; sg < EDGE_SEGS; ++sg) {
+      s_seg_off[sg] = tot;
+      const int m = a.cnt[N_SEG0 + sg];
+      tot += m < seg_cap ? m : seg_cap;
+    }
+    s_seg_off[EDGE_SEGS] = tot;
+  }
+  const bool overflow = a.cnt[N_OVERFLOW] != 0;
+  __syncthreads();
+  const int nedges = s_seg_off[EDGE_SEGS];
+  // every segment counter is cleared by the end of the move
+  auto clear_edges = [&]() {
+    if (tid < EDGE_SEGS) a.cnt[N_SEG0 + tid] = 0;
+    if (tid == 0) c[C_EDGES_VALID] = 0;
+  };
+  if (overflow) {
+    if (tid == 0) {
+      if (delta / 4 < DELTA_MIN) {
+        c[C_PHASE] = PH_FAILED;
+        c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
+      } else {
+        c[C_DELTA] = delta / 4;
+      }
+      a.cnt[N_OVERFLOW] = 0;
+    }
+    clear_edges();
+    return;
+  }
+  // sources: overloaded experts at distance 0
+  __shared__ uint8_t s_over[1024], s_under[1024];
+  __shared__ int16_t s_pos[1024];
+  __shared__ int s_bad;
+  bool under_e = false;
+  if (tid < n) {
+    const int64_t C = target(a.T, n, a.k, tid);
+    const int32_t L = a.loads[tid];
+    s_over[tid] = L > C;
+    under_e = L < C;
+    s_under[tid] = under_e;
+    s_pos[tid] = 0;
+    d[tid] = L > C ? static_cast<uint64_t>(tid) : PACKED_INF;
+  }
+  const bool cached = nedges <= EDGE_CACHE;
+  if (cached)
+    for (int sg = 0; sg < EDGE_SEGS; ++sg) {
+      const int off = s_seg_off[sg], m = s_seg_off[sg + 1] - off;
+      for (int i = tid; i < m; i += blockDim.x)
+        s_edges[off + i] = a.edges[static_cast<size_t>(sg) * seg_cap + i];
+    }
+  // Relaxation passes.  s_D is the running minimum distance of an
+  // underloaded expert (it only decreases); a pass that lowers some distance
+  // to at most s_D asks for another pass.  Flagging against the running value
+  // flags a superset of "changed at or below the final D*", so the passes
+  // stop only when every distance <= D* and its predecessor is final.
+  __shared__ unsigned long long s_D;
+  if (tid == 0) {
+    s_D = static_cast<unsigned long long>(DIST_INF);
+    s_bad = 0;
+  }
+  __syncthreads();
+  if (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) < DIST_INF)
+    atomicMin(&s_D, static_cast<unsigned long long>(d[tid] >> IDX_BITS));
+  int passes = 0;
+  while (true) {
+    if (tid == 0) s_flag = 0;
+    __syncthreads();
+    for (int i = tid; i < nedges; i += blockDim.x) {
+      uint64_t ed;
+      if (cached) {
+        ed = s_edges[i];
+      } else {
+        int sg = 0;
+        while (i >= s_seg_off[sg + 1]) ++sg;
+        ed = a.edges[static_cast<size_t>(sg) * seg_cap + (i - s_seg_off[sg])];
+      }
+      const int B = static_cast<int>(ed & 1023);
+      const int A = static_cast<int>((ed >> 10) & 1023);
+      const int64_t rho = static_cast<int64_t>(ed >> 20);
+      const int64_t dA = static_cast<int64_t>(d[A] >> IDX_BITS);
+      if (dA >= DIST_INF) continue;
+      const int64_t cand = dA + rho;
+      if (cand >= DIST_INF) continue;
+      const uint64_t pk = (static_cast<uint64_t>(cand) << IDX_BITS) | static_cast<uint64_t>(A);
+      if (pk < d[B]) {
+        const uint64_t old = atomicMin(reinterpret_cast<unsigned long long*>(&d[B]), pk);
+        if (pk < old) {
+          if (s_under[B]) atomicMin(&s_D, static_cast<unsigned long long>(cand));
+          if (static_cast<uint64_t>(cand) <= s_D) s_flag = 1;
+        }
+      }
+    }
+    __syncthreads();
+    ++passes;
+    const int go = s_flag;
+    __syncthreads();
+    if (!go || passes > 4 * 1024) break;
+  }
+  const int64_t D = static_cast<int64_t>(s_D);
+  if (D >= DIST_INF || D > delta) {
+    if (tid == 0) {
+      if (delta >= DELTA_MAX) {
+        c[C_PHASE] = PH_FAILED;
+        c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
+      } else {
+        c[C_DELTA] = delta * 16;
+      }
+    }
+    clear_edges();
+    return;
+  }
+  // u* = lowest underloaded expert at distance D
+  s_red[tid] = (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) == D) ? tid : 1 << 30;
+  __syncthreads();
+  for (int st = 512; st > 0; st >>= 1) {
+    if (tid < st) s_red[tid] = min(s_red[tid], s_red[tid + st]);
+    __syncthreads();
+  }
+  // the path from u* back to its source (an overloaded expert), in LDS
+  if (tid == 0) {
+    int v = static_cast<int>(s_red[0]);
+    int len = 0;
+    bool ok = true;
+    while (true) {
+      s_path[len++] = static_cast<int16_t>(v);
+      if (s_over[v]) break;
+      v = static_cast<int>(d[v] & 1023);
+      if (len > n) {
+        ok = false;
+        break;
+      }
+    }
+    s_len = ok ? len : -1;
+  }
+  __syncthreads();
+  const int len = s_len;
+  if (len < 0) {
+    if (tid == 0) {
+      c[C_PHASE] = PH_FAILED;
+      c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
+    }
+    clear_edges();
+    return;
+  }
+  // the i-th expert from the source gains i grid units (s_path[len-1] is the
+  // source, s_path[0] = u*); a vertex appears once on a predecessor path
+  if (tid < len) s_pos[s_path[len - 1 - tid]] = static_cast<int16_t>(tid);
+  __syncthreads();
+  // every expert drops by D - min(d, D), then the path shift is added
+  if (tid < n) {
+    const int64_t dv = static_cast<int64_t>(d[tid] >> IDX_BITS);
+    const int64_t nbv = bias[tid] + ((dv < D ? dv : D) - D) + s_pos[tid];
+    bias[tid] = nbv;
+    if (nbv >= BIAS_LIMIT || nbv <= -BIAS_LIMIT) s_bad = 1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    c[C_MOVES] += 1;
+    c[C_DROP] = D;  // no bias fell by more than D
+    c[C_LAST_D] = D;
+    c[C_LAST_HOPS] = len - 1;
+    c[C_BF_PASSES] += passes;
+    if (s_bad) {
+      c[C_PHASE] = PH_FAILED;
+      c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
+    }
+  }
+  clear_edges();
+}
+
+// ---------------------------------------------------------------------------
+// Status (one block of 1024 threads): commit the quantile round of the
+// previous step, take the accumulated loads (clearing the accumulators),
+// decide the next phase exactly as the schedule prescribes (rounds until the
+// unbalanced count stalls, then augmenting paths, then done) and, in the
+// augmenting-path phase, make this step's move.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void status_pass(Args a) {
-  __shared__ int32_t s_imb[1024], s_res[1024];
+  __shared__ int32_t s_imb[16], s_res[16];
+  __shared__ int s_move;
   const int n = a.n;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int imb = 0, res = 0;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    const int32_t L = a.acc[e];
-    a.acc[e] = 0;
+    int32_t part[ACC_COPIES];
+#pragma unroll
+    for (int r = 0; r < ACC_COPIES; ++r) part[r] = a.acc[r * n + e];
+    int32_t L = 0;
+#pragma unroll
+    for (int r = 0; r < ACC_COPIES; ++r) {
+      L += part[r];
+      a.acc[r * n + e] = 0;
+    }
     a.loads[e] = L;
     const int64_t d = static_cast<int64_t>(L) - target(a.T, n, a.k, e);
     imb += d != 0;
     const int ad = static_cast<int>(d < 0 ? -d : d);
     res = res > ad ? res : ad;
   }
-  s_imb[threadIdx.x] = imb;
-  s_res[threadIdx.x] = res;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    imb += __shfl_xor(imb, off);
+    res = max(res, __shfl_xor(res, off));
+  }
+  if (lane == 0) {
+    s_imb[wid] = imb;
+    s_res[wid] = res;
+  }
   __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
-      s_imb[threadIdx.x] += s_imb[threadIdx.x + s];
-      s_res[threadIdx.x] = max(s_res[threadIdx.x], s_res[threadIdx.x + s]);
+  if (threadIdx.x == 0) {
+    imb = 0;
+    res = 0;
+    for (int w = 0; w < 16; ++w) {
+      imb += s_imb[w];
+      res = max(res, s_res[w]);
     }
-    __syncthreads();
+    int64_t* c = a.ctrl;
+    if (c[C_ROUND] != 0) {  // the previous step's quantile round becomes live
+      c[C_ROUND] = 0;
+      c[C_CUR] ^= 1;
+      c[C_ROUNDS] += 1;
+      if (a.cnt[N_BIASRANGE]) {
+        c[C_PHASE] = PH_FAILED;
+        c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
+      }
+    }
+    c[C_IMB] = imb;
+    c[C_RESID] = res;
+    c[C_PIVOT] = 1;  // th[].k1 now holds this pass's keys; biases unchanged so far
+    c[C_DROP] = 0;
+    const int64_t ph = c[C_PHASE];
+    if (ph == PH_ROUNDS) {
+      bool round = false;
+      if (imb == 0) {
+        c[C_PHASE] = PH_DONE;
+      } else if (c[C_ROUNDS] >= c[C_MAX_ROUNDS]) {
+        c[C_PHASE] = PH_SAP;
+      } else if (c[C_BEST] < 0 || imb < c[C_BEST]) {
+        c[C_BEST] = imb;
+        c[C_SINCE] = 0;
+        round = true;
+      } else if (++c[C_SINCE] >= STALL_ROUNDS) {
+        c[C_PHASE] = PH_SAP;
+      } else {
+        round = true;
+      }
+      c[C_ROUND] = round ? 1 : 0;  // the quantile kernel runs; the next status commits it
+    } else if (ph == PH_SAP) {
+      if (imb == 0) {
+        c[C_PHASE] = PH_DONE;
+      } else if (c[C_MOVES] >= MAX_SAP_MOVES) {
+        c[C_PHASE] = PH_FAILED;
+        c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
+      }
+    }
+    s_move = c[C_PHASE] == PH_SAP && c[C_EDGES_VALID] != 0;
   }
-  if (threadIdx.x != 0) return;
-  int64_t* c = a.ctrl;
-  imb = s_imb[0];
-  c[C_IMB] = imb;
-  c[C_RESID] = s_res[0];
-  c[C_PIVOT] = 1;  // th_k1 now holds this pass's keys; biases unchanged so far
-  c[C_DROP] = 0;
-  const int64_t ph = c[C_PHASE];
-  if (ph == PH_ROUNDS) {
-    bool round = false;
-    if (imb == 0) {
-      c[C_PHASE] = PH_DONE;
-    } else if (c[C_ROUNDS] >= c[C_MAX_ROUNDS]) {
-      c[C_PHASE] = PH_SAP;
-    } else if (c[C_BEST] < 0 || imb < c[C_BEST]) {
-      c[C_BEST] = imb;
-      c[C_SINCE] = 0;
-      round = true;
-    } else if (++c[C_SINCE] >= STALL_ROUNDS) {
-      c[C_PHASE] = PH_SAP;
-    } else {
-      round = true;
-    }
-    c[C_ROUND] = round ? 1 : 0;  // the quantile kernel runs, the finish kernel commits
-  } else if (ph == PH_SAP) {
-    if (imb == 0) {
-      c[C_PHASE] = PH_DONE;
-    } else if (c[C_MOVES] >= MAX_SAP_MOVES) {
-      c[C_PHASE] = PH_FAILED;
-      c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
-    }
-  }
+  __syncthreads();
+  if (s_move) sap_move(a);
 }
 
 // ---------------------------------------------------------------------------
 // One quantile round (one block per expert, reading the transposed scores so
 // the column is contiguous): an unbalanced expert finds the C-th and
 // (C+1)-th largest margins over all tokens exactly and jumps to minus their
-// midpoint.  New biases go to the idle bias buffer; the finish kernel makes
-// them live.
+// midpoint.  New biases go to the idle bias buffer, which the next step
+// reads as live.
 //
 // Selection: one pass bins d = margin - cut (the cut is -1024*bias; d > 0 iff
 // the token currently picks the expert) into 2048 order-preserving buckets
@@ -470,20 +733,25 @@ __global__ __launch_bounds__(1024) void status_pass(Args a) {
 // buckets into LDS and the ranks are resolved by exact counting.  A bucket
 // too large for LDS falls back to an MSB-first radix select.
 // ---------------------------------------------------------------------------
-constexpr int SEL_BLOCK = 256;
-constexpr int QREG = 16;  // margins kept in registers per thread (T <= 4096)
+constexpr int SEL_BLOCK = 1024;
+constexpr int SEL_WAVES = SEL_BLOCK / 64;
+constexpr int QREG = 16;  // margins held in registers per thread: one memory pass for T <= 16384
 constexpr int NBUCKET = 2048;
 constexpr int GATHER_CAP = 4096;
 constexpr int DIG = 10;
 constexpr int NBIN = 1 << DIG;
 
+// Margin of token t for expert e: its key without the bias minus the key the
+// expert has to beat (the k-th key when e is not chosen, the (k+1)-th when it is).
+__device__ __forceinline__ int64_t margin_from(float s, KeyPair th, int64_t be, int e) {
+  const int64_t sfx = score_fixed(s);
+  const uint64_t key = pack_key(sfx, be, e);
+  const bool sel = static_cast<int64_t>(key) >= th.k;
+  return static_cast<int64_t>(pack_key(sfx, 0, e)) - (sel ? th.k1 : th.k);
+}
+
 __device__ __forceinline__ int64_t margin_of(const Args& a, const int64_t* bias, int e, int t) {
-  const int64_t sfx = score_fixed(a.scoresT[static_cast<size_t>(e) * a.T + t]);
-  const uint64_t key = pack_key(sfx, bias[e], e);
-  const int64_t thk = a.th_k[t];
-  const bool sel = static_cast<int64_t>(key) >= thk;
-  const int64_t base = static_cast<int64_t>(pack_key(sfx, 0, e));
-  return base - (sel ? a.th_k1[t] : thk);
+  return margin_from(a.scoresT[static_cast<size_t>(e) * a.T + t], a.th[t], bias[e], e);
 }
 
 __device__ __forceinline__ int log_code(uint64_t x) {
@@ -563,25 +831,39 @@ __global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
   }
   __shared__ int32_t hist[NBUCKET];
   __shared__ int64_t gat[GATHER_CAP];
-  __shared__ int32_t scan[SEL_BLOCK];
+  __shared__ int32_t wsum[SEL_WAVES];
   __shared__ int s_bucket[2];
   __shared__ int64_t s_above[2];
   __shared__ int s_cnt;
   __shared__ int64_t s_val[2];
   const int tid = threadIdx.x;
-  const int64_t cut = -bias[e] * 1024;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int64_t be = bias[e];
+  const int64_t cut = -be * 1024;
 
   for (int i = tid; i < NBUCKET; i += SEL_BLOCK) hist[i] = 0;
   if (tid == 0) s_cnt = 0;
-  __syncthreads();
-  // the first QREG margins of each thread stay in registers for the gather
-  int64_t mreg[QREG];
+  // every operand of this thread's first QREG tokens is requested before
+  // any is used, so the loads overlap instead of forming a chain
+  const float* col = a.scoresT + static_cast<size_t>(e) * T;
+  float sv[QREG];
+  KeyPair thv[QREG];
 #pragma unroll
   for (int i = 0; i < QREG; ++i) {
     const int t = tid + i * SEL_BLOCK;
-    mreg[i] = t < T ? margin_of(a, bias, e, t) : 0;
-    if (t < T) atomicAdd(&hist[bucket_of(mreg[i] - cut)], 1);
+    if (t < T) {
+      sv[i] = col[t];
+      thv[i] = a.th[t];
+    }
   }
+  int64_t mreg[QREG];
+#pragma unroll
+  for (int i = 0; i < QREG; ++i)
+    mreg[i] = tid + i * SEL_BLOCK < T ? margin_from(sv[i], thv[i], be, e) : 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < QREG; ++i)
+    if (tid + i * SEL_BLOCK < T) atomicAdd(&hist[bucket_of(mreg[i] - cut)], 1);
   for (int t = tid + QREG * SEL_BLOCK; t < T; t += SEL_BLOCK)
     atomicAdd(&hist[bucket_of(margin_of(a, bias, e, t) - cut)], 1);
   __syncthreads();
@@ -590,24 +872,36 @@ __global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
   int64_t r1 = C, r2 = C + 1;
   if (C == 0) r1 = r2 = 1;
   if (C == T) r1 = r2 = T;
-  // thread i owns buckets [2048 - 8(i+1), 2048 - 8i): counts in descending order
+  // thread i owns the PER buckets below 2048 - PER*i: counts in descending
+  // order; inclusive block scan = shuffle scan in the wave + wave offsets
   constexpr int PER = NBUCKET / SEL_BLOCK;
   int32_t own = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) own += hist[NBUCKET - 1 - (tid * PER + j)];
-  scan[tid] = own;
-  __syncthreads();
-  for (int off = 1; off < SEL_BLOCK; off <<= 1) {
-    const int32_t v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  int32_t incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
   }
-  const int64_t before = scan[tid] - own;  // values in buckets above this thread's chunk
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  if (tid < 64) {
+    int32_t w = tid < SEL_WAVES ? wsum[tid] : 0;
+#pragma unroll
+    for (int off = 1; off < SEL_WAVES; off <<= 1) {
+      const int32_t u = __shfl_up(w, off);
+      if (lane >= off) w += u;
+    }
+    if (tid < SEL_WAVES) wsum[tid] = w;
+  }
+  __syncthreads();
+  if (wid > 0) incl += wsum[wid - 1];
+  const int64_t before = incl - own;  // values in buckets above this thread's chunk
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int64_t r = q == 0 ? r1 : r2;
-    if (before < r && r <= scan[tid]) {
+    if (before < r && r <= incl) {
       int64_t acc = before;
       for (int j = 0; j < PER; ++j) {
         const int b = NBUCKET - 1 - (tid * PER + j);
@@ -668,203 +962,6 @@ __global__ __launch_bounds__(SEL_BLOCK) void quantile_round(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Finish a step (one block of 1024 threads): make a quantile round's biases
-// live, or make one augmenting-path move on this step's sparse edge list.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void finish_step(Args a) {
-  int64_t* c = a.ctrl;
-  const int n = a.n;
-  const int tid = threadIdx.x;
-  __shared__ uint64_t d[1024];
-  __shared__ int64_t s_red[1024];
-  __shared__ int s_flag;
-  __shared__ int16_t s_path[1032];
-  __shared__ int s_len;
-  // 16384 cached edges (128 KB) + the state above and below: about 150 KB
-  constexpr int EDGE_CACHE = 16384;
-  __shared__ uint64_t s_edges[EDGE_CACHE];
-
-  const int64_t ph = c[C_PHASE];
-  if (ph == PH_ROUNDS) {
-    if (c[C_ROUND] == 0) return;
-    // commit the round: largest bias decrease for the next top-k pivot
-    const int cur = static_cast<int>(c[C_CUR] & 1);
-    const int64_t* ob = a.bfx + cur * n;
-    const int64_t* nb = a.bfx + (cur ^ 1) * n;
-    int64_t dmax = 0;
-    for (int e = tid; e < n; e += blockDim.x) dmax = max(dmax, ob[e] - nb[e]);
-    s_red[tid] = dmax;
-    __syncthreads();
-    for (int st = 512; st > 0; st >>= 1) {
-      if (tid < st) s_red[tid] = max(s_red[tid], s_red[tid + st]);
-      __syncthreads();
-    }
-    if (tid == 0) {
-      c[C_ROUND] = 0;
-      c[C_CUR] ^= 1;
-      c[C_ROUNDS] += 1;
-      c[C_DROP] = s_red[0];
-      if (a.cnt[N_BIASRANGE]) {
-        c[C_PHASE] = PH_FAILED;
-        c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
-      }
-    }
-    return;
-  }
-  if (ph != PH_SAP || c[C_EDGES_VALID] == 0) return;
-
-  const int cur = static_cast<int>(c[C_CUR] & 1);
-  int64_t* bias = a.bfx + cur * n;
-  const int64_t delta = c[C_DELTA];
-  const int nedges = a.cnt[N_EDGES];
-  const bool overflow = a.cnt[N_OVERFLOW] != 0 || nedges > a.edge_cap;
-  __syncthreads();
-  if (overflow) {
-    if (tid == 0) {
-      if (delta / 4 < DELTA_MIN) {
-        c[C_PHASE] = PH_FAILED;
-        c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
-      } else {
-        c[C_DELTA] = delta / 4;
-      }
-      c[C_EDGES_VALID] = 0;
-      a.cnt[N_EDGES] = 0;
-      a.cnt[N_OVERFLOW] = 0;
-    }
-    return;
-  }
-  // sources: overloaded experts at distance 0
-  __shared__ uint8_t s_over[1024], s_under[1024];
-  __shared__ int16_t s_pos[1024];
-  __shared__ int s_bad;
-  bool under_e = false;
-  if (tid < n) {
-    const int64_t C = target(a.T, n, a.k, tid);
-    const int32_t L = a.loads[tid];
-    s_over[tid] = L > C;
-    under_e = L < C;
-    s_under[tid] = under_e;
-    s_pos[tid] = 0;
-    d[tid] = L > C ? static_cast<uint64_t>(tid) : PACKED_INF;
-  }
-  const bool cached = nedges <= EDGE_CACHE;
-  if (cached)
-    for (int i = tid; i < nedges; i += blockDim.x) s_edges[i] = a.edges[i];
-  // Relaxation passes.  s_D is the running minimum distance of an
-  // underloaded expert (it only decreases); a pass that lowers some distance
-  // to at most s_D asks for another pass.  Flagging against the running value
-  // flags a superset of "changed at or below the final D*", so the passes
-  // stop only when every distance <= D* and its predecessor is final.
-  __shared__ unsigned long long s_D;
-  if (tid == 0) {
-    s_D = static_cast<unsigned long long>(DIST_INF);
-    s_bad = 0;
-  }
-  __syncthreads();
-  if (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) < DIST_INF)
-    atomicMin(&s_D, static_cast<unsigned long long>(d[tid] >> IDX_BITS));
-  int passes = 0;
-  while (true) {
-    if (tid == 0) s_flag = 0;
-    __syncthreads();
-    for (int i = tid; i < nedges; i += blockDim.x) {
-      const uint64_t ed = cached ? s_edges[i] : a.edges[i];
-      const int B = static_cast<int>(ed & 1023);
-      const int A = static_cast<int>((ed >> 10) & 1023);
-      const int64_t rho = static_cast<int64_t>(ed >> 20);
-      const int64_t dA = static_cast<int64_t>(d[A] >> IDX_BITS);
-      if (dA >= DIST_INF) continue;
-      const int64_t cand = dA + rho;
-      if (cand >= DIST_INF) continue;
-      const uint64_t pk = (static_cast<uint64_t>(cand) << IDX_BITS) | static_cast<uint64_t>(A);
-      if (pk < d[B]) {
-        const uint64_t old = atomicMin(reinterpret_cast<unsigned long long*>(&d[B]), pk);
-        if (pk < old) {
-          if (s_under[B]) atomicMin(&s_D, static_cast<unsigned long long>(cand));
-          if (static_cast<uint64_t>(cand) <= s_D) s_flag = 1;
-        }
-      }
-    }
-    __syncthreads();
-    ++passes;
-    const int go = s_flag;
-    __syncthreads();
-    if (!go || passes > 4 * 1024) break;
-  }
-  const int64_t D = static_cast<int64_t>(s_D);
-  if (D >= DIST_INF || D > delta) {
-    if (tid == 0) {
-      if (delta >= DELTA_MAX) {
-        c[C_PHASE] = PH_FAILED;
-        c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
-      } else {
-        c[C_DELTA] = delta * 16;
-      }
-      c[C_EDGES_VALID] = 0;
-      a.cnt[N_EDGES] = 0;
-    }
-    return;
-  }
-  // u* = lowest underloaded expert at distance D
-  s_red[tid] = (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) == D) ? tid : 1 << 30;
-  __syncthreads();
-  for (int st = 512; st > 0; st >>= 1) {
-    if (tid < st) s_red[tid] = min(s_red[tid], s_red[tid + st]);
-    __syncthreads();
-  }
-  // the path from u* back to its source (an overloaded expert), in LDS
-  if (tid == 0) {
-    int v = static_cast<int>(s_red[0]);
-    int len = 0;
-    bool ok = true;
-    while (true) {
-      s_path[len++] = static_cast<int16_t>(v);
-      if (s_over[v]) break;
-      v = static_cast<int>(d[v] & 1023);
-      if (len > n) {
-        ok = false;
-        break;
-      }
-    }
-    s_len = ok ? len : -1;
-  }
-  __syncthreads();
-  const int len = s_len;
-  if (len < 0) {
-    if (tid == 0) {
-      c[C_PHASE] = PH_FAILED;
-      c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
-    }
-    return;
-  }
-  // the i-th expert from the source gains i grid units (s_path[len-1] is the
-  // source, s_path[0] = u*); a vertex appears once on a predecessor path
-  if (tid < len) s_pos[s_path[len - 1 - tid]] = static_cast<int16_t>(tid);
-  __syncthreads();
-  // every expert drops by D - min(d, D), then the path shift is added
-  if (tid < n) {
-    const int64_t dv = static_cast<int64_t>(d[tid] >> IDX_BITS);
-    const int64_t nbv = bias[tid] + ((dv < D ? dv : D) - D) + s_pos[tid];
-    bias[tid] = nbv;
-    if (nbv >= BIAS_LIMIT || nbv <= -BIAS_LIMIT) s_bad = 1;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    c[C_MOVES] += 1;
-    c[C_DROP] = D;  // no bias fell by more than D
-    c[C_LAST_D] = D;
-    c[C_LAST_HOPS] = len - 1;
-    c[C_BF_PASSES] += passes;
-    if (s_bad) {
-      c[C_PHASE] = PH_FAILED;
-      c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
-    }
-    c[C_EDGES_VALID] = 0;
-    a.cnt[N_EDGES] = 0;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Small helpers: init, transposition, centring, bias conversion.
 // ---------------------------------------------------------------------------
 __global__ void init_ctrl(Args a, const double* bias_in, int mode, int max_rounds) {
@@ -880,8 +977,8 @@ __global__ void init_ctrl(Args a, const double* bias_in, int mode, int max_round
     }
     a.bfx[e] = v;
     a.bfx[n + e] = v;
-    a.acc[e] = 0;
   }
+  for (int i = threadIdx.x; i < ACC_COPIES * n; i += blockDim.x) a.acc[i] = 0;
   if (threadIdx.x == 0) {
     int64_t* c = a.ctrl;
     for (int i = 0; i < C_COUNT; ++i) c[i] = 0;
@@ -925,9 +1022,18 @@ __global__ void center_and_export(Args a, double* bias_out, int32_t* info) {
   __shared__ long long s[1024];
   const int n = a.n;
   int64_t* c = a.ctrl;
-  const int cur = static_cast<int>(c[C_CUR] & 1);
+  // a quantile round left uncommitted when the host's step cap ended the loop
+  const bool pending = c[C_PHASE] == PH_ROUNDS && c[C_ROUND] != 0;
+  const int cur = static_cast<int>(c[C_CUR] & 1) ^ (pending ? 1 : 0);
   int64_t* bias = a.bfx + cur * n;
   const bool balanced = c[C_PHASE] == PH_DONE;
+  __syncthreads();
+  if (pending && threadIdx.x == 0) {
+    c[C_ROUND] = 0;
+    c[C_CUR] = cur;
+    c[C_ROUNDS] += 1;
+    if (a.cnt[N_BIASRANGE]) c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
+  }
   long long acc = 0;
   for (int e = threadIdx.x; e < n; e += blockDim.x) acc += bias[e];
   s[threadIdx.x] = acc;
@@ -978,10 +1084,9 @@ size_t route_workspace_layout(int32_t T, int32_t n, RouteWorkspace* ws, void* ba
   RouteWorkspace w;
   w.scoresT = cv.take<float>(static_cast<size_t>(T) * n);
   w.bfx = cv.take<int64_t>(2 * static_cast<size_t>(n));
-  w.th_k = cv.take<int64_t>(T);
-  w.th_k1 = cv.take<int64_t>(T);
+  w.th = cv.take<KeyPair>(T);
   w.loads = cv.take<int32_t>(n);
-  w.acc = cv.take<int32_t>(n);
+  w.acc = cv.take<int32_t>(static_cast<size_t>(qb::ACC_COPIES) * n);
   w.ctrl = cv.take<int64_t>(qb::C_COUNT);
   w.cnt = cv.take<int32_t>(qb::N_COUNT);
   w.edge_cap = edge_capacity(T);
@@ -1038,8 +1143,7 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
   a.n = n;
   a.k = k;
   a.bfx = ws.bfx;
-  a.th_k = ws.th_k;
-  a.th_k1 = ws.th_k1;
+  a.th = ws.th;
   a.loads = ws.loads;
   a.acc = ws.acc;
   a.ctrl = ws.ctrl;
@@ -1048,7 +1152,7 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
   a.edge_cap = ws.edge_cap;
   a.idx = idx;
   a.w = w;
-  const int grid = T > 0 ? (T + 3) / 4 : 1;  // one token per wave
+  const int grid = T > 0 ? std::min((T + 3) / 4, TOPK_MAX_GRID) : 1;  // 4 waves per block
   if (max_rounds <= 0) max_rounds = 64;
   const size_t smem = topk_smem_bytes();
 
@@ -1079,7 +1183,6 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
         hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 0);
         hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), 0, stream, a);
         hipLaunchKernelGGL(quantile_round, dim3(n), dim3(SEL_BLOCK), 0, stream, a);
-        hipLaunchKernelGGL(finish_step, dim3(1), dim3(1024), 0, stream, a);
       }
       MOE_LAUNCH_CHECK();
       MOE_HIP_CHECK(hipMemcpyAsync(ps->word + 8 * slot, ws.ctrl + C_PHASE, sizeof(int64_t),

@@ -5,14 +5,19 @@
 
 namespace moe {
 
+// A token's k-th and (k+1)-th largest packed keys, read together as one
+// 16-byte load.
+struct alignas(16) KeyPair {
+  int64_t k, k1;
+};
+
 // Device scratch of the routing driver, carved from the caller's workspace.
 struct RouteWorkspace {
   float* scoresT;       // [n][T] transposed scores (per-expert margin passes)
   int64_t* bfx;         // [2][n] fixed-point biases (live half chosen on the device)
-  int64_t* th_k;        // [T] k-th largest key per token
-  int64_t* th_k1;       // [T] (k+1)-th largest key per token
+  KeyPair* th;          // [T] k-th and (k+1)-th largest keys per token
   int32_t* loads;       // [n]
-  int32_t* acc;         // [n] load accumulator of the top-k pass (cleared by the status pass)
+  int32_t* acc;         // [copies][n] load accumulators of the top-k pass (cleared by the status pass)
   int64_t* ctrl;        // control words (phase, counters)
   int32_t* cnt;         // edge count and error flags
   uint64_t* edges;      // sparse edge list of the augmenting-path phase
