@@ -26,12 +26,12 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 # HBM bytes per launch of the routed gate/up kernel, from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE runs scaled by a 1 GiB device copy (profiles/
-# routed_gate_up_hbm_traffic.txt); None where not measured for the current
+# routed_gemm_hbm_traffic.txt); None where not measured for the current
 # kernel.
-TRAFFIC = {"k3_prefill": 27.020e9,   # gemm_pipe<96, 256, 1, SITU, 64, 3, nt>
-           "k3_decode": 26.313e9,    # gemm_pipe<32, 256, 1, SITU, 64, 3, nt>
-           "k3_mxfp4": None,         # kernel changed since measured
-           "k3_prefill_16k": None}
+TRAFFIC = {"k3_prefill": 27.017e9,      # gemm_pipe<96, 256, 1, SITU, 64, 3, nt>
+           "k3_decode": 26.313e9,       # gemm_pipe<32, 256, 1, SITU, 64, 3, nt>
+           "k3_mxfp4": 9.942e9,         # gemm_pipe_fp4<160, 256, 1, SITU>
+           "k3_prefill_16k": 31.371e9}  # gemm_pipe<160, 256, 1, SITU, 64, 3>
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
 
 
