@@ -16,6 +16,8 @@
 // The epilogue goes through LDS so that stores are row-contiguous.
 #include "gemm.hpp"
 
+#include <atomic>
+
 namespace moe {
 namespace gemm {
 
@@ -1086,7 +1088,7 @@ static int run_bf16(const Params& p, hipStream_t stream) {
 }
 
 template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT>
-static int run_pipe(const Params& p, hipStream_t stream) {
+static int run_pipe(const Params& p, hipStream_t stream, size_t pad_lds = 0) {
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   for (int s = 0; s < p.nseg; ++s)
     if (p.seg[s].K % BKP != 0) return MOE_EUNSUPPORTED;
@@ -1095,9 +1097,31 @@ static int run_pipe(const Params& p, hipStream_t stream) {
   const int64_t G = static_cast<int64_t>(mt) * ntn * (p.ksplit > 1 ? p.ksplit : 1);
   if (G <= 0) return MOE_OK;
   const int64_t G8 = (G + 7) / 8 * 8;
+  if (pad_lds > 0) {  // unused dynamic LDS that caps the blocks per CU
+    static std::atomic<bool> configured{false};
+    if (!configured.load(std::memory_order_relaxed)) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(pad_lds)) != hipSuccess)
+        return MOE_EHIP;
+      configured.store(true, std::memory_order_relaxed);
+    }
+  }
   hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT>), dim3(static_cast<unsigned>(G8)),
-                     dim3(NTHREADS), 0, stream, p);
+                     dim3(NTHREADS), pad_lds, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// 128 x 128 tiles (48 KB of LDS, about 130 registers per lane) padded to 88 KB
+// of LDS: one block per CU, the rest of the CU left to kernels on other streams.
+static int run_shared_tiles(const Params& p, int epi, hipStream_t s) {
+  constexpr size_t PAD = 40 * 1024;
+  switch (epi) {
+    case EPI_BF16: return run_pipe<128, 128, 2, EPI_BF16, 32, 3, false>(p, s, PAD);
+    case EPI_F32: return run_pipe<128, 128, 2, EPI_F32, 32, 3, false>(p, s, PAD);
+    case EPI_SITU: return run_pipe<128, 128, 2, EPI_SITU, 32, 3, false>(p, s, PAD);
+    default: return MOE_EUNSUPPORTED;
+  }
 }
 
 // Ring depth: 3 stages (a fourth measured no faster on the weight-streaming
@@ -1220,6 +1244,11 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
     if (bm_hint == 160) return dispatch_pipe<160, 256, 1, 64>(q, epi, stream);
     if (bm_hint == 256) return dispatch_pipe<256, 256, 2, 32>(q, epi, stream);
     return dispatch_pipe<128, 128, 2, 32>(q, epi, stream);
+  }
+  if (bfmt == B_DENSE && bm_hint == BM_SHARE && p.M >= 256) {
+    Params q = p;
+    q.ksplit = 1;
+    return run_shared_tiles(q, epi, stream);
   }
   if (bfmt == B_DENSE) {
     int K = 0;

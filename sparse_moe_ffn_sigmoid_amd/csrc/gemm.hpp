@@ -57,6 +57,11 @@ size_t splitk_bytes(int M, int N, int K, int epi);
 // Whether the pipelined MXFP4 kernel takes 160-row tiles for this K.
 size_t fp4_tall_tile_fits(int K);
 
+// bm_hint of a dense product that runs on another stream beside the
+// latency-bound routing kernels: 128 x 128 tiles held to one block per CU, so
+// that those kernels' blocks find registers and LDS on every CU.
+constexpr int BM_SHARE = -1;
+
 // Launch helpers (defined in gemm.hip).  `act_bf16` selects the bf16 MFMA
 // kernels, otherwise the fp32 kernels run.
 int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipStream_t stream);

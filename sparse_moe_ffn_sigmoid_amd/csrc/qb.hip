@@ -438,7 +438,7 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
 // then every expert drops by D - min(d, D) and the path to the nearest
 // underloaded expert is shifted by one grid unit per hop.
 // ---------------------------------------------------------------------------
-__device__ void sap_move(const Args& a) {
+__device__ void sap_move(const Args& a, int edge_cache) {
   int64_t* c = a.ctrl;
   const int n = a.n;
   const int tid = threadIdx.x;
@@ -447,9 +447,8 @@ __device__ void sap_move(const Args& a) {
   __shared__ int s_flag;
   __shared__ int16_t s_path[1032];
   __shared__ int s_len;
-  // 16384 cached edges (128 KB) + the state above and below: about 150 KB
-  constexpr int EDGE_CACHE = 16384;
-  __shared__ uint64_t s_edges[EDGE_CACHE];
+  // edge cache: the status kernel's dynamic LDS (edge_cache entries, 0 = none)
+  extern __shared__ uint64_t s_edges[];
   __shared__ int s_seg_off[EDGE_SEGS + 1];
 
 
@@ -501,7 +500,7 @@ __device__ void sap_move(const Args& a) {
     s_pos[tid] = 0;
     d[tid] = L > C ? static_cast<uint64_t>(tid) : PACKED_INF;
   }
-  const bool cached = nedges <= EDGE_CACHE;
+  const bool cached = nedges <= edge_cache;
   if (cached)
     for (int sg = 0; sg < EDGE_SEGS; ++sg) {
       const int off = s_seg_off[sg], m = s_seg_off[sg + 1] - off;
@@ -635,21 +634,23 @@ __device__ void sap_move(const Args& a) {
 // unbalanced count stalls, then augmenting paths, then done) and, in the
 // augmenting-path phase, make this step's move.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void status_pass(Args a) {
+__global__ __launch_bounds__(1024) void status_pass(Args a, int edge_cache) {
   __shared__ int32_t s_imb[16], s_res[16];
   __shared__ int s_move;
   const int n = a.n;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int imb = 0, res = 0;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    int32_t part[ACC_COPIES];
-#pragma unroll
-    for (int r = 0; r < ACC_COPIES; ++r) part[r] = a.acc[r * n + e];
     int32_t L = 0;
+    for (int r0 = 0; r0 < ACC_COPIES; r0 += 8) {
+      int32_t part[8];
 #pragma unroll
-    for (int r = 0; r < ACC_COPIES; ++r) {
-      L += part[r];
-      a.acc[r * n + e] = 0;
+      for (int r = 0; r < 8; ++r) part[r] = a.acc[(r0 + r) * n + e];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        L += part[r];
+        a.acc[(r0 + r) * n + e] = 0;
+      }
     }
     a.loads[e] = L;
     const int64_t d = static_cast<int64_t>(L) - target(a.T, n, a.k, e);
@@ -716,7 +717,7 @@ __global__ __launch_bounds__(1024) void status_pass(Args a) {
     s_move = c[C_PHASE] == PH_SAP && c[C_EDGES_VALID] != 0;
   }
   __syncthreads();
-  if (s_move) sap_move(a);
+  if (s_move) sap_move(a, edge_cache);
 }
 
 // ---------------------------------------------------------------------------
@@ -1104,6 +1105,11 @@ struct PollState {
   bool ok = false;
 };
 
+// Edges the status kernel caches in dynamic LDS once the host has seen the
+// augmenting-path phase (128 KB); before that it runs with a small LDS
+// footprint, so that its block can be resident beside other kernels' blocks.
+constexpr int SAP_EDGE_CACHE = 16384;
+
 static PollState* poll_state() {
   constexpr int MAX_DEVICES = 64;
   thread_local PollState st[MAX_DEVICES];
@@ -1111,6 +1117,10 @@ static PollState* poll_state() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
   PollState& p = st[dev];
   if (!p.ok) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(qb::status_pass),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            SAP_EDGE_CACHE * static_cast<int>(sizeof(uint64_t))) != hipSuccess)
+      return nullptr;
     if (!p.word) {
       void* w = nullptr;
       if (hipHostMalloc(&w, 128, hipHostMallocDefault) != hipSuccess) return nullptr;
@@ -1177,11 +1187,14 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
     PollState* ps = poll_state();
     if (!ps) return MOE_EHIP;
     int steps = 0, launched = 0;
+    bool sap_seen = false;  // edge cache from the first batch after the phase was seen
     while (true) {
       const int slot = launched & 1;
+      const int cache = sap_seen ? SAP_EDGE_CACHE : 0;
       for (int i = 0; i < batch; ++i) {
         hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 0);
-        hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), 0, stream, a);
+        hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), cache * sizeof(uint64_t), stream, a,
+                           cache);
         hipLaunchKernelGGL(quantile_round, dim3(n), dim3(SEL_BLOCK), 0, stream, a);
       }
       MOE_LAUNCH_CHECK();
@@ -1195,6 +1208,7 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
         MOE_HIP_CHECK(hipEventSynchronize(ps->ev[prev]));
         const int64_t phase = ps->word[8 * prev];
         if (phase == PH_DONE || phase == PH_FAILED) break;
+        if (phase == PH_SAP) sap_seen = true;
       }
       if (steps >= max_steps) break;
     }
@@ -1203,7 +1217,7 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
   hipLaunchKernelGGL(center_and_export, dim3(1), dim3(1024), 0, stream, a,
                      mode == MOE_QB_BATCH ? bias : nullptr, info);
   hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 1);
-  hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), 0, stream, a, 0);
   hipLaunchKernelGGL(export_resid, dim3(1), dim3(64), 0, stream, a, info);
   if (loads_out)
     MOE_HIP_CHECK(hipMemcpyAsync(loads_out, ws.loads, sizeof(int32_t) * n,
