@@ -144,14 +144,27 @@ __global__ __launch_bounds__(256) void combine_rmsnorm(const float* __restrict__
   float acc[MAXV];
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[static_cast<int64_t>(t) * k + j];
-    const float* src = yp + static_cast<int64_t>(inv[static_cast<int64_t>(t) * k + j]) * L;
+  // four slot rows per round trip: their loads are all in flight together
+  constexpr int RB = 4;
+  for (int j0 = 0; j0 < k; j0 += RB) {
+    float v[RB][MAXV];
+    float wj[RB];
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      if (c < L) acc[i] = fmaf(wj, src[c], acc[i]);
+    for (int q = 0; q < RB; ++q) {
+      const int j = j0 + q;
+      wj[q] = j < k ? w[static_cast<int64_t>(t) * k + j] : 0.f;
+      const float* src =
+          j < k ? yp + static_cast<int64_t>(inv[static_cast<int64_t>(t) * k + j]) * L : nullptr;
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        v[q][i] = (src && c < L) ? src[c] : 0.f;
+      }
     }
+#pragma unroll
+    for (int q = 0; q < RB; ++q)
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) acc[i] = fmaf(wj[q], v[q][i], acc[i]);
   }
   float ss = 0.f;
 #pragma unroll

@@ -1195,7 +1195,8 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
         hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 0);
         hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), cache * sizeof(uint64_t), stream, a,
                            cache);
-        hipLaunchKernelGGL(quantile_round, dim3(n), dim3(SEL_BLOCK), 0, stream, a);
+        // the augmenting-path phase never returns to quantile rounds
+        if (!sap_seen) hipLaunchKernelGGL(quantile_round, dim3(n), dim3(SEL_BLOCK), 0, stream, a);
       }
       MOE_LAUNCH_CHECK();
       MOE_HIP_CHECK(hipMemcpyAsync(ps->word + 8 * slot, ws.ctrl + C_PHASE, sizeof(int64_t),
