@@ -245,41 +245,64 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
     if (t + stride < T) load_scores(t + stride);
     uint64_t thk = 0, thk1 = 0;
     bool found = false;
-    if (use_pivot) {
-      const uint64_t P = prev > drop_key ? prev - drop_key : 1;
+    // Exact k-th and (k+1)-th keys from a pivot P with k+1 <= #{keys >= P}
+    // <= 64: the keys >= P are compacted into LDS and ranked.
+    auto try_pivot = [&](uint64_t P) -> bool {
       int c = 0;
 #pragma unroll
       for (int j = 0; j < MAX_NJ; ++j) c += __popcll(__ballot(key[j] >= P));
-      if (c >= k + 1 && c <= 64) {
-        int base = 0;
+      if (c < k + 1 || c > 64) return false;
+      int base = 0;
 #pragma unroll
-        for (int j = 0; j < MAX_NJ; ++j) {
-          const bool in = key[j] >= P;
-          const uint64_t bal = __ballot(in);
-          if (in) cand[wv * 64 + base + __popcll(bal & ((uint64_t(1) << lane) - 1))] = key[j];
-          base += __popcll(bal);
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        if (lane < c) {
-          const uint64_t v = cand[wv * 64 + lane];
-          const uint64_t* cw = cand + wv * 64;
-          int rank = 0, i = 0;
-          for (; i + 8 <= c; i += 8) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) rank += cw[i + q] > v;
-          }
-          for (; i < c; ++i) rank += cw[i] > v;
-          if (rank == k - 1) thv[wv * 2] = v;
-          if (rank == k) thv[wv * 2 + 1] = v;
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        thk = thv[wv * 2];
-        thk1 = thv[wv * 2 + 1];
-        __builtin_amdgcn_wave_barrier();
-        found = true;
+      for (int j = 0; j < MAX_NJ; ++j) {
+        const bool in = key[j] >= P;
+        const uint64_t bal = __ballot(in);
+        if (in) cand[wv * 64 + base + __popcll(bal & ((uint64_t(1) << lane) - 1))] = key[j];
+        base += __popcll(bal);
       }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      if (lane < c) {
+        const uint64_t v = cand[wv * 64 + lane];
+        const uint64_t* cw = cand + wv * 64;
+        int rank = 0, i = 0;
+        for (; i + 8 <= c; i += 8) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) rank += cw[i + q] > v;
+        }
+        for (; i < c; ++i) rank += cw[i] > v;
+        if (rank == k - 1) thv[wv * 2] = v;
+        if (rank == k) thv[wv * 2 + 1] = v;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      thk = thv[wv * 2];
+      thk1 = thv[wv * 2 + 1];
+      __builtin_amdgcn_wave_barrier();
+      return true;
+    };
+    if (use_pivot) found = try_pivot(prev > drop_key ? prev - drop_key : 1);
+    if (!found && k < n && k + 1 <= 64) {
+      // Second pivot: the (k+1)-th largest of the 64 lane maxima.  At least
+      // k+1 keys (those maxima) are >= it; usually few more are.
+      uint64_t lm = key[0];
+#pragma unroll
+      for (int j = 1; j < MAX_NJ; ++j) lm = key[j] > lm ? key[j] : lm;
+      if (lane == 0) thv[wv * 2] = 1;  // lanes without keys tie at 0: P = 1 then
+      cand[wv * 64 + lane] = lm;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      int r = 0;
+      const uint64_t* cw = cand + wv * 64;
+#pragma unroll 8
+      for (int q = 0; q < 64; ++q) r += cw[q] > lm;
+      __builtin_amdgcn_wave_barrier();
+      if (r == k && lm != 0) thv[wv * 2] = lm;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      const uint64_t P = thv[wv * 2];
+      __builtin_amdgcn_wave_barrier();
+      found = try_pivot(P);
     }
     if (!found) {
       // k+1 rounds of wave-wide maximum: each lane offers its largest
