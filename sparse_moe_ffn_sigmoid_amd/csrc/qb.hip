@@ -64,7 +64,7 @@ enum Ctrl {
 };
 // The edge list is split into EDGE_SEGS segments with one counter each
 // (chosen by block index), for the same reason as the load counters.
-constexpr int EDGE_SEGS = 32;
+constexpr int EDGE_SEGS = 256;
 enum Cnt { N_OVERFLOW = 1, N_BIASRANGE = 2, N_SEG0 = 8, N_COUNT = N_SEG0 + EDGE_SEGS };
 
 __host__ __device__ __forceinline__ int64_t target(int64_t T, int64_t n, int64_t k, int64_t e) {
@@ -425,22 +425,44 @@ __global__ __launch_bounds__(TOPK_BLOCK) void topk_pass(Args a, int emit_out) {
         if (nlow > EDGE_LIST_MAX || nhigh > EDGE_LIST_MAX) {
           if (lane == 0) atomicOr(&a.cnt[N_OVERFLOW], 1);
         } else {
-          const int P = nlow * nhigh;
-          for (int p = lane; p < P; p += 64) {
-            const int ia = p / nhigh, ib = p - ia * nhigh;
-            const int A = lowE[wv * EDGE_LIST_MAX + ia];
+          // the token's edges: lane ia pairs low candidate ia with every
+          // high one (broadcast LDS reads); counted first, then one atomic
+          // reserves them all
+          const bool has = lane < nlow;
+          const int A = has ? lowE[wv * EDGE_LIST_MAX + lane] : 0;
+          const int64_t kA = has ? lowKp[wv * EDGE_LIST_MAX + lane] : 0;
+          int mine = 0;
+          for (int ib = 0; ib < nhigh; ++ib) {
             const int B = highE[wv * EDGE_LIST_MAX + ib];
-            const int64_t rho =
-                lowKp[wv * EDGE_LIST_MAX + ia] - highKp[wv * EDGE_LIST_MAX + ib] - (A > B ? 1 : 0);
-            if (rho <= delta) {
-              const int slot = atomicAdd(&a.cnt[N_SEG0 + seg], 1);
-              if (slot < seg_cap)
-                a.edges[static_cast<size_t>(seg) * seg_cap + slot] =
-                    (static_cast<uint64_t>(rho) << 20) | (static_cast<uint64_t>(A) << 10) |
-                    static_cast<uint64_t>(B);
-              else
-                atomicOr(&a.cnt[N_OVERFLOW], 1);
+            mine += has && kA - highKp[wv * EDGE_LIST_MAX + ib] - (A > B ? 1 : 0) <= delta;
+          }
+          int incl = mine;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_up(incl, off);
+            if (lane >= off) incl += u;
+          }
+          const int total = __shfl(incl, 63);
+          if (total > 0) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&a.cnt[N_SEG0 + seg], total);
+            base = __shfl(base, 0);
+            int pos = base + incl - mine;
+            bool over = false;
+            for (int ib = 0; ib < nhigh; ++ib) {
+              const int B = highE[wv * EDGE_LIST_MAX + ib];
+              const int64_t rho = kA - highKp[wv * EDGE_LIST_MAX + ib] - (A > B ? 1 : 0);
+              if (has && rho <= delta) {
+                if (pos < seg_cap)
+                  a.edges[static_cast<size_t>(seg) * seg_cap + pos] =
+                      (static_cast<uint64_t>(rho) << 20) | (static_cast<uint64_t>(A) << 10) |
+                      static_cast<uint64_t>(B);
+                else
+                  over = true;
+                ++pos;
+              }
             }
+            if (__ballot(over) != 0 && lane == 0) atomicOr(&a.cnt[N_OVERFLOW], 1);
           }
         }
         __builtin_amdgcn_wave_barrier();
@@ -479,17 +501,41 @@ __device__ void sap_move(const Args& a, int edge_cache) {
   int64_t* bias = a.bfx + cur * n;
   const int64_t delta = c[C_DELTA];
   const int seg_cap = a.edge_cap / EDGE_SEGS;
-  if (tid == 0) {
-    int tot = 0;
-    for (int sg = 0; sg < EDGE_SEGS; ++sg) {
-      s_seg_off[sg] = tot;
-      const int m = a.cnt[N_SEG0 + sg];
-      tot += m < seg_cap ? m : seg_cap;
+  {  // segment offsets: exclusive scan of the (capped) segment counts
+    static_assert(EDGE_SEGS == 256, "scan below: four waves of 64");
+    __shared__ int s_wsum[4];
+    const int lane = tid & 63, wid = tid >> 6;
+    int m = 0;
+    if (tid < EDGE_SEGS) {
+      m = a.cnt[N_SEG0 + tid];
+      m = m < seg_cap ? m : seg_cap;
     }
-    s_seg_off[EDGE_SEGS] = tot;
+    int incl = m;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(incl, off);
+      if (lane >= off) incl += u;
+    }
+    if (tid < EDGE_SEGS && lane == 63) s_wsum[wid] = incl;
+    __syncthreads();
+    if (tid < EDGE_SEGS) {
+      int before = 0;
+      for (int w = 0; w < wid; ++w) before += s_wsum[w];
+      s_seg_off[tid] = before + incl - m;
+      if (tid == EDGE_SEGS - 1) s_seg_off[EDGE_SEGS] = before + incl;
+    }
   }
   const bool overflow = a.cnt[N_OVERFLOW] != 0;
   __syncthreads();
+  // segment of edge i (0 <= i < nedges): the last sg with s_seg_off[sg] <= i
+  auto seg_of = [&](int i) {
+    int lo = 0, hi = EDGE_SEGS - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_seg_off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
   const int nedges = s_seg_off[EDGE_SEGS];
   // every segment counter is cleared by the end of the move
   auto clear_edges = [&]() {
@@ -525,10 +571,9 @@ __device__ void sap_move(const Args& a, int edge_cache) {
   }
   const bool cached = nedges <= edge_cache;
   if (cached)
-    for (int sg = 0; sg < EDGE_SEGS; ++sg) {
-      const int off = s_seg_off[sg], m = s_seg_off[sg + 1] - off;
-      for (int i = tid; i < m; i += blockDim.x)
-        s_edges[off + i] = a.edges[static_cast<size_t>(sg) * seg_cap + i];
+    for (int i = tid; i < nedges; i += blockDim.x) {
+      const int sg = seg_of(i);
+      s_edges[i] = a.edges[static_cast<size_t>(sg) * seg_cap + (i - s_seg_off[sg])];
     }
   // Relaxation passes.  s_D is the running minimum distance of an
   // underloaded expert (it only decreases); a pass that lowers some distance
@@ -552,8 +597,7 @@ __device__ void sap_move(const Args& a, int edge_cache) {
       if (cached) {
         ed = s_edges[i];
       } else {
-        int sg = 0;
-        while (i >= s_seg_off[sg + 1]) ++sg;
+        const int sg = seg_of(i);
         ed = a.edges[static_cast<size_t>(sg) * seg_cap + (i - s_seg_off[sg])];
       }
       const int B = static_cast<int>(ed & 1023);
@@ -1015,7 +1059,7 @@ __global__ void init_ctrl(Args a, const double* bias_in, int mode, int max_round
 }
 
 __global__ void zero_cnt(Args a) {
-  if (threadIdx.x < N_COUNT) a.cnt[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < N_COUNT; i += blockDim.x) a.cnt[i] = 0;
 }
 
 __global__ void check_range(Args a) {
@@ -1101,7 +1145,9 @@ size_t topk_smem_bytes() {
 // Host driver shared by moe_route_qb and moe_latent_forward.
 // ---------------------------------------------------------------------------
 
-static int32_t edge_capacity(int32_t T) { return 16 * T + 65536; }
+// Edge list: 16 per token on average plus, in every segment, room for the
+// largest list one token can emit (64 x 64).
+static int32_t edge_capacity(int32_t T) { return 16 * T + qb::EDGE_SEGS * 4096; }
 
 size_t route_workspace_layout(int32_t T, int32_t n, RouteWorkspace* ws, void* base) {
   Carver cv(base);
