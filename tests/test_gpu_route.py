@@ -59,6 +59,12 @@ CASES = [
     ("mid", 3000, 256, 8, 0.5),
     ("max_n_k", 300, 1024, 64, 0.5),
     ("k3_prefill_shape", 4096, 896, 16, 0.5),
+    # top-k pivots: lanes without keys (n < 64), k + 1 = n, k + 1 = 64,
+    # several tokens per wave (T above three resident blocks per CU x 4)
+    ("pivot_small_n", 500, 48, 20, 0.5),
+    ("pivot_k_n_minus_1", 300, 40, 39, 0.5),
+    ("pivot_k63", 400, 200, 63, 0.5),
+    ("pivot_tokens_per_wave", 7000, 128, 6, 1.0),
 ]
 
 
