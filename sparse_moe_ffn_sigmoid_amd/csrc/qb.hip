@@ -489,7 +489,7 @@ __device__ void sap_move(const Args& a, int edge_cache) {
   const int tid = threadIdx.x;
   __shared__ uint64_t d[1024];
   __shared__ int64_t s_red[1024];
-  __shared__ int s_flag;
+  __shared__ int s_flag[3];  // rotating 'lowered a distance <= D' flags, one per pass
   __shared__ int16_t s_path[1032];
   __shared__ int s_len;
   // edge cache: the status kernel's dynamic LDS (edge_cache entries, 0 = none)
@@ -588,10 +588,15 @@ __device__ void sap_move(const Args& a, int edge_cache) {
   __syncthreads();
   if (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) < DIST_INF)
     atomicMin(&s_D, static_cast<unsigned long long>(d[tid] >> IDX_BITS));
+  // One barrier per pass: pass p raises s_flag[p % 3]; thread 0 clears the
+  // flag of pass p + 1 during pass p (its last readers finished before the
+  // barrier that ended pass p - 1).
+  if (tid < 3) s_flag[tid] = 0;
+  __syncthreads();
   int passes = 0;
   while (true) {
-    if (tid == 0) s_flag = 0;
-    __syncthreads();
+    const int fi = passes % 3;
+    if (tid == 0) s_flag[(passes + 1) % 3] = 0;
     for (int i = tid; i < nedges; i += blockDim.x) {
       uint64_t ed;
       if (cached) {
@@ -612,15 +617,13 @@ __device__ void sap_move(const Args& a, int edge_cache) {
         const uint64_t old = atomicMin(reinterpret_cast<unsigned long long*>(&d[B]), pk);
         if (pk < old) {
           if (s_under[B]) atomicMin(&s_D, static_cast<unsigned long long>(cand));
-          if (static_cast<uint64_t>(cand) <= s_D) s_flag = 1;
+          if (static_cast<uint64_t>(cand) <= s_D) s_flag[fi] = 1;
         }
       }
     }
     __syncthreads();
     ++passes;
-    const int go = s_flag;
-    __syncthreads();
-    if (!go || passes > 4 * 1024) break;
+    if (!s_flag[fi] || passes > 4 * 1024) break;
   }
   const int64_t D = static_cast<int64_t>(s_D);
   if (D >= DIST_INF || D > delta) {
@@ -636,10 +639,16 @@ __device__ void sap_move(const Args& a, int edge_cache) {
     return;
   }
   // u* = lowest underloaded expert at distance D
-  s_red[tid] = (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) == D) ? tid : 1 << 30;
-  __syncthreads();
-  for (int st = 512; st > 0; st >>= 1) {
-    if (tid < st) s_red[tid] = min(s_red[tid], s_red[tid + st]);
+  {
+    int u = (tid < n && under_e && static_cast<int64_t>(d[tid] >> IDX_BITS) == D) ? tid : 1 << 30;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) u = min(u, __shfl_xor(u, off));
+    if ((tid & 63) == 0) s_red[tid >> 6] = u;
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) u = min(u, static_cast<int>(s_red[w]));
+      s_red[0] = u;
+    }
     __syncthreads();
   }
   // the path from u* back to its source (an overloaded expert), in LDS
