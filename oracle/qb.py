@@ -387,6 +387,63 @@ def route_qb(scores, k, bias=None, mode=MODE_BATCH, max_rounds=64, stall_rounds=
                 info=(rounds, status, residual, sap_moves))
 
 
+def step_to_fixed(step) -> int:
+    """A bias step in score units on the 2^-40 grid (round half to even)."""
+    v = int(np.rint(np.float64(step) * (1 << FRAC_BITS)))
+    if v <= 0 or v >= BIAS_LIMIT:
+        raise ValueError("step must be positive and below the bias range")
+    return v
+
+
+def sign_update(scores, k, step, max_rounds, bias=None):
+    """DeepSeek-V3's bias rule run on one batch, as the baseline QB is
+    compared with: each round takes the top-k under the current bias and
+    moves every expert's bias by a fixed step towards its target load,
+    b_e += step * sign(C_e - L_e), until every load equals its target or
+    ``max_rounds`` updates were made.  The pages describe it as sign descent
+    (SignSGD) on the same dual objective whose exact coordinate minimiser QB
+    takes, with a step that has to be tuned by hand ([K3-structure-5]
+    延伸解读 "Quantile Balancing与DeepSeek-V3路由的异同").  The same exact keys and
+    targets as :func:`route_qb`; no common offset is removed.
+
+    Returns the dict of :func:`route_qb` with ``info`` = (updates, status,
+    max |L - C|, 0): status 0 balanced, 1 not balanced after ``max_rounds``,
+    2 bias out of range.
+    """
+    s = np.asarray(scores, dtype=np.float32)
+    T, n = s.shape
+    if not (1 <= k <= n <= MAX_EXPERTS):
+        raise ValueError("need 1 <= k <= n <= 1024")
+    if max_rounds < 0:
+        raise ValueError("max_rounds must be >= 0")
+    sfx = to_fixed(s)
+    bfx = np.zeros(n, np.int64) if bias is None else bias_to_fixed(bias)
+    if np.abs(bfx).max(initial=0) >= BIAS_LIMIT:
+        raise ValueError("bias out of range")
+    g = step_to_fixed(step)
+    C = targets(T, n, k)
+    rounds, status = 0, STATUS_OK
+    state = select(sfx, bfx, k)
+    while True:
+        L = state[2].sum(axis=0)
+        if (L == C).all():
+            break
+        if rounds >= max_rounds:
+            status = STATUS_NOT_BALANCED
+            break
+        bfx = bfx + g * np.sign(C - L).astype(np.int64)
+        rounds += 1
+        if np.abs(bfx).max(initial=0) >= BIAS_LIMIT:
+            status = STATUS_BIAS_RANGE
+            break
+        state = select(sfx, bfx, k)
+    S = state[2]
+    L = S.sum(axis=0).astype(np.int64)
+    idx, w = ordered_outputs(s, sfx, S, k)
+    return dict(idx=idx, w=w, loads=L, bias=fixed_to_bias(bfx), bfx=bfx,
+                info=(rounds, status, int(np.abs(L - C).max(initial=0)), 0))
+
+
 def ordered_outputs(s, sfx, S, k):
     """Chosen experts per token by descending raw score (ties: lower index),
     and the raw scores renormalised over the chosen k (reading 6)."""

@@ -258,3 +258,64 @@ def test_sparse_paths_equal_full_relaxation():
             b = full
             moves += 1
         assert moves > 0
+
+
+# --- the fixed-step sign update (DeepSeek-V3's bias rule) -----------------
+# Pinned by closed forms: with n = 2, k = 1 and tokens that all prefer
+# expert 1 by margins D_t (fixed-point units), the rule raises b_0 - b_1 by
+# 2*g per round and token t switches once 2*g*r >= D_t (equal keys go to the
+# lower index), so balance (C = (T/2, T/2)) comes after ceil(D_(T/2) / 2g)
+# rounds, D_(T/2) the (T/2)-th smallest margin.
+
+def _two_expert_scores(margins_fx):
+    base = np.float32(0.25)
+    s = np.empty((len(margins_fx), 2), np.float32)
+    for t, m in enumerate(margins_fx):
+        s[t, 0] = base
+        s[t, 1] = np.float32(base + np.float64(m) * 2.0 ** -40)
+    return s
+
+
+def test_sign_update_two_experts_closed_form():
+    for g_exp in (24, 30, 33):
+        g = 1 << g_exp
+        # one token: rounds = ceil(D / 2g)
+        s = _two_expert_scores([3 * 2 ** 34])
+        D = int(qb.to_fixed(s)[0, 1] - qb.to_fixed(s)[0, 0])
+        r = qb.sign_update(s, 1, g * 2.0 ** -40, 10 ** 6)
+        assert r["info"][:2] == (-(-D // (2 * g)), qb.STATUS_OK)
+        assert r["bfx"][0] == -r["bfx"][1] == g * r["info"][0]
+        assert r["idx"][0, 0] == 0 and r["loads"].tolist() == [1, 0]
+    # four tokens, wide-apart margins: the second smallest decides
+    s = _two_expert_scores([7 * 2 ** 36, 2 ** 33, 3 * 2 ** 35, 2 ** 38])
+    sfx = qb.to_fixed(s)
+    D = np.sort(sfx[:, 1] - sfx[:, 0])
+    g = 1 << 31
+    r = qb.sign_update(s, 1, g * 2.0 ** -40, 10 ** 6)
+    assert r["info"][:3] == (-(-int(D[1]) // (2 * g)), qb.STATUS_OK, 0)
+    assert r["loads"].tolist() == [2, 2]
+
+
+def test_sign_update_exact_tie_goes_to_lower_index():
+    g = 1 << 30
+    s = _two_expert_scores([6 * g])  # D = 6g: keys equal after 3 rounds
+    D = int(qb.to_fixed(s)[0, 1] - qb.to_fixed(s)[0, 0])
+    assert D == 6 * g
+    r = qb.sign_update(s, 1, g * 2.0 ** -40, 100)
+    assert r["info"][0] == 3 and r["idx"][0, 0] == 0
+
+
+def test_sign_update_balanced_input_and_round_cap():
+    s = rand_scores(300, 16, 3)
+    ref = qb.route_qb(s, 4)
+    r = qb.sign_update(s, 4, 2.0 ** -10, 50, bias=ref["bias"])
+    assert r["info"] == (0, qb.STATUS_OK, 0, 0)
+    assert (r["bfx"] == ref["bfx"]).all() and (r["idx"] == ref["idx"]).all()
+    # from zero: a capped run reports "not balanced" with its residual; the
+    # balanced result, when reached, is the unique balanced selection
+    r0 = qb.sign_update(s, 4, 2.0 ** -10, 0)
+    assert r0["info"][0] == 0 and r0["info"][1] == qb.STATUS_NOT_BALANCED
+    assert (r0["idx"] == qb.route_qb(s, 4, mode=qb.MODE_FROZEN)["idx"]).all()
+    r5 = qb.sign_update(s, 4, 2.0 ** -10, 5)
+    assert r5["info"][0] == 5 and r5["info"][1] == qb.STATUS_NOT_BALANCED
+    assert r5["info"][2] == int(np.abs(r5["loads"] - qb.targets(300, 16, 4)).max())
