@@ -133,6 +133,31 @@ int moe_route_qb(const float* scores, int32_t T, int32_t n, int32_t k, int32_t m
                  int32_t* loads, int32_t* qb_info, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/*
+ * moe_route_sign -- the fixed-step sign update of the routing bias
+ * (DeepSeek-V3's rule), run on one batch as the baseline Quantile Balancing
+ * is compared with: sign descent on the same dual objective with a
+ * hand-tuned step (xhh.club page above, 延伸解读 "Quantile Balancing与
+ * DeepSeek-V3路由的异同").  Each round takes the top-k of the biased keys
+ * (exactly as moe_route_qb) and then moves every expert's bias by
+ * step * sign(C_e - L_e); the loop stops at exact balance or after
+ * max_rounds updates.
+ *   scores, topk_idx, topk_w, loads, workspace: as for moe_route_qb
+ *   step     bias step in score units, > 0; used as rint(step * 2^40) grid
+ *            units (at least one unit, below 2^50)
+ *   max_rounds  updates at most (>= 0; 0 = plain top-k under the given bias)
+ *   bias     [n] f64 in: the start; out: the bias after the last update
+ *            (no common offset removed)
+ *   qb_info  [4] i32: updates made, status (0 balanced, 1 not balanced after
+ *            max_rounds, 2 bias left the representable range), max
+ *            |load - target| at exit, 0
+ * Synchronises `stream` while it runs (it polls the loop's phase word).
+ */
+int moe_route_sign(const float* scores, int32_t T, int32_t n, int32_t k, double step,
+                   int32_t max_rounds, double* bias, int32_t* topk_idx, float* topk_w,
+                   int32_t* loads, int32_t* qb_info, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* Bytes of device workspace moe_latent_forward needs for this shape; 0 on bad input. */
 size_t moe_forward_workspace_bytes(const moe_shape_t* shape);
 

@@ -23,7 +23,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
 MOE_QB_FROZEN, MOE_QB_BATCH = 0, 1
-EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_forward_workspace_bytes",
+EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_route_sign",
+            "moe_forward_workspace_bytes",
             "moe_latent_forward", "moe_status_str", "moe_stage_timing", "moe_stage_times",
             "moe_stage_name")
 
@@ -49,6 +50,9 @@ _lib.moe_route_workspace_bytes.restype = _sz
 _lib.moe_route_qb.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                               _sz, _vp]
 _lib.moe_route_qb.restype = ctypes.c_int
+_lib.moe_route_sign.argtypes = [_vp, _i32, _i32, _i32, ctypes.c_double, _i32, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _sz, _vp]
+_lib.moe_route_sign.restype = ctypes.c_int
 _lib.moe_forward_workspace_bytes.argtypes = [ctypes.POINTER(MoeShape)]
 _lib.moe_forward_workspace_bytes.restype = _sz
 _lib.moe_latent_forward.argtypes = [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _vp,
@@ -123,6 +127,30 @@ def route_qb(scores: torch.Tensor, k: int, bias: torch.Tensor | None = None,
                            _ptr(loads), _ptr(info), _ptr(ws), ws.numel(), _stream())
     if st != 0:
         raise MoeError(st, "moe_route_qb")
+    return dict(idx=idx, w=w, loads=loads, bias=b, info=info)
+
+
+def route_sign(scores: torch.Tensor, k: int, step: float, max_rounds: int,
+               bias: torch.Tensor | None = None, workspace=None):
+    """DeepSeek-V3's fixed-step sign update of the bias on fp32 scores [T, n]
+    (device), the baseline for Quantile Balancing.  Returns the dict of
+    :func:`route_qb` with info = (updates, status, max |load-target|, 0)."""
+    dev = scores.device
+    T, n = scores.shape
+    _check(scores, "scores", torch.float32, (T, n), dev)
+    b = torch.zeros(n, dtype=torch.float64, device=dev) if bias is None else bias.clone()
+    _check(b, "bias", torch.float64, (n,), dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    loads = torch.empty(n, dtype=torch.int32, device=dev)
+    info = torch.zeros(4, dtype=torch.int32, device=dev)
+    need = route_workspace_bytes(T, n, k)
+    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8,
+                                                             device=dev)
+    st = _lib.moe_route_sign(_ptr(scores), T, n, k, float(step), max_rounds, _ptr(b), _ptr(idx),
+                             _ptr(w), _ptr(loads), _ptr(info), _ptr(ws), ws.numel(), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_route_sign")
     return dict(idx=idx, w=w, loads=loads, bias=b, info=info)
 
 

@@ -797,6 +797,106 @@ __global__ __launch_bounds__(1024) void status_pass(Args a, int edge_cache) {
 }
 
 // ---------------------------------------------------------------------------
+// Fixed-step sign update (DeepSeek-V3's bias rule, the baseline QB is
+// compared with; xhh.club "Kimi K3 模型结构（5）", 延伸解读 "Quantile
+// Balancing与DeepSeek-V3路由的异同": sign descent on the same dual with a
+// hand-tuned step).  One block of 1024 threads after each top-k pass: loads,
+// then b_e += step * sign(C_e - L_e) unless balanced or out of rounds.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void sign_status(Args a, int64_t step) {
+  __shared__ int32_t s_imb[16], s_res[16];
+  __shared__ int s_upd, s_bad;
+  const int n = a.n;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int imb = 0, res = 0;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    int32_t L = 0;
+    for (int r = 0; r < ACC_COPIES; ++r) {
+      L += a.acc[r * n + e];
+      a.acc[r * n + e] = 0;
+    }
+    a.loads[e] = L;
+    const int64_t d = static_cast<int64_t>(L) - target(a.T, n, a.k, e);
+    imb += d != 0;
+    const int ad = static_cast<int>(d < 0 ? -d : d);
+    res = res > ad ? res : ad;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    imb += __shfl_xor(imb, off);
+    res = max(res, __shfl_xor(res, off));
+  }
+  if (lane == 0) {
+    s_imb[wid] = imb;
+    s_res[wid] = res;
+  }
+  __syncthreads();
+  int64_t* c = a.ctrl;
+  if (threadIdx.x == 0) {
+    imb = 0;
+    res = 0;
+    for (int w = 0; w < 16; ++w) {
+      imb += s_imb[w];
+      res = max(res, s_res[w]);
+    }
+    c[C_IMB] = imb;
+    c[C_RESID] = res;
+    c[C_PIVOT] = 1;  // th[].k1 holds this pass's keys
+    c[C_DROP] = 0;
+    int upd = 0;
+    if (c[C_PHASE] == PH_ROUNDS) {
+      if (imb == 0) {
+        c[C_PHASE] = PH_DONE;
+      } else if (c[C_ROUNDS] >= c[C_MAX_ROUNDS]) {
+        c[C_PHASE] = PH_FAILED;
+        c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;
+      } else {
+        upd = 1;
+        c[C_ROUNDS] += 1;
+        c[C_DROP] = step;  // no bias falls by more than the step
+      }
+    }
+    s_upd = upd;
+    s_bad = 0;
+  }
+  __syncthreads();
+  if (!s_upd) return;
+  int64_t* bias = a.bfx + (c[C_CUR] & 1) * n;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int64_t L = a.loads[e], C = target(a.T, n, a.k, e);
+    const int64_t b = bias[e] + (L < C ? step : (L > C ? -step : 0));
+    bias[e] = b;
+    if (b >= BIAS_LIMIT || b <= -BIAS_LIMIT) s_bad = 1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && s_bad) {
+    c[C_PHASE] = PH_FAILED;
+    c[C_STATUS] = MOE_QB_STATUS_BIAS_RANGE;
+  }
+}
+
+// Bias and counters of a sign-update run (no common offset is removed).
+__global__ void sign_export(Args a, double* bias_out, int32_t* info) {
+  const int n = a.n;
+  int64_t* c = a.ctrl;
+  const int64_t* bias = a.bfx + (c[C_CUR] & 1) * n;
+  for (int e = threadIdx.x; e < n; e += blockDim.x)
+    bias_out[e] = static_cast<double>(bias[e]) * (1.0 / 1099511627776.0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t ph = c[C_PHASE];
+    if (ph != PH_DONE && c[C_STATUS] == MOE_QB_STATUS_OK)
+      c[C_STATUS] = MOE_QB_STATUS_NOT_BALANCED;  // the host's step cap ended the loop
+    c[C_DROP] = 0;  // biases unchanged since the last pass
+    if (info) {
+      info[0] = static_cast<int32_t>(c[C_ROUNDS]);
+      info[1] = static_cast<int32_t>(c[C_STATUS]);
+      info[3] = 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // One quantile round (one block per expert, reading the transposed scores so
 // the column is contiguous): an unbalanced expert finds the C-th and
 // (C+1)-th largest margins over all tokens exactly and jumps to minus their
@@ -1305,6 +1405,73 @@ int route_run(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode
   return MOE_OK;
 }
 
+// The sign-update baseline on the same workspace: top-k pass and sign status
+// per step, in polled batches like the balancing loop; then the outputs.
+int route_sign_run(const float* scores, int32_t T, int32_t n, int32_t k, int64_t step,
+                   int32_t max_rounds, double* bias, int32_t* idx, float* w, int32_t* loads_out,
+                   int32_t* info, const RouteWorkspace& ws, hipStream_t stream) {
+  using namespace qb;
+  Args a{};
+  a.scores = scores;
+  a.scoresT = ws.scoresT;
+  a.T = T;
+  a.n = n;
+  a.k = k;
+  a.bfx = ws.bfx;
+  a.th = ws.th;
+  a.loads = ws.loads;
+  a.acc = ws.acc;
+  a.ctrl = ws.ctrl;
+  a.cnt = ws.cnt;
+  a.edges = ws.edges;
+  a.edge_cap = ws.edge_cap;
+  a.idx = idx;
+  a.w = w;
+  const int grid = T > 0 ? std::min((T + 3) / 4, TOPK_MAX_GRID) : 1;
+  const size_t smem = topk_smem_bytes();
+  hipLaunchKernelGGL(zero_cnt, dim3(1), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(init_ctrl, dim3(1), dim3(1024), 0, stream, a, static_cast<const double*>(bias),
+                     static_cast<int>(MOE_QB_BATCH), max_rounds);
+  hipLaunchKernelGGL(check_range, dim3(1), dim3(64), 0, stream, a);
+  MOE_LAUNCH_CHECK();
+  if (T > 0) {
+    const int batch = 4;
+    const int max_steps = max_rounds + 2 * batch + 1;
+    PollState* ps = poll_state();
+    if (!ps) return MOE_EHIP;
+    int steps = 0, launched = 0;
+    while (true) {
+      const int slot = launched & 1;
+      for (int i = 0; i < batch; ++i) {
+        hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 0);
+        hipLaunchKernelGGL(sign_status, dim3(1), dim3(1024), 0, stream, a, step);
+      }
+      MOE_LAUNCH_CHECK();
+      MOE_HIP_CHECK(hipMemcpyAsync(ps->word + 8 * slot, ws.ctrl + C_PHASE, sizeof(int64_t),
+                                   hipMemcpyDeviceToHost, stream));
+      MOE_HIP_CHECK(hipEventRecord(ps->ev[slot], stream));
+      ++launched;
+      steps += batch;
+      if (launched >= 2) {
+        const int prev = slot ^ 1;
+        MOE_HIP_CHECK(hipEventSynchronize(ps->ev[prev]));
+        const int64_t phase = ps->word[8 * prev];
+        if (phase == PH_DONE || phase == PH_FAILED) break;
+      }
+      if (steps >= max_steps) break;
+    }
+  }
+  hipLaunchKernelGGL(sign_export, dim3(1), dim3(1024), 0, stream, a, bias, info);
+  hipLaunchKernelGGL(topk_pass, dim3(grid), dim3(TOPK_BLOCK), smem, stream, a, 1);
+  hipLaunchKernelGGL(status_pass, dim3(1), dim3(1024), 0, stream, a, 0);
+  hipLaunchKernelGGL(export_resid, dim3(1), dim3(64), 0, stream, a, info);
+  if (loads_out)
+    MOE_HIP_CHECK(hipMemcpyAsync(loads_out, ws.loads, sizeof(int32_t) * n,
+                                 hipMemcpyDeviceToDevice, stream));
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 extern "C" size_t moe_route_workspace_bytes(int32_t T, int32_t n, int32_t k) {
@@ -1327,4 +1494,23 @@ extern "C" int moe_route_qb(const float* scores, int32_t T, int32_t n, int32_t k
   moe::prof::Scope sc(moe::prof::ST_ROUTING, static_cast<hipStream_t>(stream));
   return moe::route_run(scores, T, n, k, mode, max_rounds, bias, topk_idx, topk_w, loads, qb_info,
                         ws, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int moe_route_sign(const float* scores, int32_t T, int32_t n, int32_t k, double step,
+                              int32_t max_rounds, double* bias, int32_t* topk_idx, float* topk_w,
+                              int32_t* loads, int32_t* qb_info, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  int st = moe::route_validate(T, n, k);
+  if (st != MOE_OK) return st;
+  if (max_rounds < 0 || !(step > 0.0)) return MOE_EINVAL;
+  const double sf = rint(step * 1099511627776.0);
+  if (!(sf >= 1.0 && sf < static_cast<double>(moe::qb::BIAS_LIMIT))) return MOE_EINVAL;
+  if ((T > 0 && (!scores || !topk_idx || !topk_w)) || !bias || !workspace) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MOE_EINVAL;
+  moe::RouteWorkspace ws;
+  const size_t need = moe::route_workspace_layout(T, n, &ws, workspace);
+  if (workspace_bytes < need) return MOE_EWORKSPACE;
+  moe::prof::Scope sc(moe::prof::ST_ROUTING, static_cast<hipStream_t>(stream));
+  return moe::route_sign_run(scores, T, n, k, static_cast<int64_t>(sf), max_rounds, bias, topk_idx,
+                             topk_w, loads, qb_info, ws, static_cast<hipStream_t>(stream));
 }

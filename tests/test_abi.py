@@ -71,3 +71,20 @@ def test_binding_fails_loudly_without_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import sparse_moe_ffn_sigmoid_amd"],
                        cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "libmoe_mi355x.so is missing" in r.stderr
+
+
+def test_sign_route_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    need = lib.moe_route_workspace_bytes(100, 64, 4)
+    args = lambda T, n, k, step=2.0 ** -10, rounds=8, ws=fake: (
+        fake, T, n, k, ctypes.c_double(step), rounds, fake, fake, fake, fake, fake, ws, need, None)
+    assert lib.moe_route_sign(*args(100, 64, 65)) == -1        # k > n
+    assert lib.moe_route_sign(*args(100, 2048, 4)) == -2       # n > 1024
+    assert lib.moe_route_sign(*args(100, 64, 4, step=0.0)) == -1
+    assert lib.moe_route_sign(*args(100, 64, 4, step=-1.0)) == -1
+    assert lib.moe_route_sign(*args(100, 64, 4, step=2.0 ** -45)) == -1   # below one grid unit
+    assert lib.moe_route_sign(*args(100, 64, 4, step=2.0 ** 11)) == -1    # beyond the bias range
+    assert lib.moe_route_sign(*args(100, 64, 4, rounds=-1)) == -1
+    assert lib.moe_route_sign(*args(100, 64, 4, ws=None)) == -1

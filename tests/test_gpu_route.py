@@ -138,3 +138,46 @@ def test_route_qb_workload_full_size():
         assert hashlib.sha256(got["idx"].astype("<i4").tobytes()).hexdigest() == gold["idx_sha256"]
         assert [int(v) for v in np.rint(got["bias"] * 2.0 ** 40)] == gold["bias_fixed"]
         assert [int(v) for v in got["info"]] == gold["info"]
+
+
+# --- the fixed-step sign update baseline ----------------------------------
+
+def gpu_sign(s, k, step, rounds, bias=None):
+    import sparse_moe_ffn_sigmoid_amd as moe
+    b = None if bias is None else torch.from_numpy(np.asarray(bias, np.float64)).cuda()
+    r = moe.route_sign(torch.from_numpy(s).cuda(), k, step, rounds, b)
+    torch.cuda.synchronize()
+    return {key: v.cpu().numpy() for key, v in r.items()}
+
+
+SIGN_CASES = [
+    ("tiny", 64, 32, 4, 0.3, 2.0 ** -12, 300),
+    ("decode", 64, 896, 16, 0.5, 2.0 ** -10, 64),
+    ("ragged", 1000, 100, 7, 1.0, 2.0 ** -9, 100),
+    ("k3_prefill_shape", 4096, 896, 16, 0.5, 2.0 ** -10, 64),
+    ("no_rounds", 500, 64, 8, 0.5, 2.0 ** -10, 0),
+]
+
+
+@pytest.mark.parametrize("name,T,n,k,std,step,rounds", SIGN_CASES)
+def test_route_sign_parity(name, T, n, k, std, step, rounds):
+    announce(f"sign {name} T={T} n={n} k={k} step={step} rounds={rounds}")
+    s = scores(T, n, std)
+    ref = qb.sign_update(s, k, step, rounds)
+    got = gpu_sign(s, k, step, rounds)
+    assert (got["idx"] == ref["idx"]).all()
+    assert (got["loads"] == ref["loads"]).all()
+    assert (got["bias"] == ref["bias"]).all()
+    assert tuple(int(v) for v in got["info"]) == tuple(ref["info"])
+    assert np.allclose(got["w"], ref["w"], rtol=(k + 1) * 2.0 ** -24, atol=0)
+
+
+def test_route_sign_two_experts_closed_form():
+    # n = 2, k = 1, one token preferring expert 1 by D grid units: balance
+    # after ceil(D / 2g) updates (the oracle's pin), here on the GPU
+    s = np.array([[0.25, 0.25 + 3 * 2.0 ** -6]], np.float32)
+    D = int(qb.to_fixed(s)[0, 1] - qb.to_fixed(s)[0, 0])
+    g = 1 << 30
+    got = gpu_sign(s, 1, g * 2.0 ** -40, 10000)
+    assert int(got["info"][0]) == -(-D // (2 * g)) and int(got["info"][1]) == 0
+    assert got["idx"][0, 0] == 0
