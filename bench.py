@@ -107,6 +107,39 @@ def cpu_baseline(inp, shape, sample_tokens):
                        f"({t_layer:.1f} s); tokens/s = 1 / (route_s/T + layer_s/sample)")}
 
 
+def sign_baseline(moe, sh, w, x, bias0, ws, shape):
+    """QB and the fixed-step sign update on the router scores of this batch:
+    updates made, status, max |load - target| and the routing time."""
+    import torch
+    scores = moe.latent_forward(sh, w, x, bias=bias0, workspace=ws, want_scores=True)["scores"]
+    scores = scores.contiguous()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        r = fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return r, ev[0].elapsed_time(ev[1])
+
+    r, ms = timed(lambda: moe.route_qb(scores, shape.k))
+    info = [int(v) for v in r["info"].cpu()]
+    out = {"scores": "this batch's router scores",
+           "qb": {"rounds": info[0], "moves": info[3], "status": info[1],
+                  "max_abs_imbalance": info[2], "ms": ms}}
+    rows = []
+    for step in (2.0 ** -7, 2.0 ** -10, 2.0 ** -13):
+        for rounds in (64, 256, 1024):
+            r, ms = timed(lambda: moe.route_sign(scores, shape.k, step, rounds))
+            info = [int(v) for v in r["info"].cpu()]
+            rows.append({"step": step, "max_rounds": rounds, "updates": info[0],
+                         "status": info[1], "max_abs_imbalance": info[2], "ms": ms})
+    out["sign"] = rows
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +150,9 @@ def main():
     ap.add_argument("--qb", default="batch", choices=["batch", "frozen"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sign-baseline", action="store_true",
+                    help="also route this batch's scores with the fixed-step sign update "
+                         "(DeepSeek-V3's bias rule) and report rounds / imbalance / time beside QB")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many bytes "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -227,6 +263,8 @@ def main():
             "wall_s": wall,
         },
     }
+    if args.sign_baseline:
+        rec["routing_baseline"] = sign_baseline(moe, sh, w, x, bias0, ws, shape)
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
