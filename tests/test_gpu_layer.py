@@ -95,3 +95,18 @@ def test_layer_empty_batch():
     announce("layer T=0")
     got = run_gpu(moe, shape, inp)
     assert got["out"].shape == (0, shape.d) and (got["loads"] == 0).all()
+
+
+def test_bf16_decode_with_bias_from_a_qb_batch():
+    # inference routing: QB balances a prefill batch, then a decode batch of
+    # the same layer is routed with that bias frozen
+    import sparse_moe_ffn_sigmoid_amd as moe
+    pre = workloads.small_shape(T=400, k=4)
+    inp = workloads.layer_inputs(pre, "cpu", seed=6, random_gamma=True)
+    announce("prefill batch with QB")
+    got_pre = run_gpu(moe, pre, inp)
+    assert int(got_pre["info"][1]) == qb.STATUS_OK
+    assert (got_pre["loads"] == qb.targets(pre.T, pre.n, pre.k)).all()
+    dec = workloads.small_shape(T=16, k=4)
+    check_layer(dec, seed=6, qb_mode=qb.MODE_FROZEN, bias=got_pre["bias"],
+                name="decode, bias carried over")
