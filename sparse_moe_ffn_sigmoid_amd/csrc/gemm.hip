@@ -28,6 +28,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements)
 constexpr int NTHREADS = 256;
+constexpr int DENSE_GROUP_M = 4;
 
 struct Tile {
   int expert, row0, rows, n0;
@@ -70,10 +71,16 @@ __device__ __forceinline__ bool locate_tile(const Params& p, int ntn, int bn_out
   }
   const int G = gridDim.x;
   const int tau = (b & 7) * (G >> 3) + (b >> 3);
-  const int mt = tau / ntn, nt = tau - mt * ntn;
+  const int ntm = (p.M + BM - 1) / BM;
+  if (tau >= ntm * ntn) return false;
+  // groups of DENSE_GROUP_M row tiles walked column by column: the blocks an
+  // XCD runs side by side share a few A and B panels in its L2
+  const int grp = tau / (DENSE_GROUP_M * ntn);
+  const int gm = min(DENSE_GROUP_M, ntm - grp * DENSE_GROUP_M);
+  const int r = tau - grp * DENSE_GROUP_M * ntn;
+  const int mt = grp * DENSE_GROUP_M + r % gm, nt = r / gm;
   t.expert = 0;
   t.row0 = mt * BM;
-  if (t.row0 >= p.M) return false;
   t.rows = min(BM, p.M - t.row0);
   t.n0 = nt * bn_out;
   return true;
@@ -396,6 +403,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most `ahead` stages of PER load instructions each are still
+// in flight (ahead is uniform across the block and at most MAXA).
+template <int MAXA, int PER>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (MAXA <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= MAXA)
+      wait_vmcnt<MAXA * PER>();
+    else
+      wait_stages<MAXA - 1, PER>(ahead);
+  }
+}
+
 // chunk swizzle of a row: 128-byte rows XOR with r mod 8, 64-byte rows with
 // (r / 2) mod 4 (two rows share a 128-byte bank window)
 template <int BKP>
@@ -403,9 +424,10 @@ __device__ __forceinline__ int swz(int r) {
   return BKP == 64 ? (r & 7) : ((r >> 1) & 3);
 }
 
-template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT>
-__global__ __launch_bounds__(NTHREADS, (BKP == 32 && BM * BN <= 128 * 256) ? 2 : 1) void gemm_pipe(Params p) {
-  constexpr int WN = 4 / WM;
+template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT, int NW>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 256) ? 2 : 1) void gemm_pipe(Params p) {
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves per block");
+  constexpr int WN = NW / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold 32x32 blocks");
@@ -416,15 +438,17 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 && BM * BN <= 128 * 256) ? 2 :
   constexpr int RPI = 64 / CH;       // rows per load instruction
   constexpr int NA = BM / RPI, NB = BN / RPI;
   static_assert(NA * RPI == BM && NB * RPI == BN, "tile rows per instruction");
-  constexpr int MA = (NA + 3) / 4, MB = (NB + 3) / 4;
-  // Every wave issues MA (MB) load instructions per stage; when 4 does not
-  // divide NA (NB) the surplus ones repeat instruction i-1 of the same wave's
-  // neighbour range (same source, same LDS bytes), so the per-wave count of
-  // outstanding loads is uniform and known at compile time.
-  auto a_ins = [](int w, int i) { const int x = w + 4 * i; return x < NA ? x : x - 4; };
-  auto b_ins = [](int w, int i) { const int x = w + 4 * i; return x < NB ? x : x - 4; };
+  constexpr int MA = (NA + NW - 1) / NW, MB = (NB + NW - 1) / NW;
+  static_assert(NA >= NW && NB >= NW, "every wave loads A and B rows");
+  // Every wave issues MA (MB) load instructions per stage; when NW does not
+  // divide NA (NB) the surplus ones repeat the wave's own instruction i-1
+  // (same source, same LDS bytes), so the per-wave count of outstanding loads
+  // is uniform and known at compile time.
+  auto a_ins = [](int w, int i) { const int x = w + NW * i; return x < NA ? x : x - NW; };
+  auto b_ins = [](int w, int i) { const int x = w + NW * i; return x < NB ? x : x - NW; };
 
-  static_assert(NST == 3 || NST == 4, "ring depth");
+  static_assert(NST >= 3 && NST <= 6, "ring depth");
+  static_assert((NST - 2) * (MA + MB) < 64, "loads in flight exceed the vmcnt range");
   // One LDS variable per stage (A rows, then B rows): the compiler tracks
   // direct-to-LDS loads per variable, so reads of one stage do not wait for
   // loads still in flight into another.
@@ -432,8 +456,12 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 && BM * BN <= 128 * 256) ? 2 :
   __shared__ __attribute__((aligned(1024))) bf16_t st0[SW];
   __shared__ __attribute__((aligned(1024))) bf16_t st1[SW];
   __shared__ __attribute__((aligned(1024))) bf16_t st2[SW];
-  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST == 4 ? SW : 8];
-  bf16_t* const stg[4] = {st0, st1, st2, st3};
+  // (unused stages are 16-byte stubs, so a 160 KB ring is not pushed over
+  // the limit by alignment padding)
+  __shared__ __attribute__((aligned(NST >= 4 ? 1024 : 16))) bf16_t st3[NST >= 4 ? SW : 8];
+  __shared__ __attribute__((aligned(NST >= 5 ? 1024 : 16))) bf16_t st4[NST >= 5 ? SW : 8];
+  __shared__ __attribute__((aligned(NST >= 6 ? 1024 : 16))) bf16_t st5[NST >= 6 ? SW : 8];
+  bf16_t* const stg[6] = {st0, st1, st2, st3, st4, st5};
 
   const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
   Tile tile;
@@ -580,12 +608,7 @@ __global__ __launch_bounds__(NTHREADS, (BKP == 32 && BM * BN <= 128 * 256) ? 2 :
   auto ring = [&](int kt, bf16_t* Ac, bf16_t* Bc, bf16_t* An, bf16_t* Bn) {
     if (kt < ktot) {  // uniform across the block
       const int ahead = min(NST - 2, ktot - 1 - kt);  // tiles issued after tile kt
-      if (ahead >= 2)
-        wait_vmcnt<2 * (MA + MB)>();
-      else if (ahead == 1)
-        wait_vmcnt<MA + MB>();
-      else
-        wait_vmcnt<0>();
+      wait_stages<NST - 2, MA + MB>(ahead);
       lds_barrier();
       if (kt + NST - 1 < ktot) issue(An, Bn);
       compute(Ac, Bc);
@@ -1087,7 +1110,7 @@ static int run_bf16(const Params& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT>
+template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT, int NW = 4>
 static int run_pipe(const Params& p, hipStream_t stream, size_t pad_lds = 0) {
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   for (int s = 0; s < p.nseg; ++s)
@@ -1100,15 +1123,15 @@ static int run_pipe(const Params& p, hipStream_t stream, size_t pad_lds = 0) {
   if (pad_lds > 0) {  // unused dynamic LDS that caps the blocks per CU
     static std::atomic<bool> configured{false};
     if (!configured.load(std::memory_order_relaxed)) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT, NW>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(pad_lds)) != hipSuccess)
         return MOE_EHIP;
       configured.store(true, std::memory_order_relaxed);
     }
   }
-  hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT>), dim3(static_cast<unsigned>(G8)),
-                     dim3(NTHREADS), pad_lds, stream, p);
+  hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT, NW>), dim3(static_cast<unsigned>(G8)),
+                     dim3(64 * NW), pad_lds, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -1133,14 +1156,16 @@ constexpr int pipe_stages() {
 
 // BNT: B rows are read by exactly one block (grouped problems with one row
 // tile per expert), so they are streamed with the non-temporal policy.
-template <int BM, int BN, int WM, int BKP, bool BNT = false>
+// NW: waves per block; 8 (two per SIMD) for the 256- and 320-row MFMA-bound
+// tiles, so one wave's MFMAs cover the other's LDS and barrier waits.
+template <int BM, int BN, int WM, int BKP, bool BNT = false, int NW = 4>
 static int dispatch_pipe(const Params& p, int epi, hipStream_t s) {
   constexpr int NST = pipe_stages<BM, BN, BKP>();
   switch (epi) {
-    case EPI_BF16: return run_pipe<BM, BN, WM, EPI_BF16, BKP, NST, BNT>(p, s);
-    case EPI_F32: return run_pipe<BM, BN, WM, EPI_F32, BKP, NST, BNT>(p, s);
-    case EPI_SIGMOID: return run_pipe<BM, BN, WM, EPI_SIGMOID, BKP, NST, BNT>(p, s);
-    case EPI_SITU: return run_pipe<BM, BN, WM, EPI_SITU, BKP, NST, BNT>(p, s);
+    case EPI_BF16: return run_pipe<BM, BN, WM, EPI_BF16, BKP, NST, BNT, NW>(p, s);
+    case EPI_F32: return run_pipe<BM, BN, WM, EPI_F32, BKP, NST, BNT, NW>(p, s);
+    case EPI_SIGMOID: return run_pipe<BM, BN, WM, EPI_SIGMOID, BKP, NST, BNT, NW>(p, s);
+    case EPI_SITU: return run_pipe<BM, BN, WM, EPI_SITU, BKP, NST, BNT, NW>(p, s);
     default: return MOE_EUNSUPPORTED;
   }
 }
@@ -1240,9 +1265,11 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
     if (bm_hint <= 32) return dispatch_pipe<32, 256, 1, 64, true>(q, epi, stream);
     if (bm_hint <= 96)  // 128-byte row pieces per stage, one block per CU
       return dispatch_pipe<96, 256, 1, 64, true>(q, epi, stream);
-    // tall experts (MFMA-bound): 160 x 64 or 128 x 128 per wave
+    // tall experts (MFMA-bound): 160 x 64, 160 x 64 (8 waves) or 128 x 64
+    // (8 waves) per wave
     if (bm_hint == 160) return dispatch_pipe<160, 256, 1, 64>(q, epi, stream);
-    if (bm_hint == 256) return dispatch_pipe<256, 256, 2, 32>(q, epi, stream);
+    if (bm_hint == 320) return dispatch_pipe<320, 256, 2, 32, false, 8>(q, epi, stream);
+    if (bm_hint == 256) return dispatch_pipe<256, 256, 2, 32, false, 8>(q, epi, stream);
     return dispatch_pipe<128, 128, 2, 32>(q, epi, stream);
   }
   if (bfmt == B_DENSE && bm_hint == BM_SHARE && p.M >= 256) {
@@ -1263,7 +1290,7 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
     else if (d.cfg == 1)
       rc = dispatch_pipe<64, 256, 1, 64>(q, epi, stream);
     else if (d.cfg == 4)
-      rc = dispatch_pipe<256, 256, 2, 32>(q, epi, stream);
+      rc = dispatch_pipe<256, 256, 2, 32, false, 8>(q, epi, stream);
     else if (d.cfg == 3)
       rc = dispatch_pipe<256, 128, 2, 32>(q, epi, stream);
     else

@@ -209,8 +209,8 @@ struct ForwardWorkspace {
 };
 
 // Tile height of the grouped expert GEMMs, from the mean rows per expert
-// (exact under QB): 32 for decode-like batches, 96 up to 96 rows, 160 up to
-// 320 rows (one or two tiles per expert), else 256; MXFP4 takes 160 when its
+// (exact under QB): 32 for decode-like batches, then 96, 160 or 320 rows
+// (one tile per expert up to 320 rows), else 256; MXFP4 takes 160 when its
 // pipelined kernel applies, else 128.
 static int grouped_bm(const moe_shape_t& s) {
   const int64_t avg = (static_cast<int64_t>(s.T) * s.top_k + s.n_experts - 1) / s.n_experts;
@@ -223,7 +223,8 @@ static int grouped_bm(const moe_shape_t& s) {
     return 128;
   }
   if (avg <= 96) return 96;
-  if (avg <= 320) return 160;  // one or two 160-row tiles per expert
+  if (avg <= 160) return 160;
+  if (avg <= 320) return 320;
   return 256;
 }
 

@@ -52,9 +52,12 @@ def test_tiny_fp32_layer():
     dict(T=37, n=24, k=3, d=448, latent=192, m=128, shared=192),
     dict(T=16, n=64, k=4),                                     # ~1 row per expert (small-M tile)
     dict(T=600, n=16, k=4),                                    # 150 rows per expert: one 160-row tile
+    dict(T=1000, n=16, k=4, seed=7),                           # 250 rows: one 320-row tile (8 waves)
 ])
 def test_bf16_layer(kw):
-    check_layer(workloads.small_shape(**kw), seed=1, name=f"bf16 {kw}")
+    kw = dict(kw)
+    seed = kw.pop("seed", 1)
+    check_layer(workloads.small_shape(**kw), seed=seed, name=f"bf16 {kw}")
 
 
 def test_mxfp4_layer():
@@ -86,6 +89,16 @@ def test_bf16_layer_frozen_bias():
     shape = workloads.small_shape(T=120)
     bias = np.rint(np.random.default_rng(4).normal(0, 0.1, shape.n) * 2.0 ** 40) * 2.0 ** -40
     check_layer(shape, seed=4, qb_mode=qb.MODE_FROZEN, bias=bias, name="bf16 frozen")
+
+
+def test_bf16_layer_frozen_uneven_tall_tiles():
+    # a skewed router with a frozen zero bias: 250 rows per expert on average
+    # (320-row tiles), loads from 28 to 838 rows (up to three tiles, ragged).
+    # Seed 8 is not used: rounding the oracle's z, h, h_s, y-hat and output
+    # to bf16 alone moves its output by 2.07e-2 there, above the bf16 bar.
+    shape = workloads.small_shape(T=1000, n=16, k=4, offset_std=1.0)
+    check_layer(shape, seed=9, qb_mode=qb.MODE_FROZEN, bias=np.zeros(shape.n),
+                name="bf16 frozen, uneven 320-row tiles")
 
 
 def test_layer_empty_batch():

@@ -94,7 +94,7 @@ def test_full_size_layer_sampled(wl, qb_mode):
 
 
 # K3 widths with fewer experts, so that each expert holds 150, 300 or 512 rows:
-# one 160-row tile, two 160-row tiles (ragged), two 256 x 256 tiles.
+# one 160-row tile, one 320-row tile (ragged), two 256 x 256 tiles.
 @pytest.mark.parametrize("T,n", [(600, 64), (1200, 64), (2048, 64)])
 def test_tall_expert_tiles_k3_width(T, n):
     shape = dataclasses.replace(workloads.SHAPES["k3_prefill"], T=T, n=n)
