@@ -393,6 +393,19 @@ __device__ __forceinline__ void load_lds16_asm(const void* g, void* lds, bool nt
 #endif
 }
 
+// 4-byte global -> LDS copy per lane (lane i fills bytes [4i, 4i+4) after the
+// M0 base); same ordering rules as load_lds16_asm.
+__device__ __forceinline__ void load_lds4_asm(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+#pragma clang diagnostic pop
+#endif
+}
+
 __device__ __forceinline__ void load_lds16(const bf16_t* g, bf16_t* lds, bool nt = false) {
   load_lds16_asm(g, lds, nt);
 }
@@ -711,10 +724,15 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
   return __uint_as_float(e ? (e << 23) : 0x00400000u);
 }
 
-template <int BM, int BN, int WM, int EPI>
-__global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Params p) {
+// NW: waves per block.  SR: the E8M0 scales travel through the ring (4 bytes
+// per B row per stage: the scale bytes of this stage and its neighbour)
+// instead of a per-block panel of the whole K range, which leaves room for
+// 320-row tiles at any K.
+template <int BM, int BN, int WM, int EPI, int NW, bool SR>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_pipe_fp4(Params p) {
   constexpr int BKP = 64;
-  constexpr int WN = 4 / WM;
+  constexpr int NTH = 64 * NW;
+  constexpr int WN = NW / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold 32x32 blocks");
@@ -722,8 +740,13 @@ __global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Par
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   constexpr int NA = BM / 8, NQ = BN / 32;
   static_assert(NA * 8 == BM && NQ * 32 == BN, "tile rows per instruction");
-  constexpr int MA = (NA + 3) / 4, MQ = (NQ + 3) / 4;
-  static_assert(NA % 4 == 0 && NQ % 4 == 0, "uniform load instructions per wave");
+  constexpr int MA = NA / NW, MQ = NQ / NW;
+  static_assert(NA % NW == 0 && NQ % NW == 0, "uniform load instructions per wave");
+  // scale ring: one 4-byte piece per B row and stage, 64 rows per instruction;
+  // waves past the BN / 64 that are needed repeat a neighbour's instruction
+  constexpr int NS = BN / 64;
+  constexpr int MS = SR ? 1 : 0;
+  static_assert(!SR || (NS <= NW && NS * 64 == BN), "one scale instruction per wave");
 
   __shared__ __attribute__((aligned(1024))) bf16_t sA0[BM * BKP];
   __shared__ __attribute__((aligned(1024))) bf16_t sA1[BM * BKP];
@@ -731,7 +754,10 @@ __global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Par
   __shared__ __attribute__((aligned(1024))) uint8_t sQ0[BN * 32];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ1[BN * 32];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ2[BN * 32];
-  // scale panel [BN][K/32], sized by the launch
+  __shared__ __attribute__((aligned(16))) uint8_t sS0[SR ? BN * 4 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sS1[SR ? BN * 4 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sS2[SR ? BN * 4 : 16];
+  // scale panel [BN][K/32], sized by the launch (not used with SR)
   extern __shared__ __attribute__((aligned(16))) uint8_t sP[];
 
   const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
@@ -759,12 +785,12 @@ __global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Par
 
   // scale panel: 16-byte pieces of each B row's K/32 scale bytes
   const int sp = static_cast<int>(g.ldb >> 4);  // scale bytes per row (multiple of 16)
-  {
+  if (!SR) {
     const uint8_t* S = g.Bs + static_cast<int64_t>(tile.expert) * p.bs_expert_stride;
     const uint8_t* S2 = g.Bs2 + static_cast<int64_t>(tile.expert) * p.bs_expert_stride;
     const int per_row = sp >> 4;
     const int total = BN * per_row;
-    for (int f = tid; f < total; f += NTHREADS) {
+    for (int f = tid; f < total; f += NTH) {
       const int r = f / per_row, c = f - (f / per_row) * per_row;
       bool up;
       const int64_t row = b_row_of(r, up);
@@ -777,7 +803,7 @@ __global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Par
   int a_chunk[MA];
 #pragma unroll
   for (int i = 0; i < MA; ++i) {
-    int r = (wave + 4 * i) * 8 + (lane >> 3);
+    int r = (wave + NW * i) * 8 + (lane >> 3);
     a_chunk[i] = (lane & 7) ^ (r & 7);
     r = r < tile.rows ? r : 0;
     const int slot = tile.row0 + r;
@@ -785,6 +811,8 @@ __global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Par
   }
   const uint8_t* pq[MQ];
   const bf16_t* pa[MA];
+  const uint8_t* ps = nullptr;  // this lane's scale row (SR)
+  const int s_ins = wave % NS;  // scale instruction of this wave (SR)
   {
     const bf16_t* A = static_cast<const bf16_t*>(g.A);
     const uint8_t* Q = static_cast<const uint8_t*>(g.B) + static_cast<int64_t>(tile.expert) * p.b_expert_stride;
@@ -793,26 +821,35 @@ __global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Par
     for (int i = 0; i < MA; ++i) pa[i] = A + a_off[i] * g.lda + a_chunk[i] * 8;
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
-      const int r = (wave + 4 * i) * 32 + (lane >> 1);
+      const int r = (wave + NW * i) * 32 + (lane >> 1);
       const int half = (lane & 1) ^ ((r >> 2) & 1);
       bool up;
       const int64_t row = b_row_of(r, up);
       pq[i] = (up ? Q2 : Q) + row * g.ldb + half * 16;
     }
+    if (SR) {
+      bool up;
+      const int64_t row = b_row_of(s_ins * 64 + lane, up);
+      ps = (up ? g.Bs2 : g.Bs) + static_cast<int64_t>(tile.expert) * p.bs_expert_stride + row * sp;
+    }
   }
   const int ktot = g.K / BKP;
 
-  auto issue = [&](bf16_t* As, uint8_t* Qs) {
+  int issued = 0;  // stages issued so far
+  auto issue = [&](bf16_t* As, uint8_t* Qs, uint8_t* Ss) {
 #pragma unroll
     for (int i = 0; i < MA; ++i) {
-      load_lds16_raw(pa[i], As + (wave + 4 * i) * 512);
+      load_lds16_raw(pa[i], As + (wave + NW * i) * 512);
       pa[i] += BKP;
     }
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
-      load_lds16_raw(pq[i], Qs + (wave + 4 * i) * 1024);
+      load_lds16_raw(pq[i], Qs + (wave + NW * i) * 1024);
       pq[i] += BKP / 2;
     }
+    if (SR)  // scale bytes 2kt, 2kt+1 of stage kt sit in the aligned word at (2kt) & ~3
+      load_lds4_asm(ps + ((2 * issued) & ~3), Ss + s_ins * 256);
+    ++issued;
   };
 
   f32x16_t acc[FM][FN];
@@ -823,7 +860,7 @@ __global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Par
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int kt, const bf16_t* As, const uint8_t* Qs) {
+  auto compute = [&](int kt, const bf16_t* As, const uint8_t* Qs, const uint8_t* Ss) {
     const int hi = lane >> 5, sw = lane & 7;
     u32x4_t q[FN];
     float sc[FN];
@@ -831,7 +868,7 @@ __global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Par
     for (int j = 0; j < FN; ++j) {
       const int rb = wn * WTN + j * 32 + (lane & 31);
       q[j] = *reinterpret_cast<const u32x4_t*>(Qs + rb * 32 + ((hi ^ ((rb >> 2) & 1)) * 16));
-      sc[j] = e8m0_to_f32(sP[rb * sp + kt * 2 + hi]);
+      sc[j] = e8m0_to_f32(SR ? Ss[rb * 4 + (kt & 1) * 2 + hi] : sP[rb * sp + kt * 2 + hi]);
     }
 #pragma unroll
     for (int kk = 0; kk < BKP / 16; ++kk) {
@@ -852,23 +889,24 @@ __global__ __launch_bounds__(NTHREADS, BM >= 160 ? 1 : 2) void gemm_pipe_fp4(Par
 
   // the panel's LDS writes complete before the first barrier of the ring
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  if (ktot > 0) issue(sA0, sQ0);
-  if (ktot > 1) issue(sA1, sQ1);
-  auto ring = [&](int kt, bf16_t* Ac, uint8_t* Qc, bf16_t* An, uint8_t* Qn) {
+  if (ktot > 0) issue(sA0, sQ0, sS0);
+  if (ktot > 1) issue(sA1, sQ1, sS1);
+  auto ring = [&](int kt, bf16_t* Ac, uint8_t* Qc, uint8_t* Sc, bf16_t* An, uint8_t* Qn,
+                  uint8_t* Sn) {
     if (kt < ktot) {
       if (kt + 1 < ktot)
-        wait_vmcnt<MA + MQ>();
+        wait_vmcnt<MA + MQ + MS>();
       else
         wait_vmcnt<0>();
       lds_barrier();
-      if (kt + 2 < ktot) issue(An, Qn);
-      compute(kt, Ac, Qc);
+      if (kt + 2 < ktot) issue(An, Qn, Sn);
+      compute(kt, Ac, Qc, Sc);
     }
   };
   for (int kt = 0; kt < ktot; kt += STAGES) {
-    ring(kt, sA0, sQ0, sA2, sQ2);
-    ring(kt + 1, sA1, sQ1, sA0, sQ0);
-    ring(kt + 2, sA2, sQ2, sA1, sQ1);
+    ring(kt, sA0, sQ0, sS0, sA2, sQ2, sS2);
+    ring(kt + 1, sA1, sQ1, sS1, sA0, sQ0, sS0);
+    ring(kt + 2, sA2, sQ2, sS2, sA1, sQ1, sS1);
   }
 
 #pragma unroll
@@ -1170,11 +1208,12 @@ static int dispatch_pipe(const Params& p, int epi, hipStream_t s) {
   }
 }
 
-// Static LDS of the MXFP4 kernel, and the LDS a block may use in all (two
+// Static LDS of the MXFP4 kernel (an upper bound: 1 KB is left for the
+// placement of the small arrays), and the LDS a block may use in all (two
 // blocks per CU up to 128-row tiles, one block per CU for taller tiles).
 template <int BM, int BN>
 constexpr size_t fp4_static_lds() {
-  return static_cast<size_t>(3) * (BM * 64 * 2 + BN * 32);
+  return static_cast<size_t>(3) * (BM * 64 * 2 + BN * 32) + 1024;
 }
 template <int BM>
 constexpr size_t fp4_lds_budget() {
@@ -1186,12 +1225,15 @@ size_t fp4_tall_tile_fits(int K) {
                              fp4_lds_budget<160>();
 }
 
+bool fp4_tile320_fits(int K) { return K > 0 && K % 128 == 0; }
+
 // Returns 1 when the shape does not fit the pipelined MXFP4 kernel (the caller
-// then uses the register-staged kernel).
-template <int BM, int BN, int WM, int EPI>
+// then uses the register-staged kernel).  SR: scales through the ring (K a
+// multiple of 128, so that every stage's scale word lies inside its row).
+template <int BM, int BN, int WM, int EPI, int NW = 4, bool SR = false>
 static int run_pipe_fp4(const Params& p, hipStream_t stream) {
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
-  if (p.nseg != 1 || p.seg[0].K % 512 != 0) return 1;
+  if (p.nseg != 1 || p.seg[0].K % (SR ? 128 : 512) != 0) return 1;
   const Seg& g = p.seg[0];
   const uintptr_t align = reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B) |
                           reinterpret_cast<uintptr_t>(g.B2) | reinterpret_cast<uintptr_t>(g.Bs) |
@@ -1199,7 +1241,7 @@ static int run_pipe_fp4(const Params& p, hipStream_t stream) {
                           static_cast<uintptr_t>(g.lda * 2) | static_cast<uintptr_t>(p.b_expert_stride) |
                           static_cast<uintptr_t>(p.bs_expert_stride);
   if (align % 16 != 0) return 1;
-  const size_t panel = static_cast<size_t>(BN) * (p.seg[0].K / 32);
+  const size_t panel = SR ? 0 : static_cast<size_t>(BN) * (p.seg[0].K / 32);
   if (fp4_static_lds<BM, BN>() + panel > fp4_lds_budget<BM>()) return 1;
   const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
   const int mt = p.tiles ? p.max_mtiles : (p.M + BM - 1) / BM;
@@ -1207,16 +1249,16 @@ static int run_pipe_fp4(const Params& p, hipStream_t stream) {
   if (G <= 0) return MOE_OK;
   const int64_t G8 = (G + 7) / 8 * 8;
   static bool configured = false;
-  if (!configured) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI>),
+  if (!SR && !configured) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(fp4_lds_budget<BM>() - fp4_static_lds<BM, BN>())) !=
         hipSuccess)
       return MOE_EHIP;
     configured = true;
   }
-  hipLaunchKernelGGL((gemm_pipe_fp4<BM, BN, WM, EPI>), dim3(static_cast<unsigned>(G8)),
-                     dim3(NTHREADS), panel, stream, p);
+  hipLaunchKernelGGL((gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR>), dim3(static_cast<unsigned>(G8)),
+                     dim3(64 * NW), panel, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -1308,6 +1350,16 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
   // decoded per fragment; shapes outside that kernel's limits use the
   // register-staged kernel that decodes while writing LDS
   int rc = 1;
+  if (bm_hint == 320) {
+    // 320-row tiles, 8 waves, scales through the ring
+    if (epi == EPI_SITU)
+      rc = run_pipe_fp4<320, 256, 2, EPI_SITU, 8, true>(p, stream);
+    else if (epi == EPI_BF16)
+      rc = run_pipe_fp4<320, 256, 2, EPI_BF16, 8, true>(p, stream);
+    else if (epi == EPI_F32)
+      rc = run_pipe_fp4<320, 256, 2, EPI_F32, 8, true>(p, stream);
+    return rc == 1 ? MOE_EUNSUPPORTED : rc;
+  }
   if (bm_hint == 160) {
     // tiles were cut 160 rows tall: only the pipelined kernel takes them
     if (epi == EPI_SITU)

@@ -57,6 +57,9 @@ size_t splitk_bytes(int M, int N, int K, int epi);
 // Whether the pipelined MXFP4 kernel takes 160-row tiles for this K.
 size_t fp4_tall_tile_fits(int K);
 
+// Whether the 320-row MXFP4 kernel (scales through the ring) takes this K.
+bool fp4_tile320_fits(int K);
+
 // bm_hint of a dense product that runs on another stream beside the
 // latency-bound routing kernels: 128 x 128 tiles held to one block per CU, so
 // that those kernels' blocks find registers and LDS on every CU.

@@ -217,8 +217,12 @@ static int grouped_bm(const moe_shape_t& s) {
   if (s.act_dtype != MOE_BF16) return 64;
   if (avg <= 32) return 32;
   if (s.routed_dtype == MOE_MXFP4) {
-    // MFMA-bound: 160-row tiles (5 x 2 fragments per wave) when the
-    // pipelined MXFP4 kernel takes both K widths
+    // MFMA-bound: 320-row tiles on 8 waves for 161 - 320 rows per expert,
+    // else 160-row tiles (5 x 2 fragments per wave), when the pipelined
+    // MXFP4 kernels take both K widths
+    if (avg > 160 && avg <= 320 && gemm::fp4_tile320_fits(s.latent) &&
+        gemm::fp4_tile320_fits(s.inter))
+      return 320;
     if (gemm::fp4_tall_tile_fits(s.latent) && gemm::fp4_tall_tile_fits(s.inter)) return 160;
     return 128;
   }

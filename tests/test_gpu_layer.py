@@ -65,15 +65,19 @@ def test_mxfp4_layer():
 
 
 # Widths that are multiples of 512 take the pipelined MXFP4 kernel (scale
-# panel in LDS); the others take the register-staged one.  Cases cover the
-# tile shapes (few rows per expert: 32 x 256; many: 160 x 256), row and
-# column tails.
+# panel in LDS); the others take the register-staged one, except for 161 -
+# 320 rows per expert, where widths that are multiples of 128 take the
+# 320-row kernel (8 waves, scales through the ring).  Cases cover the tile
+# shapes (few rows per expert: 32 x 256; many: 160 x 256 and 320 x 256), row
+# and column tails.
 @pytest.mark.parametrize("kw", [
     dict(T=300, k=4, d=1024, latent=512, m=512),              # 32x256 tiles, both GEMMs
     dict(T=300, k=4, d=1024, latent=512, m=576),              # gate/up column tail
     dict(T=300, k=4, d=1024, latent=640, m=512),              # down column tail
     dict(T=640, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 160-row tiles, full
-    dict(T=700, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 160-row tiles + 15-row tail
+    dict(T=700, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # one 320-row tile, 175 rows
+    dict(T=1200, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # one 320-row tile, 300 rows
+    dict(T=1000, n=16, k=4, d=1024, latent=640, m=512, shared=256),  # 320 rows, 20 scale bytes per row
 ])
 def test_mxfp4_layer_pipelined(kw):
     check_layer(workloads.small_shape(routed="mxfp4", **kw), seed=5, name=f"mxfp4 {kw}")
@@ -89,6 +93,15 @@ def test_bf16_layer_frozen_bias():
     shape = workloads.small_shape(T=120)
     bias = np.rint(np.random.default_rng(4).normal(0, 0.1, shape.n) * 2.0 ** 40) * 2.0 ** -40
     check_layer(shape, seed=4, qb_mode=qb.MODE_FROZEN, bias=bias, name="bf16 frozen")
+
+
+def test_mxfp4_layer_frozen_uneven_320_row_tiles():
+    # skewed router, frozen zero bias: loads from tens to several hundred
+    # rows per expert on 320-row MXFP4 tiles (up to three tiles per expert)
+    shape = workloads.small_shape(routed="mxfp4", T=1000, n=16, k=4, d=1024, latent=512, m=512,
+                                  shared=256, offset_std=1.0)
+    check_layer(shape, seed=9, qb_mode=qb.MODE_FROZEN, bias=np.zeros(shape.n),
+                name="mxfp4 frozen, uneven 320-row tiles")
 
 
 def test_bf16_layer_frozen_uneven_tall_tiles():
