@@ -1086,7 +1086,11 @@ static DensePlan plan_dense(int M, int N, int K, int epi) {
   } else if (M <= 64) {
     d.cfg = 1; d.bm = 64; d.bn = 256; d.bkp = 64; target = 256;
   } else if (M >= 256 && epi != EPI_SIGMOID && tiles_of(M, N, 256, 256, epi) >= 256) {
-    // large products: 128 x 128 per wave (0.5 KB of LDS reads per MFMA)
+    // large products: 128 x 64 per wave, 8 waves
+    d.cfg = 4; d.bm = 256; d.bn = 256; d.bkp = 32; target = 256;
+  } else if (M >= 1024 && epi == EPI_SIGMOID) {
+    // the router (few columns, K = 3 d): 256 x 256 tiles, split along K
+    // until they fill the chip
     d.cfg = 4; d.bm = 256; d.bn = 256; d.bkp = 32; target = 256;
   } else if (M >= 256 && tiles_of(M, N, 256, 128, epi) >= 256) {
     d.cfg = 3; d.bm = 256; d.bn = 128; d.bkp = 32; target = 512;
