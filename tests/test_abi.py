@@ -88,3 +88,68 @@ def test_sign_route_validation_on_host():
     assert lib.moe_route_sign(*args(100, 64, 4, step=2.0 ** 11)) == -1    # beyond the bias range
     assert lib.moe_route_sign(*args(100, 64, 4, rounds=-1)) == -1
     assert lib.moe_route_sign(*args(100, 64, 4, ws=None)) == -1
+
+
+def _shape(moe, **kw):
+    base = dict(T=4096, d=7168, latent=3584, n=896, k=16, m=2048, shared=6144,
+                act=moe.MOE_BF16, routed=moe.MOE_BF16, eps=1e-6, mode=moe.MOE_QB_BATCH, rounds=64)
+    base.update(kw)
+    return moe.MoeShape(base["T"], base["d"], base["latent"], base["n"], base["k"], base["m"],
+                        base["shared"], base["act"], base["routed"], base["eps"], base["mode"],
+                        base["rounds"])
+
+
+def test_forward_workspace_sizing_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    ws = lambda **kw: lib.moe_forward_workspace_bytes(ctypes.byref(_shape(moe, **kw)))
+    # the K3 prefill batch: scores, routed rows h (bf16) and y (fp32) dominate
+    T, k, n, m, L = 4096, 16, 896, 2048, 3584
+    need = ws()
+    floor = T * n * 4 + T * k * (m * 2 + L * 4)
+    assert floor <= need <= floor + (1 << 30)
+    assert ws(T=8192) > need > ws(T=64) > 0
+    assert ws(T=0) > 0                               # an empty batch is valid
+    assert ws(routed=moe.MOE_MXFP4) > 0
+    assert ws(act=moe.MOE_F32, routed=moe.MOE_F32) > 0
+    # shapes the library does not take: size 0
+    assert ws(d=7168 + 32) == 0                      # widths must be multiples of 64
+    assert ws(latent=4096 + 64) == 0                 # latent above 4096
+    assert ws(k=n + 1) == 0
+    assert ws(n=2048) == 0
+    assert ws(act=moe.MOE_F32, routed=moe.MOE_MXFP4) == 0
+    assert ws(act=moe.MOE_F32, routed=moe.MOE_BF16) == 0
+    assert ws(mode=5) == 0
+
+
+def test_forward_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)                  # never dereferenced: validation fails first
+    names = [f[0] for f in moe.MoeWeights._fields_]
+    full = moe.MoeWeights(*[fake] * len(names))
+    sh = _shape(moe, T=64, d=256, latent=128, n=32, k=4, m=64, shared=128)
+    need = lib.moe_forward_workspace_bytes(ctypes.byref(sh))
+    assert need > 0
+
+    def call(shape=sh, weights=full, x=fake, out=fake, bias=fake, ws=fake, wsb=need):
+        return lib.moe_latent_forward(ctypes.byref(shape), ctypes.byref(weights), x, out, bias,
+                                      None, None, None, None, None, None, ws, wsb, None)
+
+    assert call(wsb=need - 1) == -3                  # workspace too small
+    assert call(ws=ctypes.c_void_p((1 << 20) + 64)) == -1   # workspace not 256-byte aligned
+    assert call(ws=None) == -1
+    assert call(bias=None) == -1
+    assert call(x=None) == -1
+    assert call(out=None) == -1
+    for name in ("w_router", "w_down", "w_up", "w_gate", "w_uproj", "w_dn", "rms_gamma",
+                 "ws_gate", "ws_up", "ws_down"):
+        w = moe.MoeWeights(*[None if f == name else fake for f in names])
+        assert call(weights=w) == -1, name
+    # MXFP4 routed weights need their E8M0 scales
+    mx = _shape(moe, T=64, d=256, latent=128, n=32, k=4, m=64, shared=128, routed=moe.MOE_MXFP4)
+    need_mx = lib.moe_forward_workspace_bytes(ctypes.byref(mx))
+    no_scales = moe.MoeWeights(*[None if f in ("s_gate", "s_uproj", "s_dn") else fake
+                                 for f in names])
+    assert call(shape=mx, weights=no_scales, wsb=need_mx) == -1
+    assert call(shape=_shape(moe, T=64, d=250, latent=128, n=32, k=4, m=64, shared=128)) == -2
