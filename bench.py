@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0
 TRAFFIC = {"k3_prefill": 27.019e9,      # gemm_pipe<96, 256, 1, SITU, 64, 3, nt>
            "k3_decode": 26.312e9,       # gemm_pipe<32, 256, 1, SITU, 64, 3, nt>
            "k3_mxfp4": 9.928e9,         # gemm_pipe_fp4<320, 256, 2, SITU, 8 waves, scale ring>
-           "k3_prefill_16k": 29.243e9}  # gemm_pipe<320, 256, 2, SITU, 32, 3, 8 waves>
+           "k3_prefill_16k": 29.243e9}  # gemm_pipe<320, 256, 2, SITU, 64, 2, nt, 8 waves>
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
 
 
