@@ -468,9 +468,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
   constexpr int SW = (BM + BN) * BKP;
   __shared__ __attribute__((aligned(1024))) bf16_t st0[SW];
   __shared__ __attribute__((aligned(1024))) bf16_t st1[SW];
-  __shared__ __attribute__((aligned(1024))) bf16_t st2[SW];
   // (unused stages are 16-byte stubs, so a 160 KB ring is not pushed over
   // the limit by alignment padding)
+  __shared__ __attribute__((aligned(NST >= 3 ? 1024 : 16))) bf16_t st2[NST >= 3 ? SW : 8];
   __shared__ __attribute__((aligned(NST >= 4 ? 1024 : 16))) bf16_t st3[NST >= 4 ? SW : 8];
   __shared__ __attribute__((aligned(NST >= 5 ? 1024 : 16))) bf16_t st4[NST >= 5 ? SW : 8];
   __shared__ __attribute__((aligned(NST >= 6 ? 1024 : 16))) bf16_t st5[NST >= 6 ? SW : 8];
