@@ -25,13 +25,14 @@ Steps, in the pages' order:
    intermediate 6144 at full width, added to the routed output
    ([K3-structure-5] Q&A on the shared expert).
 
-Readings (also in the design doc): the projections carry no bias terms; the shared
+Readings: the projections carry no bias terms; the shared
 MLP uses SiTU-GLU too (``hidden_act: situ`` is model-wide); RMSNorm eps = 1e-6
 with gain gamma; routed scaling factor 1.
 
-Parity status: sigmoid, SiTU-GLU, RMSNorm, MXFP4 decoding and the shared-MLP
-merge are pinned by tests (closed forms, bounds, identities, the OCP code
-table); the composition of the whole layer is "parity unpinned" beyond those
+Parity status: sigmoid, SiTU-GLU, RMSNorm, MXFP4 decoding, the MXFP8 (E4M3)
+activation codec of the W4A8 experts and the shared-MLP merge are pinned by
+tests (closed forms, bounds, identities, the OCP code tables, brute-force
+nearest values); the composition of the whole layer is "parity unpinned" beyond those
 component pins, since the pages print no worked example.
 """
 from __future__ import annotations
@@ -94,6 +95,84 @@ def mxfp4_decode(codes, scales):
     return val * np.repeat(scale, 32, axis=1)
 
 
+# MXFP8 activations (OCP Microscaling v1.0: E4M3 elements, one E8M0 scale per
+# 32 consecutive elements of a row).  The W4A8 reading of the pages' MXFP4
+# deployment of the routed experts ([Stable-LatentMoE] "Key Components" item 4;
+# [K3-structure-5] 延伸解读 on MXFP4 deployment) quantises the experts' inputs,
+# the latent rows z and the SiTU-GLU outputs h, to this format as well.
+E4M3_MAX = 448.0           # 1.75 * 2^8, the largest finite E4M3 value
+E4M3_EMAX = 8              # exponent of the largest power of two in E4M3
+
+
+def e4m3_decode(codes):
+    """E4M3 codes -> float64: sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    v = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return np.where(c >> 7 == 1, -v, v)
+
+
+def e4m3_encode(q):
+    """Round float64 values to the nearest E4M3 value (ties to the even
+    mantissa), saturating at +-448; the sign bit follows the sign of q."""
+    q = np.asarray(q, np.float64)
+    a = np.minimum(np.abs(q), E4M3_MAX)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    E = np.maximum(ex - 1, -6)                  # exponent of the value's binade (subnormals: -6)
+    quantum = np.ldexp(1.0, E - 3)              # 3 mantissa bits
+    r = np.rint(a / quantum) * quantum          # round half to even
+    _, ex_r = np.frexp(np.where(r > 0, r, 1.0))
+    Er = ex_r - 1
+    normal = r >= 2.0 ** -6
+    mant = np.where(normal, np.rint(r / np.ldexp(1.0, Er) * 8) - 8, np.rint(r / 2.0 ** -9))
+    code = np.where(normal, ((Er + 7) << 3) + mant, mant).astype(np.int64)
+    return (code | np.where(np.signbit(q), 0x80, 0)).astype(np.uint8)
+
+
+def mxfp8_quantize(v):
+    """Rows of float64 values [rows, K] (K a multiple of 32) -> (E4M3 codes
+    [rows, K], E8M0 scales [rows, K/32]).  Per block: shared exponent
+    floor(log2 amax) - 8, stored biased by 127 and clamped to [0, 254] (an
+    all-zero block takes 0); elements v / 2^X rounded by :func:`e4m3_encode`."""
+    v = np.asarray(v, np.float64)
+    rows, K = v.shape
+    blk = v.reshape(rows, K // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.where(amax > 0, ex - 1 - E4M3_EMAX, -127)
+    sb = np.clip(X + 127, 0, 254).astype(np.uint8)
+    q = blk / np.ldexp(1.0, sb.astype(np.int64) - 127)[:, :, None]
+    return e4m3_encode(q).reshape(rows, K), sb
+
+
+def mxfp8_decode(codes, scales):
+    codes = np.asarray(codes, np.uint8)
+    rows, K = codes.shape
+    sc = np.ldexp(1.0, np.asarray(scales, np.int64) - 127)
+    return e4m3_decode(codes) * np.repeat(sc, 32, axis=1)
+
+
+def mxfp8_round(v):
+    """Quantise to MXFP8 and decode."""
+    return mxfp8_decode(*mxfp8_quantize(v))
+
+
+def bf16_round(v):
+    """float64 -> nearest float32 -> nearest bfloat16 (both ties to even), as float64."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(v, np.float64).astype(np.float32))
+    return t.bfloat16().double().numpy()
+
+
+def w4a8_activation(v):
+    """What a W4A8 expert reads: the activation in its bf16 storage format,
+    quantised to MXFP8 (the reading taken for W4A8: activations are quantised
+    from the bf16 values the layer stores)."""
+    return mxfp8_round(bf16_round(v))
+
+
 def as_f64(t):
     """torch tensor / ndarray (fp32, bf16) -> float64 ndarray."""
     if hasattr(t, "detach"):
@@ -130,11 +209,15 @@ def route_layer(inp, k, mode=qb.MODE_BATCH, bias=None):
     return r
 
 
-def layer_forward(inp, idx, w, eps, tokens=None):
+def layer_forward(inp, idx, w, eps, tokens=None, act_mxfp8=False):
     """Layer output (float64) for the given routing ``idx``/``w`` [T, k].
 
     ``tokens`` restricts the computation to those token rows (experts are
     decoded one at a time, so full-size layers can be sampled).
+    ``act_mxfp8``: W4A8 experts -- the latent rows z entering the routed
+    experts and the SiTU-GLU outputs h entering their down-projections are
+    rounded to bf16 (their storage format) and then to MXFP8 (per row,
+    blocks of 32 along the row).
     """
     x = as_f64(inp["x"])
     T = x.shape[0]
@@ -149,8 +232,10 @@ def layer_forward(inp, idx, w, eps, tokens=None):
         wg = expert_matrix(inp["w_gate"], int(e))
         wu = expert_matrix(inp["w_uproj"], int(e))
         wd = expert_matrix(inp["w_dn"], int(e))
-        ze = z[rows]
+        ze = w4a8_activation(z[rows]) if act_mxfp8 else z[rows]
         h = situ_glu(ze @ wg.T, ze @ wu.T)
+        if act_mxfp8:
+            h = w4a8_activation(h)
         y[rows] += w_s[rows, slots][:, None] * (h @ wd.T)
     yn = rmsnorm(y, as_f64(inp["rms_gamma"]), eps)
     out = yn @ as_f64(inp["w_up"]).T

@@ -19,7 +19,7 @@ What the pages fix
   DeepSeek-V3's fixed-step sign update is SignSGD on the same dual
   ([K3-structure-5] 延伸解读 "Quantile Balancing与DeepSeek-V3路由的异同").
 
-Readings taken where the pages are open (each is listed in the design doc)
+Readings taken where the pages are open
 --------------------------------------------------------------------
 1. Exact arithmetic.  Scores are fp32; ``sfx = rint(s * 2^40)`` is exact for
    s >= 2^-17.  A bias is an int64 on the same 2^-40 grid.  The comparison

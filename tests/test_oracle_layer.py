@@ -143,3 +143,90 @@ def test_router_scores_with_zero_input_are_sigmoid_of_offset():
     s = layer.router_scores(np.zeros((2, 4)), np.ones((3, 4)), p)
     assert s.dtype == np.float32
     assert np.allclose(s, 1 / (1 + np.exp(-p))[None, :], rtol=1e-7)
+
+
+# --- MXFP8 (E4M3) activations of the W4A8 experts: OCP Microscaling v1.0 ---
+
+def test_e4m3_code_table():
+    c = np.arange(256, dtype=np.uint8)
+    v = layer.e4m3_decode(c)
+    # the format's landmarks: smallest subnormal 2^-9, smallest normal 2^-6,
+    # one (0x38), largest finite 448 = 1.75 * 2^8, NaN at S.1111.111 only
+    assert v[0x00] == 0 and v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x39] == 1.125 and v[0x3C] == 1.5
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0
+    assert np.isnan(v[[0x7F, 0xFF]]).all() and np.isnan(v).sum() == 2
+    assert (np.diff(v[:0x7F]) > 0).all()                     # positive codes increase
+    assert (v[0x80:0xFF] == -v[:0x7F]).all()                 # the sign bit only negates
+    fin = ~np.isnan(v)
+    assert (layer.e4m3_encode(v[fin]) == c[fin]).all()       # every finite value round-trips
+
+
+def test_e4m3_rounding_ties_and_saturation():
+    enc = layer.e4m3_encode
+    # ties between neighbours go to the even mantissa
+    assert enc(np.array([1.0625]))[0] == 0x38 and enc(np.array([1.1875]))[0] == 0x3A
+    assert enc(np.array([2.0 ** -10]))[0] == 0x00 and enc(np.array([3 * 2.0 ** -10]))[0] == 0x02
+    # just off a tie rounds to the nearer value
+    assert enc(np.array([1.0625 + 1e-9]))[0] == 0x39
+    # saturation at 448 instead of overflow to NaN
+    assert (layer.e4m3_decode(enc(np.array([449.0, 464.0, 1e6, -1e6]))) == [448, 448, 448, -448]).all()
+    # brute force: the encoded value is a nearest finite E4M3 value
+    grid = layer.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    x = np.random.default_rng(0).uniform(0, 448, 20000) * 2.0 ** np.random.default_rng(1).integers(-14, 1, 20000)
+    r = layer.e4m3_decode(enc(x))
+    best = np.abs(grid[None, :] - x[:, None]).min(axis=1)
+    assert np.array_equal(np.abs(r - x), best)
+
+
+def test_mxfp8_block_scale_rule_and_error_bound():
+    rng = np.random.default_rng(2)
+    v = rng.normal(0, 1, (64, 256)) * np.exp(rng.normal(0, 3, (64, 1)))
+    v[3, 32:64] = 0.0                                       # an all-zero block
+    codes, sb = layer.mxfp8_quantize(v)
+    assert codes.shape == v.shape and sb.shape == (64, 8)
+    amax = np.abs(v.reshape(64, 8, 32)).max(axis=2)
+    nz = amax > 0
+    # shared exponent floor(log2 amax) - 8: the block maximum lands in [2^8, 2^9)
+    X = sb.astype(np.int64) - 127
+    assert ((amax[nz] >= 2.0 ** (X[nz] + 8)) & (amax[nz] < 2.0 ** (X[nz] + 9))).all()
+    assert sb[3, 1] == 0 and (codes[3, 32:64] == 0).all()
+    d = layer.mxfp8_decode(codes, sb)
+    # error bound: half a unit in the last place, relative 2^-4 for normals, and
+    # the saturation of block maxima in (448, 512) * 2^X
+    ulp = np.maximum(np.abs(v), np.repeat(2.0 ** (X + 2), 32, axis=1))
+    sat = np.abs(v) > 448 * np.repeat(2.0 ** X, 32, axis=1)
+    assert (np.abs(d - v)[~sat] <= ulp[~sat] * 2.0 ** -4 + 1e-300).all()
+    assert (np.abs(d[sat]) == 448 * np.repeat(2.0 ** X, 32, axis=1)[sat]).all()
+    # exactly representable blocks come back unchanged
+    grid = layer.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    w = rng.choice(grid[grid > 0], (8, 64)) * 2.0 ** -5
+    w[:, ::32] = 256 * 2.0 ** -5                              # block maximum 2^8 * 2^X
+    assert np.array_equal(layer.mxfp8_round(w), w)
+
+
+def test_w4a8_layer_moves_by_the_activation_rounding():
+    shape = workloads.small_shape(routed="mxfp4", T=48, k=4, n=16, d=256, latent=128, m=128,
+                                  shared=128)
+    inp = workloads.layer_inputs(shape, "cpu", seed=4)
+    s = layer.router_scores(layer.as_f64(inp["x"]), layer.as_f64(inp["w_router"]),
+                            layer.as_f64(inp["logit_offset"]))
+    r = qb.route_qb(s, shape.k)
+    a16 = layer.layer_forward(inp, r["idx"], r["w"], shape.eps)
+    a8 = layer.layer_forward(inp, r["idx"], r["w"], shape.eps, act_mxfp8=True)
+    # E4M3 rounding (ties to even) leaves a relative error uniform within
+    # +-2^-4 of each element of z and h: rms 2^-4 / sqrt(3) = 3.6% each.  The
+    # routed half of the output moves by about that much; rms(a8 - a16) / rms(a16)
+    # must lie well inside (0.5%, 8%)
+    rel_rms = np.sqrt(np.mean((a8 - a16) ** 2) / np.mean(a16 ** 2))
+    assert 0.005 < rel_rms < 0.08
+    # no rounding at all when the activations already sit on the MXFP8 grid
+    z = layer.as_f64(inp["x"]) @ layer.as_f64(inp["w_down"]).T
+    q = layer.w4a8_activation(z)
+    assert np.array_equal(layer.w4a8_activation(q), q)
+
+
+def test_bf16_round_ties_to_even():
+    # 1 + 2^-8 is halfway between bf16 neighbours 1 and 1 + 2^-7: ties to even (1)
+    v = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)])
+    assert np.array_equal(layer.bf16_round(v), [1.0, 1.0 + 2.0 ** -6, -1.0])
