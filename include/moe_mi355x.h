@@ -64,7 +64,15 @@ typedef enum {
   MOE_EHIP = -4           /* a HIP runtime call or kernel launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_MXFP4 = 2,    /* routed weights: E2M1 codes + E8M0 scales per 32 (bf16 activations) */
+  MOE_MXFP4_A8 = 3  /* routed weights as MOE_MXFP4; the routed experts' inputs z and h are
+                       quantised on the fly from bf16 to MXFP8 (E4M3 + E8M0 per 32) and
+                       multiplied with gfx950's scaled MFMA (W4A8).  latent and inter must be
+                       multiples of 128 (else MOE_EUNSUPPORTED) */
+} moe_dtype;
 
 typedef enum {
   MOE_QB_FROZEN = 0,  /* use the given bias as is (inference: bias frozen) */
@@ -85,7 +93,7 @@ typedef struct {
   int32_t inter;         /* routed intermediate width m, multiple of 64 */
   int32_t shared_inter;  /* merged shared-expert intermediate (2 x 3072), multiple of 64 */
   int32_t act_dtype;     /* MOE_F32 or MOE_BF16: x, out and the dense weights */
-  int32_t routed_dtype;  /* act_dtype, or MOE_MXFP4 with MOE_BF16 activations */
+  int32_t routed_dtype;  /* act_dtype, or MOE_MXFP4 / MOE_MXFP4_A8 with MOE_BF16 activations */
   float rms_eps;         /* RMSNorm epsilon (1e-6) */
   int32_t qb_mode;       /* moe_qb_mode */
   int32_t qb_max_rounds; /* cap on quantile coordinate rounds (<= 0: 64) */

@@ -21,7 +21,7 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python sparse_moe_ffn_sigmoid_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
-MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_MXFP4, MOE_MXFP4_A8 = 0, 1, 2, 3
 MOE_QB_FROZEN, MOE_QB_BATCH = 0, 1
 EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_route_sign",
             "moe_forward_workspace_bytes",
@@ -185,7 +185,7 @@ def latent_forward(shape: MoeShape, weights: dict, x: torch.Tensor, bias=None,
         _check(weights["router_logit_offset"], "router_logit_offset", torch.float32, (n,), dev)
     _check(weights["w_down"], "w_down", adt, (l, d), dev)
     _check(weights["w_up"], "w_up", adt, (d, l), dev)
-    if shape.routed_dtype == MOE_MXFP4:
+    if shape.routed_dtype in (MOE_MXFP4, MOE_MXFP4_A8):
         for nm, sn, rows, K in (("w_gate", "s_gate", m, l), ("w_uproj", "s_uproj", m, l),
                                 ("w_dn", "s_dn", l, m)):
             _check(weights[nm], nm, torch.uint8, (n, rows, K // 2), dev)

@@ -551,7 +551,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
     const bf16_t* B2 = static_cast<const bf16_t*>(g.B2) +
                        static_cast<int64_t>(tile.expert) * p.b_expert_stride + skip;
 #pragma unroll
-    for (int i = 0; i < MA; ++i) pa[i] = A + a_off[i] * g.lda + a_chunk[i] * 8;
+    for (int i = 0; i < MA; ++i)
+      pa[i] = A + a_off[i] * g.lda + a_chunk[i] * 8;
 #pragma unroll
     for (int i = 0; i < MB; ++i) pb[i] = (b_up[i] ? B2 : B) + b_off[i] * g.ldb + b_chunk[i] * 8;
   };
@@ -728,8 +729,13 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 // per B row per stage: the scale bytes of this stage and its neighbour)
 // instead of a per-block panel of the whole K range, which leaves room for
 // 320-row tiles at any K.
-template <int BM, int BN, int WM, int EPI, int NW, bool SR>
+// A8 (with SR): A holds MXFP8 codes (one byte per element, 64 bytes per row
+// and stage, 16-byte chunks XOR-swizzled by (row / 2) mod 4) and its E8M0
+// scales travel through the ring like B's; one scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4) per fragment pair and stage.
+template <int BM, int BN, int WM, int EPI, int NW, bool SR, bool A8 = false>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_pipe_fp4(Params p) {
+  static_assert(!A8 || SR, "MXFP8 A needs the scale ring");
   constexpr int BKP = 64;
   constexpr int NTH = 64 * NW;
   constexpr int WN = NW / WM;
@@ -738,19 +744,29 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold 32x32 blocks");
   static_assert(EPI != EPI_SITU || FN % 2 == 0, "SiTU needs gate/up fragment pairs");
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
-  constexpr int NA = BM / 8, NQ = BN / 32;
-  static_assert(NA * 8 == BM && NQ * 32 == BN, "tile rows per instruction");
-  constexpr int MA = NA / NW, MQ = NQ / NW;
-  static_assert(NA % NW == 0 && NQ % NW == 0, "uniform load instructions per wave");
+  // A: 8 rows of 128 bytes (bf16) or 16 rows of 64 bytes (E4M3) per instruction
+  constexpr int A_RPI = A8 ? 16 : 8;
+  constexpr int NA = BM / A_RPI, NQ = BN / 32;
+  static_assert(NA * A_RPI == BM && NQ * 32 == BN, "tile rows per instruction");
+  constexpr int MA = (NA + NW - 1) / NW, MQ = NQ / NW;
+  static_assert(NA >= NW && NQ % NW == 0, "uniform load instructions per wave");
+  // surplus A instructions repeat the wave's own instruction i-1
+  auto a_ins = [](int w, int i) { const int x = w + NW * i; return x < NA ? x : x - NW; };
+  // A scales: 64 rows per instruction, waves past them repeat a neighbour's
+  constexpr int NSA = A8 ? (BM + 63) / 64 : 1;
+  static_assert(!A8 || NSA <= NW, "one A scale instruction per wave");
   // scale ring: one 4-byte piece per B row and stage, 64 rows per instruction;
   // waves past the BN / 64 that are needed repeat a neighbour's instruction
   constexpr int NS = BN / 64;
-  constexpr int MS = SR ? 1 : 0;
+  constexpr int MS = (SR ? 1 : 0) + (A8 ? 1 : 0);
   static_assert(!SR || (NS <= NW && NS * 64 == BN), "one scale instruction per wave");
 
-  __shared__ __attribute__((aligned(1024))) bf16_t sA0[BM * BKP];
-  __shared__ __attribute__((aligned(1024))) bf16_t sA1[BM * BKP];
-  __shared__ __attribute__((aligned(1024))) bf16_t sA2[BM * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA0[A8 ? BM * BKP / 2 : BM * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA1[A8 ? BM * BKP / 2 : BM * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA2[A8 ? BM * BKP / 2 : BM * BKP];
+  __shared__ __attribute__((aligned(16))) uint8_t sT0[A8 ? NSA * 256 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sT1[A8 ? NSA * 256 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sT2[A8 ? NSA * 256 : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ0[BN * 32];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ1[BN * 32];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ2[BN * 32];
@@ -803,8 +819,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   int a_chunk[MA];
 #pragma unroll
   for (int i = 0; i < MA; ++i) {
-    int r = (wave + NW * i) * 8 + (lane >> 3);
-    a_chunk[i] = (lane & 7) ^ (r & 7);
+    int r;
+    if (A8) {
+      r = a_ins(wave, i) * 16 + (lane >> 2);
+      a_chunk[i] = (lane & 3) ^ ((r >> 1) & 3);
+    } else {
+      r = a_ins(wave, i) * 8 + (lane >> 3);
+      a_chunk[i] = (lane & 7) ^ (r & 7);
+    }
     r = r < tile.rows ? r : 0;
     const int slot = tile.row0 + r;
     a_off[i] = p.a_rows ? p.a_rows[slot] : slot;
@@ -813,12 +835,24 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   const bf16_t* pa[MA];
   const uint8_t* ps = nullptr;  // this lane's scale row (SR)
   const int s_ins = wave % NS;  // scale instruction of this wave (SR)
+  const uint8_t* pt = nullptr;  // this lane's A scale row (A8)
+  const int t_ins = wave % NSA;
+  if (A8) {
+    int r = t_ins * 64 + lane;
+    r = r < tile.rows ? r : 0;
+    const int slot = tile.row0 + r;
+    const int64_t row = p.a_rows ? p.a_rows[slot] : slot;
+    pt = g.As + row * (g.K / 32);
+  }
   {
     const bf16_t* A = static_cast<const bf16_t*>(g.A);
     const uint8_t* Q = static_cast<const uint8_t*>(g.B) + static_cast<int64_t>(tile.expert) * p.b_expert_stride;
     const uint8_t* Q2 = static_cast<const uint8_t*>(g.B2) + static_cast<int64_t>(tile.expert) * p.b_expert_stride;
 #pragma unroll
-    for (int i = 0; i < MA; ++i) pa[i] = A + a_off[i] * g.lda + a_chunk[i] * 8;
+    for (int i = 0; i < MA; ++i)
+      pa[i] = A8 ? reinterpret_cast<const bf16_t*>(reinterpret_cast<const uint8_t*>(g.A) +
+                                                   a_off[i] * g.lda + a_chunk[i] * 16)
+                 : A + a_off[i] * g.lda + a_chunk[i] * 8;
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
       const int r = (wave + NW * i) * 32 + (lane >> 1);
@@ -836,12 +870,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   const int ktot = g.K / BKP;
 
   int issued = 0;  // stages issued so far
-  auto issue = [&](bf16_t* As, uint8_t* Qs, uint8_t* Ss) {
+  auto issue = [&](bf16_t* As, uint8_t* Qs, uint8_t* Ss, uint8_t* Ts) {
 #pragma unroll
     for (int i = 0; i < MA; ++i) {
-      load_lds16_raw(pa[i], As + (wave + NW * i) * 512);
-      pa[i] += BKP;
+      // one instruction fills 1 KB: 8 bf16 rows or 16 E4M3 rows of the stage
+      load_lds16_raw(pa[i], As + a_ins(wave, i) * 512);
+      pa[i] += A8 ? BKP / 2 : BKP;  // bf16_t units
     }
+    if (A8) load_lds4_asm(pt + ((2 * issued) & ~3), Ts + t_ins * 256);
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
       load_lds16_raw(pq[i], Qs + (wave + NW * i) * 1024);
@@ -860,8 +896,41 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int kt, const bf16_t* As, const uint8_t* Qs, const uint8_t* Ss) {
+  auto compute = [&](int kt, const bf16_t* As, const uint8_t* Qs, const uint8_t* Ss,
+                     const uint8_t* Ts) {
     const int hi = lane >> 5, sw = lane & 7;
+    if constexpr (A8) {
+      // lane (r, h): B codes of K [32h, 32h+32), A codes of K [16h, 16h+16)
+      // and [32+16h, 32+16h+16); scale registers of block h on both sides
+      typedef int v8i_t __attribute__((ext_vector_type(8)));
+      v8i_t bq[FN];
+      int sb[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int rb = wn * WTN + j * 32 + (lane & 31);
+        const u32x4_t q = *reinterpret_cast<const u32x4_t*>(Qs + rb * 32 + ((hi ^ ((rb >> 2) & 1)) * 16));
+        bq[j] = v8i_t{static_cast<int>(q[0]), static_cast<int>(q[1]), static_cast<int>(q[2]),
+                      static_cast<int>(q[3]), 0, 0, 0, 0};
+        sb[j] = Ss[rb * 4 + (kt & 1) * 2 + hi];
+      }
+      const uint8_t* Ab = reinterpret_cast<const uint8_t*>(As);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int ra = wm * WTM + i * 32 + (lane & 31);
+        const int s = (ra >> 1) & 3;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(Ab + ra * 64 + ((hi ^ s) * 16));
+        const u32x4_t up = *reinterpret_cast<const u32x4_t*>(Ab + ra * 64 + (((2 + hi) ^ s) * 16));
+        const v8i_t aq = {static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                          static_cast<int>(lo[3]), static_cast<int>(up[0]), static_cast<int>(up[1]),
+                          static_cast<int>(up[2]), static_cast<int>(up[3])};
+        const int sa = Ts[ra * 4 + (kt & 1) * 2 + hi];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq, bq[j], acc[i][j], 0, 4, 0,
+                                                                     sa, 0, sb[j]);
+      }
+      return;
+    }
     u32x4_t q[FN];
     float sc[FN];
 #pragma unroll
@@ -889,24 +958,24 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
 
   // the panel's LDS writes complete before the first barrier of the ring
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  if (ktot > 0) issue(sA0, sQ0, sS0);
-  if (ktot > 1) issue(sA1, sQ1, sS1);
-  auto ring = [&](int kt, bf16_t* Ac, uint8_t* Qc, uint8_t* Sc, bf16_t* An, uint8_t* Qn,
-                  uint8_t* Sn) {
+  if (ktot > 0) issue(sA0, sQ0, sS0, sT0);
+  if (ktot > 1) issue(sA1, sQ1, sS1, sT1);
+  auto ring = [&](int kt, bf16_t* Ac, uint8_t* Qc, uint8_t* Sc, uint8_t* Tc, bf16_t* An,
+                  uint8_t* Qn, uint8_t* Sn, uint8_t* Tn) {
     if (kt < ktot) {
       if (kt + 1 < ktot)
         wait_vmcnt<MA + MQ + MS>();
       else
         wait_vmcnt<0>();
       lds_barrier();
-      if (kt + 2 < ktot) issue(An, Qn, Sn);
-      compute(kt, Ac, Qc, Sc);
+      if (kt + 2 < ktot) issue(An, Qn, Sn, Tn);
+      compute(kt, Ac, Qc, Sc, Tc);
     }
   };
   for (int kt = 0; kt < ktot; kt += STAGES) {
-    ring(kt, sA0, sQ0, sS0, sA2, sQ2, sS2);
-    ring(kt + 1, sA1, sQ1, sS1, sA0, sQ0, sS0);
-    ring(kt + 2, sA2, sQ2, sS2, sA1, sQ1, sS1);
+    ring(kt, sA0, sQ0, sS0, sT0, sA2, sQ2, sS2, sT2);
+    ring(kt + 1, sA1, sQ1, sS1, sT1, sA0, sQ0, sS0, sT0);
+    ring(kt + 2, sA2, sQ2, sS2, sT2, sA1, sQ1, sS1, sT1);
   }
 
 #pragma unroll
@@ -1237,15 +1306,16 @@ bool fp4_tile320_fits(int K) { return K > 0 && K % 128 == 0; }
 // Returns 1 when the shape does not fit the pipelined MXFP4 kernel (the caller
 // then uses the register-staged kernel).  SR: scales through the ring (K a
 // multiple of 128, so that every stage's scale word lies inside its row).
-template <int BM, int BN, int WM, int EPI, int NW = 4, bool SR = false>
+template <int BM, int BN, int WM, int EPI, int NW = 4, bool SR = false, bool A8 = false>
 static int run_pipe_fp4(const Params& p, hipStream_t stream) {
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   if (p.nseg != 1 || p.seg[0].K % (SR ? 128 : 512) != 0) return 1;
   const Seg& g = p.seg[0];
   const uintptr_t align = reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B) |
                           reinterpret_cast<uintptr_t>(g.B2) | reinterpret_cast<uintptr_t>(g.Bs) |
-                          reinterpret_cast<uintptr_t>(g.Bs2) |
-                          static_cast<uintptr_t>(g.lda * 2) | static_cast<uintptr_t>(p.b_expert_stride) |
+                          reinterpret_cast<uintptr_t>(g.Bs2) | reinterpret_cast<uintptr_t>(g.As) |
+                          static_cast<uintptr_t>(g.lda * (A8 ? 1 : 2)) |
+                          static_cast<uintptr_t>(p.b_expert_stride) |
                           static_cast<uintptr_t>(p.bs_expert_stride);
   if (align % 16 != 0) return 1;
   const size_t panel = SR ? 0 : static_cast<size_t>(BN) * (p.seg[0].K / 32);
@@ -1257,14 +1327,14 @@ static int run_pipe_fp4(const Params& p, hipStream_t stream) {
   const int64_t G8 = (G + 7) / 8 * 8;
   static bool configured = false;
   if (!SR && !configured) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, A8>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(fp4_lds_budget<BM>() - fp4_static_lds<BM, BN>())) !=
         hipSuccess)
       return MOE_EHIP;
     configured = true;
   }
-  hipLaunchKernelGGL((gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR>), dim3(static_cast<unsigned>(G8)),
+  hipLaunchKernelGGL((gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, A8>), dim3(static_cast<unsigned>(G8)),
                      dim3(64 * NW), panel, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -1353,6 +1423,17 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
       case EPI_SITU: return run_reduce<EPI_SITU>(q, d, stream);
       default: return MOE_EUNSUPPORTED;
     }
+  }
+  if (bfmt == B_MXFP4_A8) {
+    // W4A8: 320-row tiles on 8 waves, E4M3 A and E2M1 B multiplied by the
+    // scaled MFMA; no other tile height takes these operands
+    if (bm_hint != 320) return MOE_EUNSUPPORTED;
+    int rc8 = 1;
+    if (epi == EPI_SITU)
+      rc8 = run_pipe_fp4<320, 256, 2, EPI_SITU, 8, true, true>(p, stream);
+    else if (epi == EPI_F32)
+      rc8 = run_pipe_fp4<320, 256, 2, EPI_F32, 8, true, true>(p, stream);
+    return rc8 == 1 ? MOE_EUNSUPPORTED : rc8;
   }
   // MXFP4 routed experts: codes straight to LDS, scales in a per-block panel,
   // decoded per fragment; shapes outside that kernel's limits use the

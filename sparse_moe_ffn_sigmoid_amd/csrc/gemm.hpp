@@ -13,7 +13,8 @@ enum Epilogue : int {
   EPI_SITU = 3,     // C (act)  = SiTU-GLU(acc_gate, acc_up); B rows come in gate/up pairs
 };
 
-enum BFormat : int { B_DENSE = 0, B_MXFP4 = 1 };
+// B_MXFP4_A8: MXFP4 B with MXFP8 (E4M3) A codes and E8M0 A scales (W4A8)
+enum BFormat : int { B_DENSE = 0, B_MXFP4 = 1, B_MXFP4_A8 = 2 };
 
 // One K segment: A [rows][K] (K contiguous, leading dim lda), B [N][K] (ldb).
 struct Seg {
@@ -23,6 +24,7 @@ struct Seg {
   const void* B2;  // EPI_SITU: the "up" matrix paired with B (the gate matrix)
   const uint8_t* Bs;   // MXFP4 scales [N][K/32] for B
   const uint8_t* Bs2;  // MXFP4 scales for B2
+  const uint8_t* As;   // B_MXFP4_A8: E8M0 scales of A [rows][K/32] (A holds E4M3 codes, lda in bytes)
   int64_t ldb;         // elements (dense) or bytes (MXFP4 codes)
   int K;
 };

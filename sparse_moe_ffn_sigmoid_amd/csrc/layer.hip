@@ -10,6 +10,7 @@
 // latent aggregation, before the up-projection) and the shared expert (two
 // experts merged into one MLP of width 6144 at full width, added to the
 // routed output).
+#include <algorithm>
 #include <mutex>
 
 #include "common.hpp"
@@ -130,6 +131,51 @@ __global__ __launch_bounds__(256) void expert_slots(const uint8_t* sel, int T, i
   }
 }
 
+// bf16 rows -> MXFP8 (OCP Microscaling: E4M3 elements, one E8M0 scale per 32
+// consecutive elements of a row).  Per block: shared exponent
+// X = floor(log2 amax) - 8 (8 = E4M3's largest exponent), stored as X + 127
+// clamped to [0, 254] (0 for an all-zero block); elements v / 2^X rounded to
+// the nearest E4M3 value, ties to the even mantissa, saturating at 448.  One
+// half-wave per block; blocks are consecutive in the row-major input.
+__global__ __launch_bounds__(256) void mx8_quantize(const bf16_t* __restrict__ in, int64_t nblk,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales) {
+  const int l = threadIdx.x & 31;
+  const int64_t first = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 5;
+  const int64_t step = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 5;
+  for (int64_t b = first; b < nblk; b += step) {
+    const float v = bf16_to_f32(in[b * 32 + l]);
+    float amax = fabsf(v);
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+    int sb = 0;
+    if (amax > 0.f) {
+      const uint32_t ab = __float_as_uint(amax);
+      const int e = static_cast<int>((ab >> 23) & 255u);
+      const int fl = e ? e - 127 : (31 - __clz(ab & 0x7fffffu)) - 149;  // floor(log2 amax)
+      sb = min(max(fl - 8 + 127, 0), 254);
+    }
+    const float q = ldexpf(v, 127 - sb);  // exact: a power-of-two scaling
+    const float a = fabsf(q);
+    uint32_t code;
+    if (a >= 448.f) {
+      code = 0x7Eu;
+    } else if (a >= 0.015625f) {  // normal E4M3: 3 mantissa bits, round half to even
+      const uint32_t bits = __float_as_uint(a);
+      uint32_t keep = (bits >> 20) & 7u, field = ((bits >> 23) & 255u) - 127u + 7u;
+      const uint32_t rem = bits & 0xFFFFFu;
+      if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
+      if (keep == 8u) { keep = 0u; ++field; }
+      code = (field << 3) | keep;
+    } else {  // subnormal: multiples of 2^-9 (8 * 2^-9 is the smallest normal, code 8)
+      code = static_cast<uint32_t>(rintf(a * 512.f));
+    }
+    code |= (__float_as_uint(q) >> 31) << 7;
+    codes[b * 32 + l] = static_cast<uint8_t>(code);
+    if (l == 0) scales[b] = static_cast<uint8_t>(sb);
+  }
+}
+
 // y_t = sum_j w[t][j] * yp[inv[t][j]] in fp32 (j ascending), then
 // RMSNorm: y * rsqrt(mean(y^2) + eps) * gamma.  One block per token.
 template <typename ACT>
@@ -202,6 +248,10 @@ struct ForwardWorkspace {
   void* h;            // [T*k][inter]
   void* yp;           // [T*k][latent]
   void* yhat;         // [T][latent]
+  uint8_t* zq;        // W4A8: z as E4M3 codes [T][latent] and E8M0 scales [T][latent/32]
+  uint8_t* zq_scale;
+  uint8_t* hq;        // W4A8: h as E4M3 codes [T*k][inter] and scales [T*k][inter/32]
+  uint8_t* hq_scale;
   int bm;
   int max_mtiles;
   float* partial;     // split-K partial sums of the dense GEMMs (used one at a time)
@@ -215,6 +265,7 @@ struct ForwardWorkspace {
 static int grouped_bm(const moe_shape_t& s) {
   const int64_t avg = (static_cast<int64_t>(s.T) * s.top_k + s.n_experts - 1) / s.n_experts;
   if (s.act_dtype != MOE_BF16) return 64;
+  if (s.routed_dtype == MOE_MXFP4_A8) return 320;  // the only W4A8 tile
   if (avg <= 32) return 32;
   if (s.routed_dtype == MOE_MXFP4) {
     // MFMA-bound: 320-row tiles on 8 waves for 161 - 320 rows per expert,
@@ -259,6 +310,11 @@ static size_t forward_layout(const moe_shape_t& s, ForwardWorkspace* fw, void* b
   f.h = cv.take<char>(T * k * s.inter * es);
   f.yp = cv.take<float>(T * k * s.latent);  // fp32: the combine sums unrounded products
   f.yhat = cv.take<char>(T * s.latent * es);
+  const bool a8 = s.routed_dtype == MOE_MXFP4_A8;
+  f.zq = cv.take<uint8_t>(a8 ? T * s.latent : 0);
+  f.zq_scale = cv.take<uint8_t>(a8 ? T * s.latent / 32 : 0);
+  f.hq = cv.take<uint8_t>(a8 ? T * k * s.inter : 0);
+  f.hq_scale = cv.take<uint8_t>(a8 ? T * k * s.inter / 32 : 0);
   // The dense GEMMs that may split K never overlap in time: the router runs
   // before the shared branch forks, the two shared-branch products run in
   // order on one stream, and the up-projection runs after the join.
@@ -286,15 +342,17 @@ static int validate(const moe_shape_t* sp, const moe_weights_t* w) {
   if (s.d % 64 || s.latent % 64 || s.inter % 64 || s.shared_inter % 64) return MOE_EUNSUPPORTED;
   if (s.latent > 256 * 16) return MOE_EUNSUPPORTED;
   if (s.act_dtype != MOE_F32 && s.act_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-  if (!(s.routed_dtype == s.act_dtype || (s.routed_dtype == MOE_MXFP4 && s.act_dtype == MOE_BF16)))
-    return MOE_EUNSUPPORTED;
+  const bool mx = s.routed_dtype == MOE_MXFP4 || s.routed_dtype == MOE_MXFP4_A8;
+  if (!(s.routed_dtype == s.act_dtype || (mx && s.act_dtype == MOE_BF16))) return MOE_EUNSUPPORTED;
+  // W4A8 scale words stay inside their rows when K is a multiple of 128
+  if (s.routed_dtype == MOE_MXFP4_A8 && (s.latent % 128 || s.inter % 128)) return MOE_EUNSUPPORTED;
   if (s.qb_mode != MOE_QB_BATCH && s.qb_mode != MOE_QB_FROZEN) return MOE_EINVAL;
   if (!(s.rms_eps >= 0.f)) return MOE_EINVAL;
   if (w) {
     if (!w->w_router || !w->w_down || !w->w_up || !w->w_gate || !w->w_uproj || !w->w_dn ||
         !w->rms_gamma || !w->ws_gate || !w->ws_up || !w->ws_down)
       return MOE_EINVAL;
-    if (s.routed_dtype == MOE_MXFP4 && (!w->s_gate || !w->s_uproj || !w->s_dn)) return MOE_EINVAL;
+    if (mx && (!w->s_gate || !w->s_uproj || !w->s_dn)) return MOE_EINVAL;
   }
   return MOE_OK;
 }
@@ -414,6 +472,13 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     {
       prof::Scope sc(prof::ST_LATENT_DOWN, sst);
       if ((rc = gemm::launch(p, store_epi, gemm::B_DENSE, bf, side_hint, sst)) != MOE_OK) return rc;
+      if (s.routed_dtype == MOE_MXFP4_A8) {  // z -> MXFP8 for the routed experts
+        const int64_t nblk = static_cast<int64_t>(T) * (L / 32);
+        hipLaunchKernelGGL(mx8_quantize,
+                           dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 7) / 8, 16384))),
+                           dim3(256), 0, sst, static_cast<const bf16_t*>(f.z), nblk, f.zq, f.zq_scale);
+        MOE_LAUNCH_CHECK();
+      }
     }
     gemm::Params q{};
     q.M = T;
@@ -458,14 +523,19 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
   }
 
   if (side) MOE_HIP_CHECK(hipStreamWaitEvent(st, side->join, 0));
-  const bool mx = s.routed_dtype == MOE_MXFP4;
-  const int bfmt = mx ? gemm::B_MXFP4 : gemm::B_DENSE;
+  const bool a8 = s.routed_dtype == MOE_MXFP4_A8;
+  const bool mx = s.routed_dtype == MOE_MXFP4 || a8;
+  const int bfmt = a8 ? gemm::B_MXFP4_A8 : mx ? gemm::B_MXFP4 : gemm::B_DENSE;
   // 5. routed gate/up with SiTU-GLU: h[slot] = SiTU(z[perm[slot]] Wg_e^T, z[perm[slot]] Wu_e^T)
   {
     gemm::Params p{};
     p.N = m;
     p.nseg = 1;
-    p.seg[0] = seg(f.z, L, wt.w_gate, mx ? L / 2 : L, L);
+    if (a8)  // W4A8: the E4M3 codes of z, one byte per element
+      p.seg[0] = seg(f.zq, L, wt.w_gate, L / 2, L);
+    else
+      p.seg[0] = seg(f.z, L, wt.w_gate, mx ? L / 2 : L, L);
+    p.seg[0].As = f.zq_scale;
     p.seg[0].B2 = wt.w_uproj;
     p.seg[0].Bs = wt.s_gate;
     p.seg[0].Bs2 = wt.s_uproj;
@@ -480,12 +550,22 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     prof::Scope sc(prof::ST_ROUTED_GATE_UP, st);
     if ((rc = gemm::launch(p, gemm::EPI_SITU, bfmt, bf, f.bm, st)) != MOE_OK) return rc;
   }
+  if (a8) {  // h -> MXFP8 for the down-projection
+    const int64_t nblk = static_cast<int64_t>(T) * k * (m / 32);
+    hipLaunchKernelGGL(mx8_quantize, dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 7) / 8, 16384))),
+                       dim3(256), 0, st, static_cast<const bf16_t*>(f.h), nblk, f.hq, f.hq_scale);
+    MOE_LAUNCH_CHECK();
+  }
   // 6. routed down: yp[slot] = h[slot] Wd_e^T
   {
     gemm::Params p{};
     p.N = L;
     p.nseg = 1;
-    p.seg[0] = seg(f.h, m, wt.w_dn, mx ? m / 2 : m, m);
+    if (a8)
+      p.seg[0] = seg(f.hq, m, wt.w_dn, m / 2, m);
+    else
+      p.seg[0] = seg(f.h, m, wt.w_dn, mx ? m / 2 : m, m);
+    p.seg[0].As = f.hq_scale;
     p.seg[0].Bs = wt.s_dn;
     p.b_expert_stride = mx ? static_cast<int64_t>(L) * m / 2 : static_cast<int64_t>(L) * m;
     p.bs_expert_stride = static_cast<int64_t>(L) * m / 32;

@@ -8,7 +8,7 @@ import workloads
 from oracle import layer as olayer
 from oracle import qb
 
-DT = {"f32": 0, "bf16": 1, "mxfp4": 2}
+DT = {"f32": 0, "bf16": 1, "mxfp4": 2, "mxfp4_a8": 3}
 
 
 def announce(name):

@@ -118,6 +118,9 @@ def test_forward_workspace_sizing_on_host():
     assert ws(k=n + 1) == 0
     assert ws(n=2048) == 0
     assert ws(act=moe.MOE_F32, routed=moe.MOE_MXFP4) == 0
+    assert ws(routed=moe.MOE_MXFP4_A8) > ws(routed=moe.MOE_MXFP4)   # room for the MXFP8 rows
+    assert ws(routed=moe.MOE_MXFP4_A8, latent=3584 + 64) == 0       # W4A8 widths: multiples of 128
+    assert ws(routed=moe.MOE_MXFP4_A8, m=2048 + 64) == 0
     assert ws(act=moe.MOE_F32, routed=moe.MOE_BF16) == 0
     assert ws(mode=5) == 0
 

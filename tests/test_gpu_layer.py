@@ -17,7 +17,7 @@ from oracle import qb
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 1e-1}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 1e-1, "mxfp4_a8": 1e-1}
 
 
 def check_layer(shape, seed=0, qb_mode=qb.MODE_BATCH, bias=None, name=""):
@@ -32,10 +32,11 @@ def check_layer(shape, seed=0, qb_mode=qb.MODE_BATCH, bias=None, name=""):
     assert tuple(int(v) for v in got["info"]) == tuple(ref["info"])
     if qb_mode == qb.MODE_BATCH:
         assert (got["bias"] == ref["bias"]).all()
-    out_ref = olayer.layer_forward(inp, ref["idx"], ref["w"], shape.eps)
+    out_ref = olayer.layer_forward(inp, ref["idx"], ref["w"], shape.eps,
+                                   act_mxfp8=shape.routed == "mxfp4_a8")
     err = rel_err(got["out"], out_ref)
     print(f"  max|diff|/rms = {err:.3e}", flush=True)
-    assert err <= TOL[shape.routed if shape.routed == "mxfp4" else shape.act], err
+    assert err <= TOL[shape.routed if shape.routed.startswith("mxfp4") else shape.act], err
     # the HIP router on its own
     announce(f"router {name}")
     own = run_gpu(moe, shape, inp, bias=bias, qb_mode=qb_mode)
@@ -81,6 +82,25 @@ def test_mxfp4_layer():
 ])
 def test_mxfp4_layer_pipelined(kw):
     check_layer(workloads.small_shape(routed="mxfp4", **kw), seed=5, name=f"mxfp4 {kw}")
+
+
+# W4A8: MXFP4 weights times MXFP8 activations on the scaled MFMA (320-row
+# tiles only), against the oracle that rounds z and h to bf16 and then MXFP8
+@pytest.mark.parametrize("kw", [
+    dict(T=300, n=16, k=4, d=1024, latent=512, m=512, shared=256),   # 75 rows per expert
+    dict(T=1200, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 300 rows per expert
+    dict(T=1000, n=16, k=4, d=1024, latent=640, m=384, shared=256),  # 20 / 12 scale bytes per row
+    dict(T=200, n=40, k=6, d=512, latent=256, m=256, shared=320),    # ragged loads, column tails
+])
+def test_w4a8_layer(kw):
+    check_layer(workloads.small_shape(routed="mxfp4_a8", **kw), seed=11, name=f"w4a8 {kw}")
+
+
+def test_w4a8_layer_frozen_uneven_tiles():
+    shape = workloads.small_shape(routed="mxfp4_a8", T=1000, n=16, k=4, d=1024, latent=512, m=512,
+                                  shared=256, offset_std=1.0)
+    check_layer(shape, seed=12, qb_mode=qb.MODE_FROZEN, bias=np.zeros(shape.n),
+                name="w4a8 frozen, uneven 320-row tiles")
 
 
 def test_mxfp4_layer_frozen_zero_bias():

@@ -25,7 +25,7 @@ from oracle import qb
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "mxfp4": 1e-1}
+TOL = {"bf16": 2e-2, "mxfp4": 1e-1, "mxfp4_a8": 1e-1}
 SCALES = {"w_gate": "s_gate", "w_uproj": "s_uproj", "w_dn": "s_dn"}
 
 
@@ -42,7 +42,7 @@ def forward_as_benchmarked(shape, qb_mode):
         else:
             w[key] = v
     w["router_logit_offset"] = w.pop("logit_offset")
-    routed = moe.MOE_MXFP4 if shape.routed == "mxfp4" else moe.MOE_BF16
+    routed = {"bf16": moe.MOE_BF16, "mxfp4": moe.MOE_MXFP4, "mxfp4_a8": moe.MOE_MXFP4_A8}[shape.routed]
     sh = moe.make_shape(shape.T, shape.d, shape.latent, shape.n, shape.k, shape.m, shape.shared,
                         moe.MOE_BF16, routed, shape.eps, qb_mode, 64)
     ws = torch.empty(moe.forward_workspace_bytes(sh), dtype=torch.uint8, device=dev)
@@ -88,6 +88,7 @@ def check_routing(shape, got, qb_mode):
     ("k3_mxfp4", qb.MODE_BATCH),
     ("k3_mxfp4", qb.MODE_FROZEN),
     ("k3_prefill_16k", qb.MODE_BATCH),
+    ("k3_mxfp4_a8", qb.MODE_BATCH),
 ])
 def test_full_size_layer_sampled(wl, qb_mode):
     check_sampled(workloads.SHAPES[wl], qb_mode, wl)
@@ -115,7 +116,8 @@ def check_sampled(shape, qb_mode, name):
     # layer outputs of the sampled tokens, oracle weights from the same scores
     sub = dict(inp)
     sub["x"] = inp["x"][torch.from_numpy(tokens).cuda()]
-    out_ref = olayer.layer_forward(sub, got["idx"][tokens], w_ref[tokens], shape.eps)
+    out_ref = olayer.layer_forward(sub, got["idx"][tokens], w_ref[tokens], shape.eps,
+                                   act_mxfp8=shape.routed == "mxfp4_a8")
     err = rel_err(got["out"][tokens], out_ref)
     print(f"  info={got['info'].tolist()} sampled max|diff|/rms = {err:.3e}", flush=True)
     assert err <= TOL[shape.routed]
