@@ -131,23 +131,56 @@ __global__ __launch_bounds__(256) void expert_slots(const uint8_t* sel, int T, i
   }
 }
 
+// One element v / 2^X -> E4M3 code: nearest value, ties to the even mantissa,
+// saturating at 448; the sign bit is q's.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const float a = fabsf(q);
+  uint32_t code;
+  if (a >= 448.f) {
+    code = 0x7Eu;
+  } else if (a >= 0.015625f) {  // normal E4M3: 3 mantissa bits, round half to even
+    const uint32_t bits = __float_as_uint(a);
+    uint32_t keep = (bits >> 20) & 7u, field = ((bits >> 23) & 255u) - 127u + 7u;
+    const uint32_t rem = bits & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
+    if (keep == 8u) {
+      keep = 0u;
+      ++field;
+    }
+    code = (field << 3) | keep;
+  } else {  // subnormal: multiples of 2^-9 (8 * 2^-9 is the smallest normal, code 8)
+    code = static_cast<uint32_t>(rintf(a * 512.f));
+  }
+  return code | ((__float_as_uint(q) >> 31) << 7);
+}
+
 // bf16 rows -> MXFP8 (OCP Microscaling: E4M3 elements, one E8M0 scale per 32
 // consecutive elements of a row).  Per block: shared exponent
 // X = floor(log2 amax) - 8 (8 = E4M3's largest exponent), stored as X + 127
 // clamped to [0, 254] (0 for an all-zero block); elements v / 2^X rounded to
-// the nearest E4M3 value, ties to the even mantissa, saturating at 448.  One
-// half-wave per block; blocks are consecutive in the row-major input.
+// the nearest E4M3 value, ties to the even mantissa, saturating at 448.
+// Each lane takes 8 consecutive elements (one 16-byte load, one 8-byte store),
+// four lanes a block; blocks are consecutive in the row-major input.
 __global__ __launch_bounds__(256) void mx8_quantize(const bf16_t* __restrict__ in, int64_t nblk,
                                                     uint8_t* __restrict__ codes,
                                                     uint8_t* __restrict__ scales) {
-  const int l = threadIdx.x & 31;
-  const int64_t first = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 5;
-  const int64_t step = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 5;
-  for (int64_t b = first; b < nblk; b += step) {
-    const float v = bf16_to_f32(in[b * 32 + l]);
-    float amax = fabsf(v);
+  const int64_t tot = nblk * 4;  // 8-element pieces
+  const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  // the stride is a multiple of 4, so the four lanes of a block stay together
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < tot; g += step) {
+    const uint4 raw = reinterpret_cast<const uint4*>(in)[g];
+    float v[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 4));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 4));
     int sb = 0;
     if (amax > 0.f) {
       const uint32_t ab = __float_as_uint(amax);
@@ -155,24 +188,14 @@ __global__ __launch_bounds__(256) void mx8_quantize(const bf16_t* __restrict__ i
       const int fl = e ? e - 127 : (31 - __clz(ab & 0x7fffffu)) - 149;  // floor(log2 amax)
       sb = min(max(fl - 8 + 127, 0), 254);
     }
-    const float q = ldexpf(v, 127 - sb);  // exact: a power-of-two scaling
-    const float a = fabsf(q);
-    uint32_t code;
-    if (a >= 448.f) {
-      code = 0x7Eu;
-    } else if (a >= 0.015625f) {  // normal E4M3: 3 mantissa bits, round half to even
-      const uint32_t bits = __float_as_uint(a);
-      uint32_t keep = (bits >> 20) & 7u, field = ((bits >> 23) & 255u) - 127u + 7u;
-      const uint32_t rem = bits & 0xFFFFFu;
-      if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
-      if (keep == 8u) { keep = 0u; ++field; }
-      code = (field << 3) | keep;
-    } else {  // subnormal: multiples of 2^-9 (8 * 2^-9 is the smallest normal, code 8)
-      code = static_cast<uint32_t>(rintf(a * 512.f));
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= e4m3_code(ldexpf(v[i], 127 - sb)) << (8 * i);      // exact power-of-two scaling
+      hi |= e4m3_code(ldexpf(v[4 + i], 127 - sb)) << (8 * i);
     }
-    code |= (__float_as_uint(q) >> 31) << 7;
-    codes[b * 32 + l] = static_cast<uint8_t>(code);
-    if (l == 0) scales[b] = static_cast<uint8_t>(sb);
+    reinterpret_cast<uint2*>(codes)[g] = make_uint2(lo, hi);
+    if ((g & 3) == 0) scales[g >> 2] = static_cast<uint8_t>(sb);
   }
 }
 
@@ -475,7 +498,7 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
       if (s.routed_dtype == MOE_MXFP4_A8) {  // z -> MXFP8 for the routed experts
         const int64_t nblk = static_cast<int64_t>(T) * (L / 32);
         hipLaunchKernelGGL(mx8_quantize,
-                           dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 7) / 8, 16384))),
+                           dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 63) / 64, 8192))),
                            dim3(256), 0, sst, static_cast<const bf16_t*>(f.z), nblk, f.zq, f.zq_scale);
         MOE_LAUNCH_CHECK();
       }
@@ -552,7 +575,7 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
   }
   if (a8) {  // h -> MXFP8 for the down-projection
     const int64_t nblk = static_cast<int64_t>(T) * k * (m / 32);
-    hipLaunchKernelGGL(mx8_quantize, dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 7) / 8, 16384))),
+    hipLaunchKernelGGL(mx8_quantize, dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 63) / 64, 8192))),
                        dim3(256), 0, st, static_cast<const bf16_t*>(f.h), nblk, f.hq, f.hq_scale);
     MOE_LAUNCH_CHECK();
   }
