@@ -733,9 +733,10 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 // and stage, 16-byte chunks XOR-swizzled by (row / 2) mod 4) and its E8M0
 // scales travel through the ring like B's; one scaled MFMA
 // (v_mfma_scale_f32_32x32x64_f8f6f4) per fragment pair and stage.
-template <int BM, int BN, int WM, int EPI, int NW, bool SR, bool A8 = false>
+template <int BM, int BN, int WM, int EPI, int NW, bool SR, bool A8 = false, int NSF = 3>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_pipe_fp4(Params p) {
   static_assert(!A8 || SR, "MXFP8 A needs the scale ring");
+  static_assert(NSF >= 3 && NSF <= 6, "ring depth");
   constexpr int BKP = 64;
   constexpr int NTH = 64 * NW;
   constexpr int WN = NW / WM;
@@ -761,18 +762,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   constexpr int MS = (SR ? 1 : 0) + (A8 ? 1 : 0);
   static_assert(!SR || (NS <= NW && NS * 64 == BN), "one scale instruction per wave");
 
-  __shared__ __attribute__((aligned(1024))) bf16_t sA0[A8 ? BM * BKP / 2 : BM * BKP];
-  __shared__ __attribute__((aligned(1024))) bf16_t sA1[A8 ? BM * BKP / 2 : BM * BKP];
-  __shared__ __attribute__((aligned(1024))) bf16_t sA2[A8 ? BM * BKP / 2 : BM * BKP];
-  __shared__ __attribute__((aligned(16))) uint8_t sT0[A8 ? NSA * 256 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sT1[A8 ? NSA * 256 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sT2[A8 ? NSA * 256 : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sQ0[BN * 32];
-  __shared__ __attribute__((aligned(1024))) uint8_t sQ1[BN * 32];
-  __shared__ __attribute__((aligned(1024))) uint8_t sQ2[BN * 32];
-  __shared__ __attribute__((aligned(16))) uint8_t sS0[SR ? BN * 4 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sS1[SR ? BN * 4 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sS2[SR ? BN * 4 : 16];
+  // NSF ring stages: A rows (bf16 or E4M3 codes), B codes, B scales, A scales
+  __shared__ __attribute__((aligned(1024))) bf16_t sA[NSF][A8 ? BM * BKP / 2 : BM * BKP];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[NSF][BN * 32];
+  __shared__ __attribute__((aligned(16))) uint8_t sS[NSF][SR ? BN * 4 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sT[NSF][A8 ? NSA * 256 : 16];
   // scale panel [BN][K/32], sized by the launch (not used with SR)
   extern __shared__ __attribute__((aligned(16))) uint8_t sP[];
 
@@ -908,9 +902,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int rb = wn * WTN + j * 32 + (lane & 31);
-        const u32x4_t q = *reinterpret_cast<const u32x4_t*>(Qs + rb * 32 + ((hi ^ ((rb >> 2) & 1)) * 16));
-        bq[j] = v8i_t{static_cast<int>(q[0]), static_cast<int>(q[1]), static_cast<int>(q[2]),
-                      static_cast<int>(q[3]), 0, 0, 0, 0};
+        typedef int v4i_t __attribute__((ext_vector_type(4)));
+        const v4i_t q = *reinterpret_cast<const v4i_t*>(Qs + rb * 32 + ((hi ^ ((rb >> 2) & 1)) * 16));
+        // E2M1 B occupies the first four registers; the other four are not read
+        bq[j] = __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);
         sb[j] = Ss[rb * 4 + (kt & 1) * 2 + hi];
       }
       const uint8_t* Ab = reinterpret_cast<const uint8_t*>(As);
@@ -958,24 +953,24 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
 
   // the panel's LDS writes complete before the first barrier of the ring
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  if (ktot > 0) issue(sA0, sQ0, sS0, sT0);
-  if (ktot > 1) issue(sA1, sQ1, sS1, sT1);
-  auto ring = [&](int kt, bf16_t* Ac, uint8_t* Qc, uint8_t* Sc, uint8_t* Tc, bf16_t* An,
-                  uint8_t* Qn, uint8_t* Sn, uint8_t* Tn) {
+  static_assert((NSF - 2) * (MA + MQ + MS) < 64, "loads in flight exceed the vmcnt range");
+#pragma unroll
+  for (int s = 0; s < NSF - 1; ++s)
+    if (s < ktot) issue(sA[s], sQ[s], sS[s], sT[s]);
+  // one ring step: wait for stage kt (the NSF - 2 issued after it may stay in
+  // flight), refill the slot stage kt-1 used, multiply stage kt
+  auto ring = [&](int kt, int c, int nx) {
     if (kt < ktot) {
-      if (kt + 1 < ktot)
-        wait_vmcnt<MA + MQ + MS>();
-      else
-        wait_vmcnt<0>();
+      const int ahead = min(NSF - 2, ktot - 1 - kt);
+      wait_stages<NSF - 2, MA + MQ + MS>(ahead);
       lds_barrier();
-      if (kt + 2 < ktot) issue(An, Qn, Sn, Tn);
-      compute(kt, Ac, Qc, Sc, Tc);
+      if (kt + NSF - 1 < ktot) issue(sA[nx], sQ[nx], sS[nx], sT[nx]);
+      compute(kt, sA[c], sQ[c], sS[c], sT[c]);
     }
   };
-  for (int kt = 0; kt < ktot; kt += STAGES) {
-    ring(kt, sA0, sQ0, sS0, sT0, sA2, sQ2, sS2, sT2);
-    ring(kt + 1, sA1, sQ1, sS1, sT1, sA0, sQ0, sS0, sT0);
-    ring(kt + 2, sA2, sQ2, sS2, sT2, sA1, sQ1, sS1, sT1);
+  for (int kt = 0; kt < ktot; kt += NSF) {
+#pragma unroll
+    for (int s = 0; s < NSF; ++s) ring(kt + s, s, (s + NSF - 1) % NSF);
   }
 
 #pragma unroll
@@ -1308,6 +1303,9 @@ bool fp4_tile320_fits(int K) { return K > 0 && K % 128 == 0; }
 // multiple of 128, so that every stage's scale word lies inside its row).
 template <int BM, int BN, int WM, int EPI, int NW = 4, bool SR = false, bool A8 = false>
 static int run_pipe_fp4(const Params& p, hipStream_t stream) {
+  // three stages: four or five (the E4M3 stages are half the size of bf16
+  // ones) measured no faster for the W4A8 tiles
+  constexpr int NSF = 3;
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   if (p.nseg != 1 || p.seg[0].K % (SR ? 128 : 512) != 0) return 1;
   const Seg& g = p.seg[0];
@@ -1327,14 +1325,14 @@ static int run_pipe_fp4(const Params& p, hipStream_t stream) {
   const int64_t G8 = (G + 7) / 8 * 8;
   static bool configured = false;
   if (!SR && !configured) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, A8>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, A8, NSF>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(fp4_lds_budget<BM>() - fp4_static_lds<BM, BN>())) !=
         hipSuccess)
       return MOE_EHIP;
     configured = true;
   }
-  hipLaunchKernelGGL((gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, A8>), dim3(static_cast<unsigned>(G8)),
+  hipLaunchKernelGGL((gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, A8, NSF>), dim3(static_cast<unsigned>(G8)),
                      dim3(64 * NW), panel, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
