@@ -729,15 +729,18 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 // per B row per stage: the scale bytes of this stage and its neighbour)
 // instead of a per-block panel of the whole K range, which leaves room for
 // 320-row tiles at any K.
-// A8 (with SR): A holds MXFP8 codes (one byte per element, 64 bytes per row
-// and stage, 16-byte chunks XOR-swizzled by (row / 2) mod 4) and its E8M0
-// scales travel through the ring like B's; one scaled MFMA
-// (v_mfma_scale_f32_32x32x64_f8f6f4) per fragment pair and stage.
+// A8 (with SR): A holds MXFP8 codes, one byte per element, and a stage spans
+// 128 K elements: 128 bytes of A per row (laid out like a bf16 stage of 64),
+// 64 bytes of B codes per row (16-byte chunks XOR-swizzled by (row / 2) mod 4)
+// and one 4-byte word of E8M0 scales per row for each of A and B.  Two scaled
+// MFMAs (v_mfma_scale_f32_32x32x64_f8f6f4) per fragment pair and stage.
 template <int BM, int BN, int WM, int EPI, int NW, bool SR, bool A8 = false, int NSF = 3>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_pipe_fp4(Params p) {
   static_assert(!A8 || SR, "MXFP8 A needs the scale ring");
-  static_assert(NSF >= 3 && NSF <= 6, "ring depth");
-  constexpr int BKP = 64;
+  static_assert(NSF >= 2 && NSF <= 6, "ring depth");
+  constexpr int BKP = 64;              // bf16 elements of A per row and stage (128 bytes)
+  constexpr int KST = A8 ? 128 : 64;   // K elements per stage
+  constexpr int QROW = KST / 2;        // E2M1 code bytes per B row and stage
   constexpr int NTH = 64 * NW;
   constexpr int WN = NW / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -745,10 +748,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold 32x32 blocks");
   static_assert(EPI != EPI_SITU || FN % 2 == 0, "SiTU needs gate/up fragment pairs");
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
-  // A: 8 rows of 128 bytes (bf16) or 16 rows of 64 bytes (E4M3) per instruction
-  constexpr int A_RPI = A8 ? 16 : 8;
-  constexpr int NA = BM / A_RPI, NQ = BN / 32;
-  static_assert(NA * A_RPI == BM && NQ * 32 == BN, "tile rows per instruction");
+  // A: 8 rows of 128 bytes per instruction; B: 1 KB of codes per instruction
+  constexpr int A_RPI = 8, Q_RPI = 1024 / QROW;
+  constexpr int NA = BM / A_RPI, NQ = BN / Q_RPI;
+  static_assert(NA * A_RPI == BM && NQ * Q_RPI == BN, "tile rows per instruction");
   constexpr int MA = (NA + NW - 1) / NW, MQ = NQ / NW;
   static_assert(NA >= NW && NQ % NW == 0, "uniform load instructions per wave");
   // surplus A instructions repeat the wave's own instruction i-1
@@ -763,8 +766,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   static_assert(!SR || (NS <= NW && NS * 64 == BN), "one scale instruction per wave");
 
   // NSF ring stages: A rows (bf16 or E4M3 codes), B codes, B scales, A scales
-  __shared__ __attribute__((aligned(1024))) bf16_t sA[NSF][A8 ? BM * BKP / 2 : BM * BKP];
-  __shared__ __attribute__((aligned(1024))) uint8_t sQ[NSF][BN * 32];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA[NSF][BM * BKP];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[NSF][BN * QROW];
   __shared__ __attribute__((aligned(16))) uint8_t sS[NSF][SR ? BN * 4 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sT[NSF][A8 ? NSA * 256 : 16];
   // scale panel [BN][K/32], sized by the launch (not used with SR)
@@ -813,14 +816,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   int a_chunk[MA];
 #pragma unroll
   for (int i = 0; i < MA; ++i) {
-    int r;
-    if (A8) {
-      r = a_ins(wave, i) * 16 + (lane >> 2);
-      a_chunk[i] = (lane & 3) ^ ((r >> 1) & 3);
-    } else {
-      r = a_ins(wave, i) * 8 + (lane >> 3);
-      a_chunk[i] = (lane & 7) ^ (r & 7);
-    }
+    int r = a_ins(wave, i) * 8 + (lane >> 3);
+    a_chunk[i] = (lane & 7) ^ (r & 7);
     r = r < tile.rows ? r : 0;
     const int slot = tile.row0 + r;
     a_off[i] = p.a_rows ? p.a_rows[slot] : slot;
@@ -849,11 +846,18 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
                  : A + a_off[i] * g.lda + a_chunk[i] * 8;
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
-      const int r = (wave + NW * i) * 32 + (lane >> 1);
-      const int half = (lane & 1) ^ ((r >> 2) & 1);
       bool up;
-      const int64_t row = b_row_of(r, up);
-      pq[i] = (up ? Q2 : Q) + row * g.ldb + half * 16;
+      if (A8) {  // 64-byte rows: four 16-byte chunks, swizzled by (row / 2) mod 4
+        const int r = (wave + NW * i) * 16 + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((r >> 1) & 3);
+        const int64_t row = b_row_of(r, up);
+        pq[i] = (up ? Q2 : Q) + row * g.ldb + chunk * 16;
+      } else {
+        const int r = (wave + NW * i) * 32 + (lane >> 1);
+        const int half = (lane & 1) ^ ((r >> 2) & 1);
+        const int64_t row = b_row_of(r, up);
+        pq[i] = (up ? Q2 : Q) + row * g.ldb + half * 16;
+      }
     }
     if (SR) {
       bool up;
@@ -861,24 +865,27 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
       ps = (up ? g.Bs2 : g.Bs) + static_cast<int64_t>(tile.expert) * p.bs_expert_stride + row * sp;
     }
   }
-  const int ktot = g.K / BKP;
+  const int ktot = g.K / KST;
 
   int issued = 0;  // stages issued so far
+  // the scale word of a stage: bytes 2kt .. 2kt+1 inside the aligned word at
+  // (2kt) & ~3 (64-element stages), or exactly bytes 4kt .. 4kt+3 (128)
+  auto scale_word = [&]() { return A8 ? 4 * issued : (2 * issued) & ~3; };
   auto issue = [&](bf16_t* As, uint8_t* Qs, uint8_t* Ss, uint8_t* Ts) {
 #pragma unroll
     for (int i = 0; i < MA; ++i) {
       // one instruction fills 1 KB: 8 bf16 rows or 16 E4M3 rows of the stage
       load_lds16_raw(pa[i], As + a_ins(wave, i) * 512);
-      pa[i] += A8 ? BKP / 2 : BKP;  // bf16_t units
+      pa[i] += BKP;  // 128 bytes
     }
-    if (A8) load_lds4_asm(pt + ((2 * issued) & ~3), Ts + t_ins * 256);
+    if (A8) load_lds4_asm(pt + scale_word(), Ts + t_ins * 256);
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
       load_lds16_raw(pq[i], Qs + (wave + NW * i) * 1024);
-      pq[i] += BKP / 2;
+      pq[i] += QROW;
     }
     if (SR)  // scale bytes 2kt, 2kt+1 of stage kt sit in the aligned word at (2kt) & ~3
-      load_lds4_asm(ps + ((2 * issued) & ~3), Ss + s_ins * 256);
+      load_lds4_asm(ps + scale_word(), Ss + s_ins * 256);
     ++issued;
   };
 
@@ -897,32 +904,39 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
       // lane (r, h): B codes of K [32h, 32h+32), A codes of K [16h, 16h+16)
       // and [32+16h, 32+16h+16); scale registers of block h on both sides
       typedef int v8i_t __attribute__((ext_vector_type(8)));
-      v8i_t bq[FN];
-      int sb[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int rb = wn * WTN + j * 32 + (lane & 31);
-        typedef int v4i_t __attribute__((ext_vector_type(4)));
-        const v4i_t q = *reinterpret_cast<const v4i_t*>(Qs + rb * 32 + ((hi ^ ((rb >> 2) & 1)) * 16));
-        // E2M1 B occupies the first four registers; the other four are not read
-        bq[j] = __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);
-        sb[j] = Ss[rb * 4 + (kt & 1) * 2 + hi];
-      }
+      typedef int v4i_t __attribute__((ext_vector_type(4)));
       const uint8_t* Ab = reinterpret_cast<const uint8_t*>(As);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int ra = wm * WTM + i * 32 + (lane & 31);
-        const int s = (ra >> 1) & 3;
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(Ab + ra * 64 + ((hi ^ s) * 16));
-        const u32x4_t up = *reinterpret_cast<const u32x4_t*>(Ab + ra * 64 + (((2 + hi) ^ s) * 16));
-        const v8i_t aq = {static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
-                          static_cast<int>(lo[3]), static_cast<int>(up[0]), static_cast<int>(up[1]),
-                          static_cast<int>(up[2]), static_cast<int>(up[3])};
-        const int sa = Ts[ra * 4 + (kt & 1) * 2 + hi];
+      for (int q2 = 0; q2 < 2; ++q2) {  // the stage's two 64-element MFMA steps
+        v8i_t bq[FN];
+        int sb[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq, bq[j], acc[i][j], 0, 4, 0,
-                                                                     sa, 0, sb[j]);
+        for (int j = 0; j < FN; ++j) {
+          const int rb = wn * WTN + j * 32 + (lane & 31);
+          const v4i_t q = *reinterpret_cast<const v4i_t*>(
+              Qs + rb * 64 + (((2 * q2 + hi) ^ ((rb >> 1) & 3)) * 16));
+          // E2M1 B occupies the first four registers; the other four are not read
+          bq[j] = __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);
+          sb[j] = Ss[rb * 4 + 2 * q2 + hi];
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int ra = wm * WTM + i * 32 + (lane & 31);
+          const int s = ra & 7;
+          const u32x4_t lo =
+              *reinterpret_cast<const u32x4_t*>(Ab + ra * 128 + (((4 * q2 + hi) ^ s) * 16));
+          const u32x4_t up =
+              *reinterpret_cast<const u32x4_t*>(Ab + ra * 128 + (((4 * q2 + 2 + hi) ^ s) * 16));
+          const v8i_t aq = {static_cast<int>(lo[0]), static_cast<int>(lo[1]),
+                            static_cast<int>(lo[2]), static_cast<int>(lo[3]),
+                            static_cast<int>(up[0]), static_cast<int>(up[1]),
+                            static_cast<int>(up[2]), static_cast<int>(up[3])};
+          const int sa = Ts[ra * 4 + 2 * q2 + hi];
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq, bq[j], acc[i][j], 0, 4,
+                                                                       0, sa, 0, sb[j]);
+        }
       }
       return;
     }
@@ -1303,9 +1317,8 @@ bool fp4_tile320_fits(int K) { return K > 0 && K % 128 == 0; }
 // multiple of 128, so that every stage's scale word lies inside its row).
 template <int BM, int BN, int WM, int EPI, int NW = 4, bool SR = false, bool A8 = false>
 static int run_pipe_fp4(const Params& p, hipStream_t stream) {
-  // three stages: four or five (the E4M3 stages are half the size of bf16
-  // ones) measured no faster for the W4A8 tiles
-  constexpr int NSF = 3;
+  // W4A8: two 128-element stages (117 KB); bf16-A: three 64-element stages
+  constexpr int NSF = A8 ? 2 : 3;
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   if (p.nseg != 1 || p.seg[0].K % (SR ? 128 : 512) != 0) return 1;
   const Seg& g = p.seg[0];
