@@ -32,7 +32,7 @@ PEAK_FP8_TFLOPS = 5000.0   # dense fp8 MFMA (the W4A8 experts' E4M3 x E2M1 produ
 TRAFFIC = {"k3_prefill": 27.019e9,      # gemm_pipe<96, 256, 1, SITU, 64, 3, nt>
            "k3_decode": 26.312e9,       # gemm_pipe<32, 256, 1, SITU, 64, 3, nt>
            "k3_mxfp4": 9.928e9,         # gemm_pipe_fp4<320, 256, 2, SITU, 8 waves, scale ring>
-           "k3_mxfp4_a8": 9.060e9,      # gemm_pipe_fp4<320, 256, 2, SITU, 8 waves, scale ring, MXFP8 A>
+           "k3_mxfp4_a8": 9.290e9,      # gemm_pipe_fp4<320, 256, 2, SITU, 8 waves, MXFP8 A, 2 x 128-element stages>
            "k3_prefill_16k": 29.243e9}  # gemm_pipe<320, 256, 2, SITU, 64, 2, nt, 8 waves>
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
 
