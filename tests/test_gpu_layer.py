@@ -91,9 +91,19 @@ def test_mxfp4_layer_pipelined(kw):
     dict(T=1200, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 300 rows per expert
     dict(T=1000, n=16, k=4, d=1024, latent=640, m=384, shared=256),  # 20 / 12 scale bytes per row
     dict(T=200, n=40, k=6, d=512, latent=256, m=256, shared=320),    # ragged loads, column tails
+    dict(T=16, n=64, k=4, d=256, latent=128, m=128, shared=128),     # decode-like: 1 row per expert
 ])
 def test_w4a8_layer(kw):
     check_layer(workloads.small_shape(routed="mxfp4_a8", **kw), seed=11, name=f"w4a8 {kw}")
+
+
+def test_w4a8_layer_empty_batch():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    shape = workloads.small_shape(routed="mxfp4_a8", T=0, latent=128, m=128)
+    inp = workloads.layer_inputs(shape, "cpu", seed=0)
+    announce("w4a8 layer T=0")
+    got = run_gpu(moe, shape, inp)
+    assert got["out"].shape == (0, shape.d) and (got["loads"] == 0).all()
 
 
 def test_w4a8_layer_frozen_uneven_tiles():
