@@ -75,6 +75,30 @@ def test_route_batch_parity(name, T, n, k, std):
     assert (got["loads"] == qb.targets(T, n, k)).all()
 
 
+def clustered_scores(protos, copies, n, noise, seed):
+    """`protos` random score rows, each repeated `copies` times with a
+    distinct uniform perturbation of size `noise` per entry: the margins of
+    an expert then form a few tight clusters of `copies` tokens each."""
+    rng = np.random.default_rng(seed)
+    base = olayer.sigmoid(rng.standard_normal((protos, n)))
+    s = np.repeat(base, copies, axis=0) + noise * rng.random((protos * copies, n))
+    return np.clip(s, 0.0, 1.0).astype(np.float32)
+
+
+@pytest.mark.parametrize("protos,copies,n,k,seed", [(3, 4500, 6, 2, 1), (4, 5000, 8, 2, 2)])
+def test_route_clustered_margins_parity(protos, copies, n, k, seed):
+    """Thousands of distinct margins inside one relative width of a few
+    percent around each unbalanced expert's target rank (every quantile
+    round here has 6,000 - 10,000 of them in the buckets it must resolve,
+    more than the 4,096 margins the quantile kernel ranks in LDS), so the
+    rounds go through its exact radix selection over all tokens.  The
+    balanced answer is still unique (no two margins are equal)."""
+    s = clustered_scores(protos, copies, n, 1e-5, seed)
+    ref, got = check(s, k, name=f"clustered {protos}x{copies}")
+    assert ref["info"][1] == qb.STATUS_OK and ref["info"][0] > 0
+    assert (got["loads"] == qb.targets(s.shape[0], n, k)).all()
+
+
 def test_route_frozen_parity():
     s = scores(500, 64, 1.0, seed=3)
     bias = np.random.default_rng(0).normal(0, 0.2, 64)
