@@ -392,6 +392,19 @@ struct SideStream {
   bool ok = false;
 };
 
+// Joins a forked side stream back into the caller's stream when a forward
+// returns early (an error after the fork), so that no side-stream work can
+// outlive the call and touch a workspace the caller then frees.
+struct SideJoin {
+  SideStream* side = nullptr;
+  hipStream_t st = nullptr;
+  bool joined = false;
+  ~SideJoin() {
+    if (side && !joined && hipEventRecord(side->join, side->s) == hipSuccess)
+      (void)hipStreamWaitEvent(st, side->join, 0);
+  }
+};
+
 static SideStream* side_stream() {
   static SideStream tab[64];
   static std::mutex init_mu;
@@ -469,10 +482,13 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
   //    z = x W_down^T, hs = SiTU(x Wgs^T, x Wus^T)
   SideStream* side = T > 0 ? side_stream() : nullptr;
   std::unique_lock<std::mutex> side_lock;
+  SideJoin side_join;  // destroyed before side_lock is released
   hipStream_t sst = st;
   if (side) {
     side_lock = std::unique_lock<std::mutex>(side->mu);
     MOE_HIP_CHECK(hipEventRecord(side->fork, st));
+    side_join.side = side;
+    side_join.st = st;
     MOE_HIP_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
     sst = side->s;
   }
@@ -545,7 +561,10 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
   MOE_LAUNCH_CHECK();
   }
 
-  if (side) MOE_HIP_CHECK(hipStreamWaitEvent(st, side->join, 0));
+  if (side) {
+    MOE_HIP_CHECK(hipStreamWaitEvent(st, side->join, 0));
+    side_join.joined = true;
+  }
   const bool a8 = s.routed_dtype == MOE_MXFP4_A8;
   const bool mx = s.routed_dtype == MOE_MXFP4 || a8;
   const int bfmt = a8 ? gemm::B_MXFP4_A8 : mx ? gemm::B_MXFP4 : gemm::B_DENSE;
