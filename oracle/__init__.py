@@ -28,7 +28,8 @@ Modules:
 * :mod:`oracle.layer`  -- router, SiTU-GLU, RMSNorm, MXFP4 decoding and the
   whole latent-MoE layer in float64.
 
-Parity status of each function is stated in its docstring; the whole-layer
-composition beyond the component pins is "parity unpinned" (no worked numeric
-example exists on the pages).
+Parity status of each function is stated in its docstring.  The pages print
+no worked numeric example of the whole layer; its composition is pinned on
+weights that are scaled permutation matrices, where the expected output can
+be written out by hand.
 """

@@ -32,8 +32,11 @@ with gain gamma; routed scaling factor 1.
 Parity status: sigmoid, SiTU-GLU, RMSNorm, MXFP4 decoding, the MXFP8 (E4M3)
 activation codec of the W4A8 experts and the shared-MLP merge are pinned by
 tests (closed forms, bounds, identities, the OCP code tables, brute-force
-nearest values); the composition of the whole layer is "parity unpinned" beyond those
-component pins, since the pages print no worked example.
+nearest values).  The pages print no worked example of the whole layer; its
+composition is pinned on weights that are scaled permutation matrices, where
+every step reduces to gathers and scalar functions written out by hand in the
+test (a transposed operand, a swapped gate/up, a wrong weight, a dropped term
+or RMSNorm in the wrong place fails it).
 """
 from __future__ import annotations
 

@@ -138,6 +138,72 @@ def test_layer_token_sampling_matches_full():
     assert np.allclose(full[[3, 17, 40]], some, rtol=1e-12, atol=1e-12)
 
 
+def test_layer_composition_with_permutation_weights():
+    """The whole layer on weights that are scaled permutation matrices, where
+    every step reduces to gathers and scalar functions that can be written
+    out by hand: z = x[sigma]; expert e: g = a_e z[pi_g], u = b_e z[pi_u],
+    y_e = c_e SiTU(g, u)[pi_d]; the latent sum over the chosen experts with
+    the renormalised raw scores, RMSNorm, a scatter back to width d, and the
+    shared MLP on the same permutation pattern.  Permutations (not
+    identities) make every transposed operand fail; distinct a, b, c per
+    expert make a swapped gate/up, a wrong expert or a wrong weight fail;
+    experts chosen by score are not the lowest indices."""
+    rng = np.random.default_rng(11)
+    T, d, lat, n, k, S = 5, 12, 6, 4, 2, 12
+    eps = 1e-6
+
+    def perm_matrix(rows, cols, src):      # M[i, src[i]] = 1: (M v)_i = v[src[i]]
+        M = np.zeros((rows, cols))
+        M[np.arange(rows), src] = 1.0
+        return M
+
+    x = rng.normal(0, 1.5, (T, d)).astype(np.float32).astype(np.float64)
+    sigma = rng.permutation(d)[:lat]                       # latent = x[sigma]
+    a, b, c = rng.uniform(0.5, 3, n), rng.uniform(2, 40, n), rng.uniform(0.5, 2, n)
+    pg = [rng.permutation(lat) for _ in range(n)]
+    pu = [rng.permutation(lat) for _ in range(n)]
+    pd = [rng.permutation(lat) for _ in range(n)]
+    tau = rng.permutation(d)[:lat]                         # out[tau[i]] += yhat[i]
+    q1, q2, q3 = rng.permutation(S), rng.permutation(S), rng.permutation(d)
+    gs, us, vs = 1.7, 9.0, 0.6
+    gamma = rng.uniform(0.5, 1.5, lat)
+    p = np.array([1.0, -0.5, 2.0, 0.3])                    # top-2 by score: experts 2, 0
+
+    inp = dict(
+        x=x, w_router=np.zeros((n, d)), logit_offset=p,
+        w_down=perm_matrix(lat, d, sigma),
+        w_gate=np.stack([a[e] * perm_matrix(lat, lat, pg[e]) for e in range(n)]),
+        w_uproj=np.stack([b[e] * perm_matrix(lat, lat, pu[e]) for e in range(n)]),
+        w_dn=np.stack([c[e] * perm_matrix(lat, lat, pd[e]) for e in range(n)]),
+        rms_gamma=gamma,
+        w_up=perm_matrix(lat, d, tau).T,
+        ws_gate=gs * perm_matrix(S, d, q1), ws_up=us * perm_matrix(S, d, q2),
+        ws_down=vs * perm_matrix(d, S, q3),
+    )
+    r = layer.route_layer(inp, k, mode=qb.MODE_FROZEN, bias=np.zeros(n))
+    assert (r["idx"] == np.array([2, 0])).all()
+    sc = 1.0 / (1.0 + np.exp(-p))
+    assert np.allclose(r["w"], (sc[[2, 0]] / sc[[2, 0]].sum())[None, :], rtol=1e-6, atol=0)
+    out = layer.layer_forward(inp, r["idx"], r["w"], eps)
+
+    def situ(g, u):   # SiLU(4 tanh(g/4)) * 25 tanh(u/25)
+        gc = 4.0 * np.tanh(g / 4.0)
+        return gc / (1.0 + np.exp(-gc)) * 25.0 * np.tanh(u / 25.0)
+
+    want = np.zeros((T, d))
+    for t in range(T):
+        z = x[t, sigma]
+        y = np.zeros(lat)
+        for j, e in enumerate(r["idx"][t]):
+            h = situ(a[e] * z[pg[e]], b[e] * z[pu[e]])
+            y += r["w"][t, j] * c[e] * h[pd[e]]
+        yhat = y / np.sqrt(np.mean(y * y) + eps) * gamma
+        want[t, tau] += yhat
+        hs = situ(gs * x[t, q1], us * x[t, q2])
+        want[t] += vs * hs[q3]
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
+
+
 def test_router_scores_with_zero_input_are_sigmoid_of_offset():
     p = np.array([-1.0, 0.0, 2.0])
     s = layer.router_scores(np.zeros((2, 4)), np.ones((3, 4)), p)
