@@ -1,5 +1,6 @@
 """Pins of the layer oracle: closed forms, bounds and identities the pages fix."""
 import numpy as np
+import pytest
 import torch
 
 import workloads
@@ -138,7 +139,8 @@ def test_layer_token_sampling_matches_full():
     assert np.allclose(full[[3, 17, 40]], some, rtol=1e-12, atol=1e-12)
 
 
-def test_layer_composition_with_permutation_weights():
+@pytest.mark.parametrize("w4a8", [False, True])
+def test_layer_composition_with_permutation_weights(w4a8):
     """The whole layer on weights that are scaled permutation matrices, where
     every step reduces to gathers and scalar functions that can be written
     out by hand: z = x[sigma]; expert e: g = a_e z[pi_g], u = b_e z[pi_u],
@@ -147,9 +149,12 @@ def test_layer_composition_with_permutation_weights():
     shared MLP on the same permutation pattern.  Permutations (not
     identities) make every transposed operand fail; distinct a, b, c per
     expert make a swapped gate/up, a wrong expert or a wrong weight fail;
-    experts chosen by score are not the lowest indices."""
+    experts chosen by score are not the lowest indices.  With ``w4a8`` the
+    expert inputs z and the SiTU-GLU outputs h (rows of 32, one MXFP8 block)
+    are rounded to bf16 and then MXFP8 at exactly those two places, with the
+    separately pinned codec."""
     rng = np.random.default_rng(11)
-    T, d, lat, n, k, S = 5, 12, 6, 4, 2, 12
+    T, d, lat, n, k, S = 5, 64, 32, 4, 2, 64
     eps = 1e-6
 
     def perm_matrix(rows, cols, src):      # M[i, src[i]] = 1: (M v)_i = v[src[i]]
@@ -184,7 +189,10 @@ def test_layer_composition_with_permutation_weights():
     assert (r["idx"] == np.array([2, 0])).all()
     sc = 1.0 / (1.0 + np.exp(-p))
     assert np.allclose(r["w"], (sc[[2, 0]] / sc[[2, 0]].sum())[None, :], rtol=1e-6, atol=0)
-    out = layer.layer_forward(inp, r["idx"], r["w"], eps)
+    out = layer.layer_forward(inp, r["idx"], r["w"], eps, act_mxfp8=w4a8)
+
+    def act(v):
+        return layer.w4a8_activation(v[None, :])[0] if w4a8 else v
 
     def situ(g, u):   # SiLU(4 tanh(g/4)) * 25 tanh(u/25)
         gc = 4.0 * np.tanh(g / 4.0)
@@ -192,10 +200,10 @@ def test_layer_composition_with_permutation_weights():
 
     want = np.zeros((T, d))
     for t in range(T):
-        z = x[t, sigma]
+        z = act(x[t, sigma])
         y = np.zeros(lat)
         for j, e in enumerate(r["idx"][t]):
-            h = situ(a[e] * z[pg[e]], b[e] * z[pu[e]])
+            h = act(situ(a[e] * z[pg[e]], b[e] * z[pu[e]]))
             y += r["w"][t, j] * c[e] * h[pd[e]]
         yhat = y / np.sqrt(np.mean(y * y) + eps) * gamma
         want[t, tau] += yhat
@@ -269,6 +277,18 @@ def test_mxfp8_block_scale_rule_and_error_bound():
     w = rng.choice(grid[grid > 0], (8, 64)) * 2.0 ** -5
     w[:, ::32] = 256 * 2.0 ** -5                              # block maximum 2^8 * 2^X
     assert np.array_equal(layer.mxfp8_round(w), w)
+
+
+def test_w4a8_activation_rounds_bf16_first():
+    # The expert reads its bf16-stored input: 1.0625 + 2^-12 becomes 1.0625
+    # in bf16, which sits exactly between the E4M3 neighbours 1 and 1.125 of
+    # its block (amax ~1.06: scale 2^-8) and goes to the even one, 1.  A
+    # direct MXFP8 rounding of the float64 value gives 1.125 instead.
+    v = np.zeros((1, 32))
+    v[0, 0] = 1.0625 + 2.0 ** -12
+    assert layer.bf16_round(v)[0, 0] == 1.0625
+    assert layer.mxfp8_round(v)[0, 0] == 1.125
+    assert layer.w4a8_activation(v)[0, 0] == 1.0
 
 
 def test_w4a8_layer_moves_by_the_activation_rounding():
