@@ -139,8 +139,8 @@ def test_layer_token_sampling_matches_full():
     assert np.allclose(full[[3, 17, 40]], some, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("w4a8", [False, True])
-def test_layer_composition_with_permutation_weights(w4a8):
+@pytest.mark.parametrize("w4a8,mx", [(False, False), (True, False), (False, True), (True, True)])
+def test_layer_composition_with_permutation_weights(w4a8, mx):
     """The whole layer on weights that are scaled permutation matrices, where
     every step reduces to gathers and scalar functions that can be written
     out by hand: z = x[sigma]; expert e: g = a_e z[pi_g], u = b_e z[pi_u],
@@ -152,7 +152,9 @@ def test_layer_composition_with_permutation_weights(w4a8):
     experts chosen by score are not the lowest indices.  With ``w4a8`` the
     expert inputs z and the SiTU-GLU outputs h (rows of 32, one MXFP8 block)
     are rounded to bf16 and then MXFP8 at exactly those two places, with the
-    separately pinned codec."""
+    separately pinned codec.  With ``mx`` the routed experts are given as
+    MXFP4 codes and E8M0 scales; a, b and c are then values that E2M1 times
+    a power of two holds exactly, so the expected output is unchanged."""
     rng = np.random.default_rng(11)
     T, d, lat, n, k, S = 5, 64, 32, 4, 2, 64
     eps = 1e-6
@@ -164,7 +166,11 @@ def test_layer_composition_with_permutation_weights(w4a8):
 
     x = rng.normal(0, 1.5, (T, d)).astype(np.float32).astype(np.float64)
     sigma = rng.permutation(d)[:lat]                       # latent = x[sigma]
-    a, b, c = rng.uniform(0.5, 3, n), rng.uniform(2, 40, n), rng.uniform(0.5, 2, n)
+    if mx:   # {1, 1.5} x 2^j: exact in MXFP4
+        a, b, c = np.array([1.5, 3.0, 0.75, 2.0]), np.array([3.0, 24.0, 12.0, 48.0]), \
+            np.array([0.75, 1.5, 1.0, 2.0])
+    else:
+        a, b, c = rng.uniform(0.5, 3, n), rng.uniform(2, 40, n), rng.uniform(0.5, 2, n)
     pg = [rng.permutation(lat) for _ in range(n)]
     pu = [rng.permutation(lat) for _ in range(n)]
     pd = [rng.permutation(lat) for _ in range(n)]
@@ -185,6 +191,10 @@ def test_layer_composition_with_permutation_weights(w4a8):
         ws_gate=gs * perm_matrix(S, d, q1), ws_up=us * perm_matrix(S, d, q2),
         ws_down=vs * perm_matrix(d, S, q3),
     )
+    if mx:
+        for key in ("w_gate", "w_uproj", "w_dn"):
+            codes, scales = workloads.mxfp4_quantize(torch.from_numpy(inp[key].reshape(-1, lat)))
+            inp[key] = (codes.reshape(n, lat, lat // 2), scales.reshape(n, lat, lat // 32))
     r = layer.route_layer(inp, k, mode=qb.MODE_FROZEN, bias=np.zeros(n))
     assert (r["idx"] == np.array([2, 0])).all()
     sc = 1.0 / (1.0 + np.exp(-p))
