@@ -44,6 +44,28 @@ def check_layer(shape, seed=0, qb_mode=qb.MODE_BATCH, bias=None, name=""):
     return got, ref
 
 
+def test_fp32_layer_on_permutation_weights():
+    """The HIP layer (fp32, frozen zero bias) on weights that are scaled
+    permutation matrices, against the output written out by hand
+    (``tests/perm_layer.py``); no oracle is involved."""
+    import torch
+    import perm_layer as P
+    import sparse_moe_ffn_sigmoid_amd as moe
+    inp, par = P.build()
+    shape = workloads.small_shape(T=P.T, d=P.D, latent=P.LAT, n=P.N, k=P.K, m=P.LAT,
+                                  shared=P.S, act="f32", routed="f32", eps=P.EPS)
+    tin = {key: torch.from_numpy(np.ascontiguousarray(v, np.float32)) for key, v in inp.items()}
+    announce("fp32 layer on permutation weights")
+    got = run_gpu(moe, shape, tin, bias=np.zeros(P.N), qb_mode=qb.MODE_FROZEN)
+    assert (got["idx"] == P.TOP).all()
+    sc = 1.0 / (1.0 + np.exp(-P.LOGIT_OFFSET[P.TOP]))
+    assert np.allclose(got["w"], (sc / sc.sum())[None, :], rtol=1e-6, atol=0)
+    want = P.expected(inp, par, got["idx"], got["w"].astype(np.float64))
+    err = rel_err(got["out"], want)
+    print(f"  max|diff|/rms = {err:.3e}", flush=True)
+    assert err <= TOL["f32"], err
+
+
 def test_tiny_fp32_layer():
     check_layer(workloads.SHAPES["tiny"], name="tiny fp32")
 

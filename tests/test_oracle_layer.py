@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 import torch
 
+import perm_layer
 import workloads
 from oracle import layer, qb
 
@@ -141,84 +142,26 @@ def test_layer_token_sampling_matches_full():
 
 @pytest.mark.parametrize("w4a8,mx", [(False, False), (True, False), (False, True), (True, True)])
 def test_layer_composition_with_permutation_weights(w4a8, mx):
-    """The whole layer on weights that are scaled permutation matrices, where
-    every step reduces to gathers and scalar functions that can be written
-    out by hand: z = x[sigma]; expert e: g = a_e z[pi_g], u = b_e z[pi_u],
-    y_e = c_e SiTU(g, u)[pi_d]; the latent sum over the chosen experts with
-    the renormalised raw scores, RMSNorm, a scatter back to width d, and the
-    shared MLP on the same permutation pattern.  Permutations (not
-    identities) make every transposed operand fail; distinct a, b, c per
-    expert make a swapped gate/up, a wrong expert or a wrong weight fail;
-    experts chosen by score are not the lowest indices.  With ``w4a8`` the
-    expert inputs z and the SiTU-GLU outputs h (rows of 32, one MXFP8 block)
-    are rounded to bf16 and then MXFP8 at exactly those two places, with the
+    """The whole layer on scaled permutation weights against its output
+    written out by hand (``tests/perm_layer.py``).  With ``w4a8`` the expert
+    inputs z and the SiTU-GLU outputs h (rows of 64, two MXFP8 blocks) are
+    rounded to bf16 and then MXFP8 at exactly those two places, with the
     separately pinned codec.  With ``mx`` the routed experts are given as
-    MXFP4 codes and E8M0 scales; a, b and c are then values that E2M1 times
-    a power of two holds exactly, so the expected output is unchanged."""
-    rng = np.random.default_rng(11)
-    T, d, lat, n, k, S = 5, 64, 32, 4, 2, 64
-    eps = 1e-6
-
-    def perm_matrix(rows, cols, src):      # M[i, src[i]] = 1: (M v)_i = v[src[i]]
-        M = np.zeros((rows, cols))
-        M[np.arange(rows), src] = 1.0
-        return M
-
-    x = rng.normal(0, 1.5, (T, d)).astype(np.float32).astype(np.float64)
-    sigma = rng.permutation(d)[:lat]                       # latent = x[sigma]
-    if mx:   # {1, 1.5} x 2^j: exact in MXFP4
-        a, b, c = np.array([1.5, 3.0, 0.75, 2.0]), np.array([3.0, 24.0, 12.0, 48.0]), \
-            np.array([0.75, 1.5, 1.0, 2.0])
-    else:
-        a, b, c = rng.uniform(0.5, 3, n), rng.uniform(2, 40, n), rng.uniform(0.5, 2, n)
-    pg = [rng.permutation(lat) for _ in range(n)]
-    pu = [rng.permutation(lat) for _ in range(n)]
-    pd = [rng.permutation(lat) for _ in range(n)]
-    tau = rng.permutation(d)[:lat]                         # out[tau[i]] += yhat[i]
-    q1, q2, q3 = rng.permutation(S), rng.permutation(S), rng.permutation(d)
-    gs, us, vs = 1.7, 9.0, 0.6
-    gamma = rng.uniform(0.5, 1.5, lat)
-    p = np.array([1.0, -0.5, 2.0, 0.3])                    # top-2 by score: experts 2, 0
-
-    inp = dict(
-        x=x, w_router=np.zeros((n, d)), logit_offset=p,
-        w_down=perm_matrix(lat, d, sigma),
-        w_gate=np.stack([a[e] * perm_matrix(lat, lat, pg[e]) for e in range(n)]),
-        w_uproj=np.stack([b[e] * perm_matrix(lat, lat, pu[e]) for e in range(n)]),
-        w_dn=np.stack([c[e] * perm_matrix(lat, lat, pd[e]) for e in range(n)]),
-        rms_gamma=gamma,
-        w_up=perm_matrix(lat, d, tau).T,
-        ws_gate=gs * perm_matrix(S, d, q1), ws_up=us * perm_matrix(S, d, q2),
-        ws_down=vs * perm_matrix(d, S, q3),
-    )
+    MXFP4 codes and E8M0 scales whose values E2M1 x 2^E holds exactly."""
+    inp, par = perm_layer.build(exact_mxfp4=mx)
     if mx:
         for key in ("w_gate", "w_uproj", "w_dn"):
-            codes, scales = workloads.mxfp4_quantize(torch.from_numpy(inp[key].reshape(-1, lat)))
+            codes, scales = workloads.mxfp4_quantize(torch.from_numpy(inp[key].reshape(-1, perm_layer.LAT)))
+            n, lat = perm_layer.N, perm_layer.LAT
             inp[key] = (codes.reshape(n, lat, lat // 2), scales.reshape(n, lat, lat // 32))
-    r = layer.route_layer(inp, k, mode=qb.MODE_FROZEN, bias=np.zeros(n))
-    assert (r["idx"] == np.array([2, 0])).all()
-    sc = 1.0 / (1.0 + np.exp(-p))
-    assert np.allclose(r["w"], (sc[[2, 0]] / sc[[2, 0]].sum())[None, :], rtol=1e-6, atol=0)
-    out = layer.layer_forward(inp, r["idx"], r["w"], eps, act_mxfp8=w4a8)
-
-    def act(v):
-        return layer.w4a8_activation(v[None, :])[0] if w4a8 else v
-
-    def situ(g, u):   # SiLU(4 tanh(g/4)) * 25 tanh(u/25)
-        gc = 4.0 * np.tanh(g / 4.0)
-        return gc / (1.0 + np.exp(-gc)) * 25.0 * np.tanh(u / 25.0)
-
-    want = np.zeros((T, d))
-    for t in range(T):
-        z = act(x[t, sigma])
-        y = np.zeros(lat)
-        for j, e in enumerate(r["idx"][t]):
-            h = act(situ(a[e] * z[pg[e]], b[e] * z[pu[e]]))
-            y += r["w"][t, j] * c[e] * h[pd[e]]
-        yhat = y / np.sqrt(np.mean(y * y) + eps) * gamma
-        want[t, tau] += yhat
-        hs = situ(gs * x[t, q1], us * x[t, q2])
-        want[t] += vs * hs[q3]
+    r = layer.route_layer(inp, perm_layer.K, mode=qb.MODE_FROZEN, bias=np.zeros(perm_layer.N))
+    assert (r["idx"] == perm_layer.TOP).all()
+    sc = 1.0 / (1.0 + np.exp(-perm_layer.LOGIT_OFFSET))
+    top = sc[perm_layer.TOP]
+    assert np.allclose(r["w"], (top / top.sum())[None, :], rtol=1e-6, atol=0)
+    out = layer.layer_forward(inp, r["idx"], r["w"], perm_layer.EPS, act_mxfp8=w4a8)
+    act = (lambda v: layer.w4a8_activation(v[None, :])[0]) if w4a8 else (lambda v: v)
+    want = perm_layer.expected(inp, par, r["idx"], r["w"], act)
     assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
 
 
