@@ -65,6 +65,10 @@ CASES = [
     ("pivot_k_n_minus_1", 300, 40, 39, 0.5),
     ("pivot_k63", 400, 200, 63, 0.5),
     ("pivot_tokens_per_wave", 7000, 128, 6, 1.0),
+    # fewer tokens than the four waves of one top-k block; every target 0 or 1
+    ("one_token", 1, 64, 4, 0.5),
+    ("three_tokens", 3, 64, 4, 0.5),
+    ("two_tokens_k3_width", 2, 896, 16, 0.5),
 ]
 
 
