@@ -76,6 +76,8 @@ def test_tiny_fp32_layer():
     dict(T=16, n=64, k=4),                                     # ~1 row per expert (small-M tile)
     dict(T=600, n=16, k=4),                                    # 150 rows per expert: one 160-row tile
     dict(T=1000, n=16, k=4, seed=7),                           # 250 rows: one 320-row tile (8 waves)
+    dict(T=1, n=64, k=4),                                      # one token: M = 1 everywhere
+    dict(T=3, n=16, k=2),
 ])
 def test_bf16_layer(kw):
     kw = dict(kw)
