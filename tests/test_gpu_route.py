@@ -103,6 +103,21 @@ def test_route_clustered_margins_parity(protos, copies, n, k, seed):
     assert (got["loads"] == qb.targets(s.shape[0], n, k)).all()
 
 
+@pytest.mark.parametrize("T,n,k,max_rounds", [(1000, 64, 4, 2), (600, 48, 3, 1), (2000, 128, 8, 3)])
+def test_route_round_cap_hands_over_to_paths(T, n, k, max_rounds):
+    """A small cap on the quantile rounds leaves tens of units of imbalance
+    to the augmenting paths (53 - 81 moves here); the result and every
+    counter must still match."""
+    s = scores(T, n, 0.5)
+    ref = qb.route_qb(s, k, max_rounds=max_rounds)
+    announce(f"round cap {max_rounds} T={T} n={n} k={k}")
+    got = gpu_route(s, k, max_rounds=max_rounds)
+    assert ref["info"][0] == max_rounds and ref["info"][1] == qb.STATUS_OK and ref["info"][3] > 0
+    assert tuple(int(v) for v in got["info"]) == tuple(ref["info"])
+    assert (got["idx"] == ref["idx"]).all() and (got["bias"] == ref["bias"]).all()
+    assert (got["loads"] == qb.targets(T, n, k)).all()
+
+
 def test_route_frozen_parity():
     s = scores(500, 64, 1.0, seed=3)
     bias = np.random.default_rng(0).normal(0, 0.2, 64)
