@@ -81,7 +81,13 @@ typedef enum {
 
 /* qb_info[4] (int32, device): rounds of quantile coordinate updates, status
  * (0 balanced / frozen, 1 not balanced within the limits, 2 bias left the
- * representable range), max |load - target| at exit, augmenting-path moves. */
+ * representable range), max |load - target| at exit, augmenting-path moves.
+ * Status 1 means that no bias balances the batch (equal scores on both sides
+ * of a target, e.g. duplicated tokens), or that the step cap was reached.
+ * That includes score rows so flat that more than 64 of one token's experts
+ * sit within the needed path length of its threshold, where the sparse edge
+ * list cannot hold the token's candidates.  The routing outputs are still
+ * the top-k under the returned bias. */
 enum { MOE_QB_STATUS_OK = 0, MOE_QB_STATUS_NOT_BALANCED = 1, MOE_QB_STATUS_BIAS_RANGE = 2 };
 
 typedef struct {
