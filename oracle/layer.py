@@ -30,7 +30,8 @@ MLP uses SiTU-GLU too (``hidden_act: situ`` is model-wide); RMSNorm eps = 1e-6
 with gain gamma; routed scaling factor 1.
 
 Parity status: sigmoid, SiTU-GLU, RMSNorm, MXFP4 decoding, the MXFP8 (E4M3)
-activation codec of the W4A8 experts and the shared-MLP merge are pinned by
+activation codec of the W4A8 experts, the MXFP4 (E2M1) activation codec of a
+W4A4 reading and the shared-MLP merge are pinned by
 tests (closed forms, bounds, identities, the OCP code tables, brute-force
 nearest values).  The pages print no worked example of the whole layer; its
 composition is pinned on weights that are scaled permutation matrices, where
@@ -160,6 +161,59 @@ def mxfp8_decode(codes, scales):
 def mxfp8_round(v):
     """Quantise to MXFP8 and decode."""
     return mxfp8_decode(*mxfp8_quantize(v))
+
+
+# MXFP4 activations (OCP Microscaling v1.0: E2M1 elements, one E8M0 scale per
+# 32 consecutive elements of a row), the W4A4 reading of the same deployment
+# passage: the experts' inputs z and h rounded to the routed weights' format.
+E2M1_MAX = 6.0             # 1.5 * 2^2, the largest E2M1 magnitude
+E2M1_EMAX = 2              # exponent of the largest power of two in E2M1
+
+
+def e2m1_encode(q):
+    """Nearest E2M1 code (sign bit 3, magnitude index 0..7 into
+    E2M1_VALUES) of float64 values: ties go to the even index (the value
+    with a zero mantissa bit), magnitudes above 6 saturate to 6."""
+    q = np.asarray(q, np.float64)
+    a = np.minimum(np.abs(q), E2M1_MAX)
+    dist = np.abs(a[..., None] - E2M1_VALUES)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best                       # one value, or two neighbours on a tie
+    idx = np.arange(8)
+    even = cand & (idx % 2 == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    return (code | np.where(np.signbit(q), 8, 0)).astype(np.uint8)
+
+
+def mxfp4_act_quantize(v):
+    """Rows of float64 values [rows, K] (K a multiple of 32) -> (E2M1 codes
+    [rows, K], one per byte, E8M0 scales [rows, K/32]).  Per block: shared
+    exponent floor(log2 amax) - 2, stored biased by 127 and clamped to
+    [0, 254] (an all-zero block takes 0); elements v / 2^X rounded by
+    :func:`e2m1_encode`."""
+    v = np.asarray(v, np.float64)
+    rows, K = v.shape
+    blk = v.reshape(rows, K // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.where(amax > 0, ex - 1 - E2M1_EMAX, -127)
+    sb = np.clip(X + 127, 0, 254).astype(np.uint8)
+    q = blk / np.ldexp(1.0, sb.astype(np.int64) - 127)[:, :, None]
+    return e2m1_encode(q).reshape(rows, K), sb
+
+
+def mxfp4_act_round(v):
+    """Quantise rows to MXFP4 and decode (codes one per byte)."""
+    codes, sb = mxfp4_act_quantize(v)
+    mag = E2M1_VALUES[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    return val * np.repeat(np.ldexp(1.0, sb.astype(np.int64) - 127), 32, axis=1)
+
+
+def w4a4_activation(v):
+    """What a W4A4 expert would read: the bf16-stored activation quantised
+    to MXFP4 (no HIP path implements this mode yet)."""
+    return mxfp4_act_round(bf16_round(v))
 
 
 def bf16_round(v):

@@ -232,6 +232,59 @@ def test_mxfp8_block_scale_rule_and_error_bound():
     assert np.array_equal(layer.mxfp8_round(w), w)
 
 
+# --- MXFP4 (E2M1) activations, the oracle side of a W4A4 reading ---------
+
+def test_e2m1_ties_and_saturation():
+    # midpoints of neighbouring E2M1 values go to the one with a zero
+    # mantissa bit (0, 1, 2, 4 are even, 0.5, 1.5, 3, 6 odd); above 6 saturates
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 1e9])
+    want = np.array([0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, 6.0])
+    for sign in (1.0, -1.0):
+        c = layer.e2m1_encode(sign * mids)
+        got = layer.E2M1_VALUES[c & 7] * np.where(c & 8, -1.0, 1.0)
+        assert (got == sign * want).all()
+        assert ((c & 8) != 0).all() == (sign < 0)
+
+
+def test_mxfp4_act_nearest_value_and_block_rule():
+    rng = np.random.default_rng(5)
+    v = rng.normal(0, 1, (64, 64)) * np.exp2(rng.integers(-20, 20, (64, 1)))
+    r = layer.mxfp4_act_round(v)
+    blk, rb = v.reshape(64, 2, 32), r.reshape(64, 2, 32)
+    amax = np.abs(blk).max(axis=2)
+    X = np.floor(np.log2(amax)) - 2                       # 6 * 2^X >= amax > 2^(X+2)
+    grid = layer.E2M1_VALUES[None, None, :] * np.exp2(X)[:, :, None]
+    nearest = np.abs(np.abs(blk)[..., None] - grid[:, :, None, :]).min(axis=-1)
+    # every result is a grid value, and no grid value is nearer (brute force)
+    assert (np.abs(np.abs(rb)[..., None] - grid[:, :, None, :]).min(axis=-1) == 0).all()
+    assert np.array_equal(np.abs(np.abs(blk) - np.abs(rb)), nearest)
+    assert (np.sign(rb) * np.sign(blk) >= 0).all()
+    # representable values round-trip exactly
+    exact = layer.E2M1_VALUES[rng.integers(0, 8, (4, 32))] * np.where(rng.random((4, 32)) < .5, -1, 1)
+    exact[:, 0] = 6.0                                      # fixes the block scale at 2^0
+    assert (layer.mxfp4_act_round(exact * 2.0 ** -7) == exact * 2.0 ** -7).all()
+
+
+def test_mxfp4_act_matches_the_weight_quantiser():
+    # two independent implementations of the same OCP rule (the seeded weight
+    # generator's quantiser in torch float32, the oracle's in float64)
+    rng = np.random.default_rng(9)
+    v = (rng.normal(0, 1, (16, 128)) * np.exp2(rng.integers(-8, 8, (16, 1)))).astype(np.float32)
+    codes, scales = workloads.mxfp4_quantize(torch.from_numpy(v))
+    assert np.array_equal(layer.mxfp4_decode(codes.numpy(), scales.numpy()),
+                          layer.mxfp4_act_round(v.astype(np.float64)))
+
+
+def test_w4a4_activation_rounds_bf16_first():
+    # 1.25 + 2^-12 is 1.25 in bf16; in a block with amax ~1.25 (scale 2^-2)
+    # that is 5 units, the midpoint of 4 and 6, which goes to 4 (1.0); the
+    # float64 value rounds up to 6 units (1.5) instead.
+    v = np.zeros((1, 32))
+    v[0, 0] = 1.25 + 2.0 ** -12
+    assert layer.mxfp4_act_round(v)[0, 0] == 1.5
+    assert layer.w4a4_activation(v)[0, 0] == 1.0
+
+
 def test_w4a8_activation_rounds_bf16_first():
     # The expert reads its bf16-stored input: 1.0625 + 2^-12 becomes 1.0625
     # in bf16, which sits exactly between the E4M3 neighbours 1 and 1.125 of
