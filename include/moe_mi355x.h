@@ -27,10 +27,9 @@
  *     auxiliary non-blocking stream (default priority) with two events,
  *     created on first use, on which moe_latent_forward runs the
  *     routing-independent shared branch (forked from and joined back into
- *     `stream`, under a per-device mutex held for the call); per host thread
- *     and device, two pinned 64-byte words and two events through which the
- *     balancing loop reads the phase of the previous batch of steps while
- *     the next batch runs; the opt-in stage-timing records.
+ *     `stream`, under a per-device mutex held for the call); per device, the
+ *     compute-unit count and wall-clock rate that size the routing loop's
+ *     grid and its wait limit; the opt-in stage-timing records.
  *   - Matrices are row-major [out_features][in_features] (K contiguous);
  *     activations are [T][features].  bf16 values are passed as raw 16-bit
  *     patterns.  MXFP4 weights: codes uint8 [rows][K/2] (element 2i in the
@@ -38,9 +37,12 @@
  *     magnitudes 0,.5,1,1.5,2,3,4,6) and one E8M0 scale byte per 32
  *     consecutive K elements, uint8 [rows][K/32] (value * 2^(byte-127)).
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
- *     Work is enqueued on it.  In MOE_QB_BATCH mode the balancing loop reads
- *     small control words back to the host, so the call synchronises
- *     `stream` while it runs; MOE_QB_FROZEN calls never synchronise.
+ *     Work is enqueued on it and no call waits on the host.  Routing (every
+ *     mode) runs as one persistent launch of at most one block per compute
+ *     unit whose blocks wait for each other through device-memory
+ *     barriers; work on other streams may delay it but must not depend on
+ *     it.  A barrier wait longer than 2 s ends the loop with qb_info status
+ *     3 (aborted) and leaves the routing outputs undefined.
  *   - Return value: MOE_OK or a negative moe_status for invalid arguments,
  *     unsupported combinations, a too-small workspace or a HIP error.  Nothing
  *     is launched when validation fails.  The outcome of balancing (rounds,
@@ -88,7 +90,12 @@ typedef enum {
  * sit within the needed path length of its threshold, where the sparse edge
  * list cannot hold the token's candidates.  The routing outputs are still
  * the top-k under the returned bias. */
-enum { MOE_QB_STATUS_OK = 0, MOE_QB_STATUS_NOT_BALANCED = 1, MOE_QB_STATUS_BIAS_RANGE = 2 };
+enum {
+  MOE_QB_STATUS_OK = 0,
+  MOE_QB_STATUS_NOT_BALANCED = 1,
+  MOE_QB_STATUS_BIAS_RANGE = 2,
+  MOE_QB_STATUS_ABORTED = 3 /* a grid-barrier wait timed out: outputs undefined */
+};
 
 typedef struct {
   int32_t T;             /* tokens in the batch (>= 0) */
@@ -165,7 +172,6 @@ int moe_route_qb(const float* scores, int32_t T, int32_t n, int32_t k, int32_t m
  *   qb_info  [4] i32: updates made, status (0 balanced, 1 not balanced after
  *            max_rounds, 2 bias left the representable range), max
  *            |load - target| at exit, 0
- * Synchronises `stream` while it runs (it polls the loop's phase word).
  */
 int moe_route_sign(const float* scores, int32_t T, int32_t n, int32_t k, double step,
                    int32_t max_rounds, double* bias, int32_t* topk_idx, float* topk_w,

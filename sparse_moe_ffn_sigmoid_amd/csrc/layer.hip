@@ -492,12 +492,21 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     MOE_HIP_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
     sst = side->s;
   }
-  // Beside balancing rounds the side GEMMs leave room on every CU for the
-  // routing kernels (measured at T = 4096: 12.73 -> 12.54 ms per layer); at
-  // larger T the slower shared tiles cost what the overlap saves, so they
-  // take the tiles that run fastest alone.
-  const int side_hint =
-      side && s.qb_mode == MOE_QB_BATCH && T <= 8192 ? gemm::BM_SHARE : 128;
+  // 3. routing (QB or frozen bias), enqueued before the shared-branch GEMMs:
+  // the balancing loop is one persistent launch that takes whole CUs; with
+  // the side stream running beside it, it takes 1/cu_share of them and the
+  // shared-branch GEMMs run on the rest.
+  {
+    prof::Scope sc(prof::ST_ROUTING, st);
+    // Above 8192 tokens the side-stream GEMMs are long enough that the
+    // batch loop is given half of the compute units and the GEMMs the rest;
+    // below that the loop is short and takes every unit.
+    const int cu_share = side && s.qb_mode == MOE_QB_BATCH && T > 8192 ? 2 : 1;
+    if ((rc = route_run(route_scores, T, n, k, s.qb_mode, s.qb_max_rounds, bias, idx, w, f.loads,
+                        info, f.route, st, cu_share)) != MOE_OK)
+      return rc;
+  }
+  const int side_hint = 128;
   if (T > 0) {
     gemm::Params p{};
     p.M = T;
@@ -536,14 +545,6 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     }
   }
   if (side) MOE_HIP_CHECK(hipEventRecord(side->join, side->s));
-
-  // 3. routing (QB or frozen bias)
-  {
-  prof::Scope sc(prof::ST_ROUTING, st);
-  if ((rc = route_run(route_scores, T, n, k, s.qb_mode, s.qb_max_rounds, bias, idx, w, f.loads,
-                      info, f.route, st)) != MOE_OK)
-    return rc;
-  }
   if (loads_out)
     MOE_HIP_CHECK(hipMemcpyAsync(loads_out, f.loads, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, st));
   if (T == 0) return MOE_OK;
