@@ -107,6 +107,7 @@ def cpu_baseline(inp, shape, sample_tokens):
     per_token = t_route / shape.T + t_layer / sample_tokens
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "logical_cpus": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": (f"oracle router + QB on the full batch of {shape.T} tokens "
                        f"({t_route:.1f} s) and the float64 layer on {sample_tokens} tokens "
                        f"({t_layer:.1f} s); tokens/s = 1 / (route_s/T + layer_s/sample)")}
@@ -145,15 +146,119 @@ def sign_baseline(moe, sh, w, x, bias0, ws, shape):
     return out
 
 
+QB_METRIC = "Quantile Balancing routing tokens/s on 1 MI355X; HBM GB/s vs peak"
+
+
+def qb_scores(T, n, offset_std, seed):
+    """Sigmoid scores (fp32) of the routing-only workload's seeded logits."""
+    import numpy as np
+
+    import workloads
+    z = workloads.qb_logits(T, n, offset_std, seed).astype(np.float64)
+    return (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+
+
+def qb_cpu_baseline(cfg, sample_tokens):
+    """The oracle's routing (Quantile Balancing on the host, float64 keys) on a
+    batch of ``sample_tokens`` tokens of the same distribution."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import qb
+    s = qb_scores(sample_tokens, cfg["n"], cfg["offset_std"], seed=1)
+    t0 = time.perf_counter()
+    r = qb.route_qb(s, cfg["k"])
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "logical_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": (f"oracle route_qb on {sample_tokens} tokens x {cfg['n']} experts, "
+                       f"k={cfg['k']} ({dt:.1f} s, {r['info'][0]} rounds + "
+                       f"{r['info'][3]} moves)")}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def run_qb(args):
+    """Routing-only workload: Quantile Balancing of T=57344 tokens over n=896
+    experts, k=16, scores from N(0,1) logits plus a per-expert N(0, 0.5^2)
+    offset.  One step = one moe_route_qb call (bias from zero)."""
+    import torch
+
+    import sparse_moe_ffn_sigmoid_amd as moe
+    import workloads
+
+    cfg = workloads.QB_SHAPE
+    T, n, k = cfg["T"], cfg["n"], cfg["k"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    scores = torch.from_numpy(qb_scores(T, n, cfg["offset_std"], seed=0)).to(dev)
+    ws = torch.empty(max(moe.route_workspace_bytes(T, n, k), 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        return moe.route_qb(scores, k, workspace=ws)
+
+    for _ in range(args.warmup):
+        r = step()
+    torch.cuda.synchronize()
+    moe.stage_timing(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        r = step()
+    end.record()
+    torch.cuda.synchronize()
+    stages = moe.stage_times()
+    moe.stage_timing(False)
+    ms_per_step = start.elapsed_time(end) / args.steps
+    info = [int(v) for v in r["info"].cpu()]
+    r_ms, r_n = stages["routing"]
+    avg_ms = r_ms / max(r_n, 1)
+    # one read of the fp32 scores per quantile round or augmenting-path move,
+    # one for the final pass, and the idx / w outputs
+    passes = info[0] + info[3] + 1
+    algo = passes * 4.0 * T * n + 8.0 * T * k
+    roof = {"bound": "hbm", "achieved": algo / (avg_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    rec = {
+        "metric": QB_METRIC, "value": T / (ms_per_step / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) logits + per-expert N(0,0.25) offsets, fp32 sigmoid)",
+        "config": {"workload": "qb_routing_57344x896", "T": T, "experts": n, "top_k": k,
+                   "offset_std": cfg["offset_std"], "qb": "batch"},
+        "roofline": dict(roof, kernel="routing loop (one persistent launch per call)",
+                         bytes_per_launch=algo, avg_ms=avg_ms, passes=passes),
+        "qb_info": info,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = qb_cpu_baseline(cfg, args.cpu_sample_qb_tokens)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="k3_prefill",
-                    choices=["k3_prefill", "k3_decode", "k3_mxfp4", "k3_mxfp4_a8", "k3_prefill_16k"])
+                    choices=["k3_prefill", "k3_decode", "k3_mxfp4", "k3_mxfp4_a8", "k3_prefill_16k",
+                             "qb"])
     ap.add_argument("--qb", default="batch", choices=["batch", "frozen"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=2)
+    ap.add_argument("--cpu-sample-qb-tokens", type=int, default=8192,
+                    help="tokens of the routing-only oracle sample (--workload qb)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sign-baseline", action="store_true",
                     help="also route this batch's scores with the fixed-step sign update "
@@ -167,6 +272,10 @@ def main():
         print("bench.py measures one MI355X: the layer here runs on a single GPU "
               "(no sharding or collectives); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "qb":
+        run_qb(args)
+        return
 
     import torch
 

@@ -36,6 +36,9 @@
  *     low nibble of byte i, 2i+1 in the high nibble, bit 3 = sign, E2M1
  *     magnitudes 0,.5,1,1.5,2,3,4,6) and one E8M0 scale byte per 32
  *     consecutive K elements, uint8 [rows][K/32] (value * 2^(byte-127)).
+ *     Every byte 0..254 is decoded exactly; a product above the bf16 range
+ *     (bytes 253 and 254 with large codes) becomes an infinity, and byte 255
+ *     (NaN in the format) gives NaN.
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *     Work is enqueued on it and no call waits on the host.  Routing (every
  *     mode) runs as one persistent launch of at most one block per compute
@@ -196,6 +199,25 @@ int moe_latent_forward(const moe_shape_t* shape, const moe_weights_t* weights, c
                        void* out, double* bias, const float* scores_in, float* scores_out,
                        int32_t* topk_idx, float* topk_w, int32_t* loads, int32_t* qb_info,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_mxfp8_quantize -- the on-the-fly MXFP8 rounding of the routed experts'
+ * inputs in MOE_MXFP4_A8 (deployment of the routed experts in microscaling
+ * formats: xhh.club page, 延伸解读 "参数规模与部署要点"; element and scale
+ * formats of the OCP Microscaling v1.0 specification).
+ *   x      [rows][K] bf16 (raw 16-bit patterns), 16-byte aligned, read only
+ *   codes  [rows][K] u8 E4M3 codes (sign bit 7, 4-bit exponent with bias 7,
+ *          3-bit mantissa), 8-byte aligned
+ *   scales [rows][K/32] u8 E8M0 (value 2^(byte-127))
+ *   K      a multiple of 32; rows >= 0 (0: nothing is launched)
+ * Per block of 32 consecutive elements of a row: X = floor(log2 amax) - 8,
+ * scale byte X + 127 clamped to [0, 254] (0 for an all-zero block); each
+ * element v / 2^(byte-127) rounded to the nearest E4M3 value, ties to the
+ * even mantissa, magnitudes beyond 448 saturating to 448.  Enqueued on
+ * `stream`; returns MOE_EINVAL for bad sizes, NULL or misaligned pointers.
+ */
+int moe_mxfp8_quantize(const void* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                       void* stream);
 
 /* Static description of a moe_status value; never NULL. */
 const char* moe_status_str(int status);

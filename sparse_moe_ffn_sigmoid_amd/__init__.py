@@ -26,7 +26,7 @@ MOE_QB_FROZEN, MOE_QB_BATCH = 0, 1
 EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_route_sign",
             "moe_forward_workspace_bytes",
             "moe_latent_forward", "moe_status_str", "moe_stage_timing", "moe_stage_times",
-            "moe_stage_name")
+            "moe_stage_name", "moe_mxfp8_quantize")
 
 
 class MoeShape(ctypes.Structure):
@@ -66,6 +66,8 @@ _lib.moe_stage_times.argtypes = [_vp, _vp, _i32]
 _lib.moe_stage_times.restype = ctypes.c_int
 _lib.moe_stage_name.argtypes = [ctypes.c_int]
 _lib.moe_stage_name.restype = ctypes.c_char_p
+_lib.moe_mxfp8_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
+_lib.moe_mxfp8_quantize.restype = ctypes.c_int
 
 
 class MoeError(RuntimeError):
@@ -152,6 +154,19 @@ def route_sign(scores: torch.Tensor, k: int, step: float, max_rounds: int,
     if st != 0:
         raise MoeError(st, "moe_route_sign")
     return dict(idx=idx, w=w, loads=loads, bias=b, info=info)
+
+
+def mxfp8_quantize(x: torch.Tensor):
+    """bf16 rows [rows, K] (device, K a multiple of 32) -> (E4M3 codes uint8
+    [rows, K], E8M0 scales uint8 [rows, K/32]), one scale per 32 elements."""
+    rows, K = x.shape
+    _check(x, "x", torch.bfloat16, (rows, K), x.device)
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    st = _lib.moe_mxfp8_quantize(_ptr(x), rows, K, _ptr(codes), _ptr(scales), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_mxfp8_quantize")
+    return codes, scales
 
 
 def make_shape(T, d, latent, n, k, inter, shared_inter, act_dtype, routed_dtype,

@@ -94,19 +94,45 @@ __device__ __forceinline__ uint32_t e2m1_bits(uint32_t m) {
   return ((126u + (m >> 1)) << 7) | ((m & 1u) << 6);
 }
 
-// 8 MXFP4 codes (one 32-bit word, element 0 in the low nibble) -> 8 bf16.
-__device__ __forceinline__ u32x4_t decode8(uint32_t q, int32_t exp_add) {
+// 8 MXFP4 codes (one 32-bit word, element 0 in the low nibble) times the
+// E8M0 scale 2^(sbyte-127) -> 8 bf16.  For scale bytes 2..252 every product
+// is a normal bf16, and the scale is added to the exponent field; outside
+// that range the products are formed in fp32 (exact: an E2M1 value has two
+// significant bits, so 2^-128 and up are representable, and products above
+// the bf16 range become infinities); byte 255, NaN in the format, gives NaN.
+__device__ __forceinline__ u32x4_t decode8(uint32_t q, int32_t sbyte) {
   u32x4_t out;
+  if (sbyte >= 2 && sbyte <= 252) {
+    const int32_t exp_add = (sbyte - 127) << 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t pair = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t nib = (q >> (8 * i + 4 * h)) & 15u;
+        const uint32_t mag = nib & 7u;
+        uint32_t bits = e2m1_bits(mag);
+        bits = mag ? static_cast<uint32_t>(static_cast<int32_t>(bits) + exp_add) : 0u;
+        bits |= (nib & 8u) << 12;
+        pair |= bits << (16 * h);
+      }
+      out[i] = pair;
+    }
+    return out;
+  }
+  // 2^(sbyte-127) in fp32: 2^-127 is a subnormal
+  const float sc = sbyte == 255 ? __uint_as_float(0x7FC00000u)
+                                : __uint_as_float(sbyte ? (static_cast<uint32_t>(sbyte) << 23)
+                                                        : 0x00400000u);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t pair = 0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t nib = (q >> (8 * i + 4 * h)) & 15u;
-      const uint32_t mag = nib & 7u;
-      uint32_t bits = e2m1_bits(mag);
-      bits = mag ? static_cast<uint32_t>(static_cast<int32_t>(bits) + exp_add) : 0u;
-      bits |= (nib & 8u) << 12;
+      const float v = __uint_as_float(e2m1_bits(nib & 7u) << 16) * sc;
+      // v has at most two significant bits: dropping the low half is exact
+      const uint32_t bits = (__float_as_uint(v) >> 16) | ((nib & 8u) << 12);
       pair |= bits << (16 * h);
     }
     out[i] = pair;
@@ -252,10 +278,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16(Params p) {
       for (int i = 0; i < B_CH; ++i) {
         const int c = tid + NTHREADS * i;
         const int r = c >> 1, half = c & 1;
-        const int32_t ea = (rsc[i] - 127) << 7;
 #pragma unroll
         for (int w = 0; w < 4; ++w)
-          *reinterpret_cast<u32x4_t*>(b_s + r * LDK + half * 32 + w * 8) = decode8(rb[i][w], ea);
+          *reinterpret_cast<u32x4_t*>(b_s + r * LDK + half * 32 + w * 8) = decode8(rb[i][w], rsc[i]);
       }
     }
   };
@@ -720,9 +745,9 @@ __device__ __forceinline__ bf16x8_t decode8_hw(uint32_t q, float scale) {
   return out;
 }
 
-// E8M0 byte -> fp32 2^(e-127) (e = 0 gives the subnormal 2^-127)
+// E8M0 byte -> fp32 2^(e-127) (e = 0 gives the subnormal 2^-127, 255 NaN)
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+  return __uint_as_float(e == 255u ? 0x7FC00000u : e ? (e << 23) : 0x00400000u);
 }
 
 // NW: waves per block.  SR: the E8M0 scales travel through the ring (4 bytes

@@ -676,3 +676,21 @@ extern "C" int moe_latent_forward(const moe_shape_t* shape, const moe_weights_t*
   return moe::layer::forward(*shape, *weights, x, out, bias, scores_in, scores_out, topk_idx,
                              topk_w, loads, qb_info, fw, static_cast<hipStream_t>(stream));
 }
+
+extern "C" int moe_mxfp8_quantize(const void* x, int64_t rows, int64_t K, uint8_t* codes,
+                                  uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_EINVAL;
+  if (rows > 0 && (!x || !codes || !scales)) return MOE_EINVAL;
+  if (rows > 0 && (reinterpret_cast<uintptr_t>(x) % 16 != 0 ||
+                   reinterpret_cast<uintptr_t>(codes) % 8 != 0))
+    return MOE_EINVAL;
+  if (rows > (int64_t(1) << 56) / K) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  const int64_t nblk = rows * (K / 32);
+  hipLaunchKernelGGL(moe::layer::mx8_quantize,
+                     dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 63) / 64, 8192))), dim3(256),
+                     0, static_cast<hipStream_t>(stream), static_cast<const moe::bf16_t*>(x), nblk,
+                     codes, scales);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}

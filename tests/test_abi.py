@@ -61,6 +61,20 @@ def test_route_validation_on_host():
     assert lib.moe_route_qb(*args(100, 64, 4, wsb=need - 1)) == -3
 
 
+def test_mxfp8_quantize_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    assert lib.moe_mxfp8_quantize(fake, 4, 48, fake, fake, None) == -1       # K % 32
+    assert lib.moe_mxfp8_quantize(fake, 4, 0, fake, fake, None) == -1
+    assert lib.moe_mxfp8_quantize(fake, -1, 64, fake, fake, None) == -1
+    assert lib.moe_mxfp8_quantize(None, 4, 64, fake, fake, None) == -1
+    assert lib.moe_mxfp8_quantize(fake, 4, 64, fake, None, None) == -1
+    assert lib.moe_mxfp8_quantize(ctypes.c_void_p((1 << 20) + 2), 4, 64, fake, fake, None) == -1
+    assert lib.moe_mxfp8_quantize(fake, 4, 64, ctypes.c_void_p((1 << 20) + 4), fake, None) == -1
+    assert lib.moe_mxfp8_quantize(None, 0, 64, None, None, None) == 0       # nothing to do
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     import subprocess
     import sys

@@ -20,10 +20,12 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 1e-1, "mxfp4_a8": 1e-1}
 
 
-def check_layer(shape, seed=0, qb_mode=qb.MODE_BATCH, bias=None, name=""):
+def check_layer(shape, seed=0, qb_mode=qb.MODE_BATCH, bias=None, name="", edit=None):
     import sparse_moe_ffn_sigmoid_amd as moe
     announce(f"layer {name} {shape}")
     inp = workloads.layer_inputs(shape, "cpu", seed=seed, random_gamma=True)
+    if edit is not None:
+        edit(inp)
     s = oracle_scores(inp)
     ref = qb.route_qb(s, shape.k, bias=bias, mode=qb_mode)
     got = run_gpu(moe, shape, inp, scores_in=s, bias=bias, qb_mode=qb_mode)
@@ -106,6 +108,43 @@ def test_mxfp4_layer():
 ])
 def test_mxfp4_layer_pipelined(kw):
     check_layer(workloads.small_shape(routed="mxfp4", **kw), seed=5, name=f"mxfp4 {kw}")
+
+
+def extreme_scale_bytes(inp, seed=0):
+    """Scale bytes at the ends of the E8M0 range: 0 and 1 (products below
+    the normal bf16 range) on a tenth of the routed blocks, 253 and 254 on
+    blocks whose codes are all zero (+0 or -0)."""
+    rng = np.random.default_rng(seed)
+    for key in ("w_gate", "w_uproj", "w_dn"):
+        codes, scales = (t.clone() for t in inp[key])
+        sc = scales.numpy()
+        cd = codes.numpy()
+        r = rng.random(sc.shape)
+        sc[r < 0.1] = rng.integers(0, 2, size=int((r < 0.1).sum()))
+        big = r > 0.97
+        sc[big] = rng.integers(253, 255, size=int(big.sum()))
+        blk = cd.reshape(*sc.shape, 16)
+        blk[big] = rng.choice(np.array([0x00, 0x88, 0x08, 0x80], np.uint8), size=(int(big.sum()), 16))
+        inp[key] = (codes, scales)
+
+
+# Both MXFP4 decoders (bf16 by exponent arithmetic in the register-staged
+# kernel, the hardware conversion in the pipelined one) over the whole E8M0
+# byte range that a finite product allows
+@pytest.mark.parametrize("kw", [
+    dict(T=300, k=4),                                          # register-staged kernel
+    dict(T=300, k=4, d=1024, latent=512, m=512),               # pipelined kernel, 32-row tiles
+    dict(T=1200, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 320-row tiles
+])
+def test_mxfp4_layer_extreme_scale_bytes(kw):
+    check_layer(workloads.small_shape(routed="mxfp4", **kw), seed=4,
+                name=f"mxfp4 extreme scales {kw}", edit=extreme_scale_bytes)
+
+
+def test_w4a8_layer_extreme_scale_bytes():
+    shape = workloads.small_shape(routed="mxfp4_a8", T=300, n=16, k=4, d=1024, latent=512,
+                                  m=512, shared=256)
+    check_layer(shape, seed=4, name="w4a8 extreme scales", edit=extreme_scale_bytes)
 
 
 # W4A8: MXFP4 weights times MXFP8 activations on the scaled MFMA (320-row

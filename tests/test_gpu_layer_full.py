@@ -29,7 +29,7 @@ TOL = {"bf16": 2e-2, "mxfp4": 1e-1, "mxfp4_a8": 1e-1}
 SCALES = {"w_gate": "s_gate", "w_uproj": "s_uproj", "w_dn": "s_dn"}
 
 
-def forward_as_benchmarked(shape, qb_mode):
+def forward_as_benchmarked(shape, qb_mode, calls=1):
     import sparse_moe_ffn_sigmoid_amd as moe
     dev = torch.device("cuda:0")
     inp = workloads.layer_inputs(shape, dev, seed=0)
@@ -47,10 +47,13 @@ def forward_as_benchmarked(shape, qb_mode):
                         moe.MOE_BF16, routed, shape.eps, qb_mode, 64)
     ws = torch.empty(moe.forward_workspace_bytes(sh), dtype=torch.uint8, device=dev)
     bias0 = torch.zeros(shape.n, dtype=torch.float64, device=dev)
-    r = moe.latent_forward(sh, w, inp["x"], bias=bias0, workspace=ws, want_scores=True)
-    torch.cuda.synchronize()
-    return inp, {k: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy()
-                 for k, v in r.items()}
+    res = []
+    for _ in range(calls):
+        r = moe.latent_forward(sh, w, inp["x"], bias=bias0, workspace=ws, want_scores=True)
+        torch.cuda.synchronize()
+        res.append({k: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy()
+                    for k, v in r.items()})
+    return (inp, res[0]) if calls == 1 else (inp, res)
 
 
 def check_routing(shape, got, qb_mode):
@@ -92,6 +95,18 @@ def check_routing(shape, got, qb_mode):
 ])
 def test_full_size_layer_sampled(wl, qb_mode):
     check_sampled(workloads.SHAPES[wl], qb_mode, wl)
+
+
+def test_forward_deterministic_k3_prefill():
+    """Two calls on the same inputs and workspace give bitwise-equal results
+    (no atomics decide an output value or its order)."""
+    announce("determinism k3_prefill")
+    inp, (a, b) = forward_as_benchmarked(workloads.SHAPES["k3_prefill"], qb.MODE_BATCH, calls=2)
+    for key in a:
+        assert a[key].dtype == b[key].dtype
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+    del inp
+    torch.cuda.empty_cache()
 
 
 # K3 widths with fewer experts, so that each expert holds 150, 300 or 512 rows:
