@@ -47,6 +47,15 @@ Readings taken where the pages are open
    balances every expert yields the *same* selection (see
    :func:`assignment_objective`), so the completion step changes no routing
    result, only how it is reached.
+   The returned bias does depend on the schedule, which is fixed by these
+   parameters: every unbalanced expert updated in each round from the same
+   start-of-round biases; stall window ``stall_rounds = 3`` (a round that
+   does not bring the unbalanced count below its best so far adds one; the
+   third in a row ends the rounds); at most ``max_rounds = 64`` rounds and
+   ``max_sap = 4096`` moves; each move takes the nearest underloaded expert
+   (ties: lowest index) and its path of lowest predecessors.  The edge-cost
+   bound of the sparse relaxation (start 2^30, x16 per retry, full
+   relaxation past 2^44) changes no result.
 5. Common offset.  After balancing, ``floor(sum(bfx)/n)`` is subtracted from
    every bias; selection is unchanged (every key of a token moves together).
 6. Output order.  ``idx[t]`` lists the chosen experts by descending raw score,
@@ -263,7 +272,8 @@ def shortest_paths_edges(A, B, rho, over, under):
             return packed
 
 
-SPARSE_DELTA = 1 << 30
+SPARSE_DELTA = 1 << 30        # first edge-cost bound of the sparse relaxation
+SPARSE_DELTA_MAX = 1 << 44    # beyond it the full relaxation is used
 
 
 def sap_step(sfx, bfx, k, C, state=None, sparse=True):
@@ -276,23 +286,25 @@ def sap_step(sfx, bfx, k, C, state=None, sparse=True):
     it.  Returns the new biases, or None when no underloaded expert is
     reachable.  With ``sparse`` the distances come from the edges of reduced
     cost <= delta (delta grows 16x until D* <= delta), which gives the same
-    distances and predecessors up to D* as the full relaxation.
+    distances and predecessors up to D* as the full relaxation; once delta
+    has passed SPARSE_DELTA_MAX without reaching D*, the full relaxation
+    decides.  The result therefore never depends on delta.
     """
     th_k, th_k1, S = state if state is not None else select(sfx, bfx, k)
     L = S.sum(axis=0)
     over, under = L > C, L < C
+    packed = None
     if sparse:
         delta = SPARSE_DELTA
-        while True:
+        while delta <= SPARSE_DELTA_MAX:
             A, B, rho = sparse_edges(sfx, bfx, S, th_k, th_k1, delta)
-            packed = shortest_paths_edges(A, B, rho, over, under)
-            D = int(np.where(under, packed >> IDX_BITS, DIST_INF).min())
+            cand = shortest_paths_edges(A, B, rho, over, under)
+            D = int(np.where(under, cand >> IDX_BITS, DIST_INF).min())
             if D <= delta:
+                packed = cand
                 break
-            if delta >= (1 << 44):
-                return None
             delta *= 16
-    else:
+    if packed is None:
         packed = shortest_paths(sfx, bfx, S, over, under)
     d = packed >> IDX_BITS
     pred = packed & (MAX_EXPERTS - 1)

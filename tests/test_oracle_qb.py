@@ -92,6 +92,101 @@ def test_lp_optimum(T, n, k, seed):
     assert (got == (x > 0.5)).all()
 
 
+def lp_selection(s, k):
+    """The balanced-assignment LP (sparse constraints): row sums k, column
+    sums C, 0 <= x <= 1, maximise sum x*s.  Totally unimodular, so the HiGHS
+    vertex is integral; returns the boolean selection."""
+    from scipy.sparse import coo_matrix
+    T, n = s.shape
+    C = qb.targets(T, n, k)
+    t_idx = np.repeat(np.arange(T), n)
+    e_idx = np.tile(np.arange(n), T)
+    cols = np.arange(T * n)
+    A_eq = coo_matrix((np.ones(2 * T * n), (np.concatenate([t_idx, T + e_idx]),
+                                             np.concatenate([cols, cols]))),
+                      shape=(T + n, T * n)).tocsr()
+    b_eq = np.concatenate([np.full(T, k), C])
+    res = linprog(-s.astype(np.float64).ravel(), A_eq=A_eq, b_eq=b_eq, bounds=(0, 1),
+                  method="highs")
+    assert res.status == 0
+    x = res.x.reshape(T, n)
+    assert np.abs(x - np.round(x)).max() < 1e-6
+    return x > 0.5
+
+
+@pytest.mark.parametrize("max_rounds", [64, 1, 0])
+def test_lp_optimum_independent_of_schedule(max_rounds):
+    """The LP solved from scratch at T=600, n=32, k=4: the selection must be
+    its optimum whether balance comes mostly from quantile rounds or mostly
+    (max_rounds 1, 0) from augmenting paths."""
+    T, n, k = 600, 32, 4
+    s = rand_scores(T, n, 41, skew=0.7)
+    r = qb.route_qb(s, k, max_rounds=max_rounds)
+    assert r["info"][1] == qb.STATUS_OK
+    if max_rounds < 64:
+        assert r["info"][3] > 20          # many moves: the schedule differs
+    assert (sel_matrix(r["idx"], n) == lp_selection(s, k)).all()
+
+
+@pytest.mark.parametrize("max_rounds", [64, 0])
+def test_k1_hungarian_large(max_rounds):
+    """k = 1 at T=2000, n=64 against the textbook assignment solver with
+    expert slots replicated (no token can take two slots of one expert when
+    k = 1, so the assignment problem is exactly the balanced routing)."""
+    T, n = 2000, 64
+    s = rand_scores(T, n, 43, skew=0.7)
+    r = qb.route_qb(s, 1, max_rounds=max_rounds)
+    assert r["info"][1] == qb.STATUS_OK
+    C = qb.targets(T, n, 1)
+    slots = np.repeat(np.arange(n), C)
+    rows, cols = linear_sum_assignment(-s.astype(np.float64)[:, slots])
+    assert (r["idx"][:, 0] == slots[cols[np.argsort(rows)]]).all()
+
+
+def test_selection_same_across_schedules_k3_like():
+    """T=2000, n=64, k=4: quantile rounds, a round cap of 2 and pure
+    augmenting paths reach different biases but the same selection, and
+    each bias certifies it (the selection is the top-k under it and every
+    load equals its target)."""
+    T, n, k = 2000, 64, 4
+    s = rand_scores(T, n, 41, skew=0.7)
+    sfx = qb.to_fixed(s)
+    C = qb.targets(T, n, k)
+    runs = [qb.route_qb(s, k, max_rounds=m) for m in (64, 2, 0)]
+    assert len({tuple(r["bfx"]) for r in runs}) > 1
+    for r in runs:
+        assert r["info"][1] == qb.STATUS_OK
+        S = sel_matrix(r["idx"], n)
+        assert (S == sel_matrix(runs[0]["idx"], n)).all()
+        K = qb.packed_keys(sfx, r["bfx"])
+        kth = -np.sort(-K, axis=1)[:, k - 1]
+        assert (S == (K >= kth[:, None])).all() and (S.sum(0) == C).all()
+
+
+def test_sap_sparse_falls_back_to_full_relaxation():
+    """A start bias that makes the only augmenting path longer than the
+    sparse bound (about 100 score units against 2^44 grid units = 16): the
+    sparse step must hand over to the full relaxation and move exactly as it
+    does."""
+    T, n, k = 40, 3, 1
+    s = rand_scores(T, n, 5, skew=0.2)
+    sfx = qb.to_fixed(s)
+    C = qb.targets(T, n, k)
+    b = np.array([0, -100 << 40, -100 << 40], np.int64)   # expert 0 takes every token
+    st = qb.select(sfx, b, k)
+    assert st[2][:, 0].all()
+    full = qb.sap_step(sfx, b, k, C, st, sparse=False)
+    fast = qb.sap_step(sfx, b, k, C, st, sparse=True)
+    assert full is not None and (fast == full).all()
+    # the move is a real one: expert 0 drops one token, one underloaded expert gains it
+    L = qb.select(sfx, full, k)[2].sum(0)
+    assert L[0] == T - 1 and sorted(L[1:]) == [0, 1]
+    # and the whole loop, from that start, still reaches the LP optimum
+    r = qb.route_qb(s, k, bias=qb.fixed_to_bias(b), max_rounds=0)
+    assert r["info"][1] == qb.STATUS_OK
+    assert (sel_matrix(r["idx"], n) == lp_selection(s, k)).all()
+
+
 def test_k1_hungarian():
     T, n = 60, 12
     s = rand_scores(T, n, 3, skew=1.0)
