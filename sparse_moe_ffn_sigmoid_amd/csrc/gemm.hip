@@ -140,6 +140,17 @@ __device__ __forceinline__ u32x4_t decode8(uint32_t q, int32_t sbyte) {
   return out;
 }
 
+// A bf16 output value and, where a second output is given, the bf16 of
+// what the first one rounded away: hi + lo holds v to about 16 bits.
+__device__ __forceinline__ void store_bf16(void* C, void* C2, int64_t off, float v) {
+  const bf16_t hi = f32_to_bf16(v);
+  static_cast<bf16_t*>(C)[off] = hi;
+  if (C2) static_cast<bf16_t*>(C2)[off] = f32_to_bf16(v - bf16_to_f32(hi));
+}
+__device__ __forceinline__ void store_bf16(const Params& p, int64_t off, float v) {
+  store_bf16(p.C, p.C2, off, v);
+}
+
 template <int BM, int BN, int WM, int EPI, int BFMT>
 __global__ __launch_bounds__(NTHREADS) void gemm_bf16(Params p) {
   constexpr int WN = 4 / WM;
@@ -691,8 +702,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
           const int grp = wn * FN + j;  // even: gate group, odd: its up group
           const int col = tile.n0 + (grp >> 1) * 32 + (lane & 31);
           if (col < p.N)
-            static_cast<bf16_t*>(p.C)[orow * p.ldc + col] =
-                f32_to_bf16(situ_glu(acc[i][j][r], acc[i][j + 1][r]));
+            store_bf16(p, orow * p.ldc + col, situ_glu(acc[i][j][r], acc[i][j + 1][r]));
         }
       } else {
 #pragma unroll
@@ -706,7 +716,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
           } else if (EPI == EPI_F32) {
             static_cast<float*>(p.C)[orow * p.ldc + col] = acc[i][j][r];
           } else {
-            static_cast<bf16_t*>(p.C)[orow * p.ldc + col] = f32_to_bf16(acc[i][j][r]);
+            store_bf16(p, orow * p.ldc + col, acc[i][j][r]);
           }
         }
       }
@@ -1025,8 +1035,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
           const int grp = wn * FN + j;
           const int col = tile.n0 + (grp >> 1) * 32 + (lane & 31);
           if (col < p.N)
-            static_cast<bf16_t*>(p.C)[orow * p.ldc + col] =
-                f32_to_bf16(situ_glu(acc[i][j][r], acc[i][j + 1][r]));
+            store_bf16(p, orow * p.ldc + col, situ_glu(acc[i][j][r], acc[i][j + 1][r]));
         }
       } else {
 #pragma unroll
@@ -1130,7 +1139,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f32(Params p) {
 // ---------------------------------------------------------------------------
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ part, int kn, int M,
-                                                      int N, int64_t nv, int bn, void* C,
+                                                      int N, int64_t nv, int bn, void* C, void* C2,
                                                       int64_t ldc, const float* col_add) {
   const int64_t total = static_cast<int64_t>(M) * N;
   const int64_t plane = static_cast<int64_t>(M) * nv;
@@ -1147,7 +1156,7 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
         g += pr[q * plane + vg];
         u += pr[q * plane + vg + 32];
       }
-      static_cast<bf16_t*>(C)[row * ldc + c] = f32_to_bf16(situ_glu(g, u));
+      store_bf16(C, C2, row * ldc + c, situ_glu(g, u));
     } else {
       float x = 0.f;
       for (int q = 0; q < kn; ++q) x += pr[q * plane + c];
@@ -1157,7 +1166,7 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
       } else if (EPI == EPI_F32) {
         static_cast<float*>(C)[row * ldc + c] = x;
       } else {
-        static_cast<bf16_t*>(C)[row * ldc + c] = f32_to_bf16(x);
+        store_bf16(C, C2, row * ldc + c, x);
       }
     }
   }
@@ -1226,7 +1235,7 @@ static int run_reduce(const Params& p, const DensePlan& d, hipStream_t stream) {
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)),
                      dim3(256), 0, stream, p.partial, d.ks, p.M, p.N,
-                     static_cast<int64_t>(d.ntn) * d.bn, d.bn, p.C, p.ldc, p.col_add);
+                     static_cast<int64_t>(d.ntn) * d.bn, d.bn, p.C, p.C2, p.ldc, p.col_add);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -1278,18 +1287,6 @@ static int run_pipe(const Params& p, hipStream_t stream, size_t pad_lds = 0) {
   hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT, NW>), dim3(static_cast<unsigned>(G8)),
                      dim3(64 * NW), pad_lds, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
-}
-
-// 128 x 128 tiles (48 KB of LDS, about 130 registers per lane) padded to 88 KB
-// of LDS: one block per CU, the rest of the CU left to kernels on other streams.
-static int run_shared_tiles(const Params& p, int epi, hipStream_t s) {
-  constexpr size_t PAD = 40 * 1024;
-  switch (epi) {
-    case EPI_BF16: return run_pipe<128, 128, 2, EPI_BF16, 32, 3, false>(p, s, PAD);
-    case EPI_F32: return run_pipe<128, 128, 2, EPI_F32, 32, 3, false>(p, s, PAD);
-    case EPI_SITU: return run_pipe<128, 128, 2, EPI_SITU, 32, 3, false>(p, s, PAD);
-    default: return MOE_EUNSUPPORTED;
-  }
 }
 
 // Ring depth: 3 stages (a fourth measured no faster on the weight-streaming
@@ -1399,6 +1396,9 @@ static int dispatch_epi(const Params& p, int epi, hipStream_t s) {
 }
 
 int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipStream_t stream) {
+  // low parts are written by the dense bf16 kernels and their split-K reduction
+  if (p.C2 && !(act_bf16 && bfmt == B_DENSE && !p.tiles && (epi == EPI_BF16 || epi == EPI_SITU)))
+    return MOE_EUNSUPPORTED;
   if (!act_bf16) {
     if (bfmt != B_DENSE) return MOE_EUNSUPPORTED;
     switch (epi) {
@@ -1427,11 +1427,6 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
     if (bm_hint == 320) return dispatch_pipe<320, 256, 2, 64, true, 8>(q, epi, stream);
     if (bm_hint == 256) return dispatch_pipe<256, 256, 2, 64, false, 8>(q, epi, stream);
     return dispatch_pipe<128, 128, 2, 32>(q, epi, stream);
-  }
-  if (bfmt == B_DENSE && bm_hint == BM_SHARE && p.M >= 256) {
-    Params q = p;
-    q.ksplit = 1;
-    return run_shared_tiles(q, epi, stream);
   }
   if (bfmt == B_DENSE) {
     int K = 0;

@@ -33,7 +33,7 @@ struct Params {
   int M;             // rows (dense problems)
   int N;             // output columns
   int nseg;
-  Seg seg[3];
+  Seg seg[4];
   // Grouped problems: per-expert base offsets of B and its scales, the tile
   // list and the gather map from output slot to A row.
   int64_t b_expert_stride;   // elements / code bytes between experts
@@ -43,6 +43,8 @@ struct Params {
   int max_mtiles;            // grid bound on M tiles
   const int32_t* a_rows;     // slot -> A row (null: identity)
   void* C;
+  void* C2;                  // bf16 outputs of dense problems: the rounding residue
+                             // bf16(v - bf16(v)) of each value, or null
   int64_t ldc;
   const float* col_add;      // EPI_SIGMOID: per-column logit offset or null
   // Split-K for dense problems with few output tiles: fp32 partial sums
@@ -61,11 +63,6 @@ size_t fp4_tall_tile_fits(int K);
 
 // Whether the 320-row MXFP4 kernel (scales through the ring) takes this K.
 bool fp4_tile320_fits(int K);
-
-// bm_hint of a dense product that runs on another stream beside the
-// latency-bound routing kernels: 128 x 128 tiles held to one block per CU, so
-// that those kernels' blocks find registers and LDS on every CU.
-constexpr int BM_SHARE = -1;
 
 // Launch helpers (defined in gemm.hip).  `act_bf16` selects the bf16 MFMA
 // kernels, otherwise the fp32 kernels run.

@@ -200,13 +200,16 @@ __global__ __launch_bounds__(256) void mx8_quantize(const bf16_t* __restrict__ i
 }
 
 // y_t = sum_j w[t][j] * yp[inv[t][j]] in fp32 (j ascending), then
-// RMSNorm: y * rsqrt(mean(y^2) + eps) * gamma.  One block per token.
+// RMSNorm: y * rsqrt(mean(y^2) + eps) * gamma.  One block per token.  With
+// bf16 output, out_lo (when given) receives bf16(v - bf16(v)), so that the
+// up-projection can take the normalised row to about 16 bits.
 template <typename ACT>
 __global__ __launch_bounds__(256) void combine_rmsnorm(const float* __restrict__ yp,
                                                        const int32_t* __restrict__ inv,
                                                        const float* __restrict__ w,
                                                        const float* __restrict__ gamma, int k,
-                                                       int L, float eps, ACT* __restrict__ out) {
+                                                       int L, float eps, ACT* __restrict__ out,
+                                                       bf16_t* __restrict__ out_lo) {
   constexpr int MAXV = 16;  // L <= 256 * MAXV
   __shared__ float s_red[256];
   const int t = blockIdx.x;
@@ -248,7 +251,12 @@ __global__ __launch_bounds__(256) void combine_rmsnorm(const float* __restrict__
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int c = threadIdx.x + 256 * i;
-    if (c < L) out[static_cast<int64_t>(t) * L + c] = from_f32<ACT>(acc[i] * scale * gamma[c]);
+    if (c < L) {
+      const float v = acc[i] * scale * gamma[c];
+      const ACT o = from_f32<ACT>(v);
+      out[static_cast<int64_t>(t) * L + c] = o;
+      if (out_lo) out_lo[static_cast<int64_t>(t) * L + c] = f32_to_bf16(v - static_cast<float>(to_f32(o)));
+    }
   }
 }
 
@@ -262,6 +270,7 @@ struct ForwardWorkspace {
   bf16_t* wsplit;     // [3][n][d] (bf16 activations)
   void* z;            // [T][latent]
   void* hs;           // [T][shared]
+  bf16_t* hs_lo;      // [T][shared] bf16 residue of hs (bf16 activations)
   int32_t* offs;      // [n+1]
   int32_t* tiles;     // [max_mtiles][4]
   int32_t* ntiles;
@@ -271,6 +280,7 @@ struct ForwardWorkspace {
   void* h;            // [T*k][inter]
   void* yp;           // [T*k][latent]
   void* yhat;         // [T][latent]
+  bf16_t* yhat_lo;    // [T][latent] bf16 residue of yhat (bf16 activations)
   uint8_t* zq;        // W4A8: z as E4M3 codes [T][latent] and E8M0 scales [T][latent/32]
   uint8_t* zq_scale;
   uint8_t* hq;        // W4A8: h as E4M3 codes [T*k][inter] and scales [T*k][inter/32]
@@ -322,6 +332,7 @@ static size_t forward_layout(const moe_shape_t& s, ForwardWorkspace* fw, void* b
   f.wsplit = cv.take<bf16_t>(s.act_dtype == MOE_BF16 ? 3 * n * s.d : 0);
   f.z = cv.take<char>(T * s.latent * es);
   f.hs = cv.take<char>(T * s.shared_inter * es);
+  f.hs_lo = cv.take<bf16_t>(es == 2 ? T * s.shared_inter : 0);
   f.bm = grouped_bm(s);
   f.max_mtiles = static_cast<int>((T * k + f.bm - 1) / f.bm + n);
   f.offs = cv.take<int32_t>(n + 1);
@@ -333,6 +344,7 @@ static size_t forward_layout(const moe_shape_t& s, ForwardWorkspace* fw, void* b
   f.h = cv.take<char>(T * k * s.inter * es);
   f.yp = cv.take<float>(T * k * s.latent);  // fp32: the combine sums unrounded products
   f.yhat = cv.take<char>(T * s.latent * es);
+  f.yhat_lo = cv.take<bf16_t>(es == 2 ? T * s.latent : 0);
   const bool a8 = s.routed_dtype == MOE_MXFP4_A8;
   f.zq = cv.take<uint8_t>(a8 ? T * s.latent : 0);
   f.zq_scale = cv.take<uint8_t>(a8 ? T * s.latent / 32 : 0);
@@ -535,6 +547,7 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     q.seg[0] = seg(x, d, wt.ws_gate, d, d);
     q.seg[0].B2 = wt.ws_up;
     q.C = f.hs;
+    q.C2 = bf ? f.hs_lo : nullptr;
     q.ldc = ms;
     q.partial = f.partial;
     q.partial_bytes = f.partial_bytes;
@@ -626,21 +639,31 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
   if (bf)
     hipLaunchKernelGGL(combine_rmsnorm<bf16_t>, dim3(T), dim3(256), 0, st,
                        static_cast<const float*>(f.yp), f.inv, w, wt.rms_gamma, k, L, s.rms_eps,
-                       static_cast<bf16_t*>(f.yhat));
+                       static_cast<bf16_t*>(f.yhat), f.yhat_lo);
   else
     hipLaunchKernelGGL(combine_rmsnorm<float>, dim3(T), dim3(256), 0, st,
                        static_cast<const float*>(f.yp), f.inv, w, wt.rms_gamma, k, L, s.rms_eps,
-                       static_cast<float*>(f.yhat));
+                       static_cast<float*>(f.yhat), nullptr);
   MOE_LAUNCH_CHECK();
   }
-  // 8. out = yhat W_up^T + hs Ws_down^T (one GEMM, K concatenated)
+  // 8. out = yhat W_up^T + hs Ws_down^T (one GEMM, K concatenated); with bf16
+  // activations each of yhat and hs enters as its bf16 value plus the bf16
+  // residue, two K segments against the same weights
   {
     gemm::Params p{};
     p.M = T;
     p.N = d;
-    p.nseg = 2;
-    p.seg[0] = seg(f.yhat, L, wt.w_up, L, L);
-    p.seg[1] = seg(f.hs, ms, wt.ws_down, ms, ms);
+    if (bf) {
+      p.nseg = 4;
+      p.seg[0] = seg(f.yhat, L, wt.w_up, L, L);
+      p.seg[1] = seg(f.yhat_lo, L, wt.w_up, L, L);
+      p.seg[2] = seg(f.hs, ms, wt.ws_down, ms, ms);
+      p.seg[3] = seg(f.hs_lo, ms, wt.ws_down, ms, ms);
+    } else {
+      p.nseg = 2;
+      p.seg[0] = seg(f.yhat, L, wt.w_up, L, L);
+      p.seg[1] = seg(f.hs, ms, wt.ws_down, ms, ms);
+    }
     p.C = out;
     p.ldc = d;
     p.partial = f.partial;
