@@ -85,16 +85,21 @@ def check_routing(shape, got, qb_mode):
     return w_ref
 
 
-@pytest.mark.parametrize("wl,qb_mode", [
-    ("k3_decode", qb.MODE_BATCH),
-    ("k3_prefill", qb.MODE_BATCH),
-    ("k3_mxfp4", qb.MODE_BATCH),
-    ("k3_mxfp4", qb.MODE_FROZEN),
-    ("k3_prefill_16k", qb.MODE_BATCH),
-    ("k3_mxfp4_a8", qb.MODE_BATCH),
+# last: how many experts (evenly spread, the first and last included) get
+# the token in their last row slot sampled (the ragged end of their row
+# group); None: every expert.  cover: tokens added until every expert is
+# in the sample.  The decode batch is sampled whole (every expert it
+# touches, every last row).
+@pytest.mark.parametrize("wl,qb_mode,last,cover", [
+    ("k3_decode", qb.MODE_BATCH, None, True),
+    ("k3_prefill", qb.MODE_BATCH, 16, True),
+    ("k3_mxfp4", qb.MODE_BATCH, 6, False),
+    ("k3_mxfp4", qb.MODE_FROZEN, 6, False),
+    ("k3_prefill_16k", qb.MODE_BATCH, 16, True),
+    ("k3_mxfp4_a8", qb.MODE_BATCH, 6, False),
 ])
-def test_full_size_layer_sampled(wl, qb_mode):
-    check_sampled(workloads.SHAPES[wl], qb_mode, wl)
+def test_full_size_layer_sampled(wl, qb_mode, last, cover):
+    check_sampled(workloads.SHAPES[wl], qb_mode, wl, last=last, cover=cover)
 
 
 def test_forward_deterministic_k3_prefill():
@@ -114,14 +119,55 @@ def test_forward_deterministic_k3_prefill():
 @pytest.mark.parametrize("T,n", [(600, 64), (1200, 64), (2048, 64)])
 def test_tall_expert_tiles_k3_width(T, n):
     shape = dataclasses.replace(workloads.SHAPES["k3_prefill"], T=T, n=n)
-    check_sampled(shape, qb.MODE_BATCH, f"T={T} n={n}")
+    check_sampled(shape, qb.MODE_BATCH, f"T={T} n={n}", last=None)
 
 
-def check_sampled(shape, qb_mode, name):
+def last_slot_tokens(idx, n):
+    """For every expert, the last token routed to it (the token in the last
+    row of the expert's row group, rows being filled in token order); -1
+    for experts with no token."""
+    T, k = idx.shape
+    last = np.full(n, -1, np.int64)
+    np.maximum.at(last, idx.ravel().astype(np.int64), np.repeat(np.arange(T), k))
+    return last
+
+
+def expert_cover(idx, tokens):
+    """Greedy set cover: tokens added until every expert that received a
+    token appears in some sampled token's selection."""
+    T, k = idx.shape
+    need = set(np.unique(idx).tolist()) - set(np.unique(idx[tokens]).tolist())
+    chosen = list(tokens)
+    while need:
+        gain = np.array([len(need.intersection(row)) for row in idx.tolist()])
+        t = int(np.argmax(gain))
+        chosen.append(t)
+        need -= set(idx[t].tolist())
+    return chosen
+
+
+def sampled_tokens(T, idx, n, last, cover=False):
+    """First, thirds and last token; the tokens in the last row slot of
+    `last` experts (evenly spread, first and last expert included; None:
+    every expert); with `cover`, a greedy cover of every touched expert."""
+    tokens = [0, T // 3, (2 * T) // 3, T - 1]
+    lt = last_slot_tokens(idx, n)
+    experts = np.arange(n) if last is None else np.unique(np.linspace(0, n - 1, last).astype(int))
+    tokens += [int(t) for t in lt[experts] if t >= 0]
+    if cover:
+        tokens = expert_cover(idx, tokens)
+    return np.unique(np.array(tokens))
+
+
+def check_sampled(shape, qb_mode, name, last=4, cover=False):
     announce(f"layer {name} qb_mode={qb_mode}")
     inp, got = forward_as_benchmarked(shape, qb_mode)
     T = shape.T
-    tokens = np.unique(np.array([0, T // 3, (2 * T) // 3, T - 1]))
+    tokens = sampled_tokens(T, got["idx"], shape.n, last, cover)
+    touched = np.unique(got["idx"][tokens])
+    print(f"  {tokens.size} tokens sampled, {touched.size} experts", flush=True)
+    if cover or last is None:
+        assert touched.size == int((got["loads"] > 0).sum())
     # router on the sampled tokens
     x_s = olayer.as_f64(inp["x"][torch.from_numpy(tokens).cuda()])
     s_ref = olayer.router_scores(x_s, olayer.as_f64(inp["w_router"]),
