@@ -158,6 +158,23 @@ int moe_route_qb(const float* scores, int32_t T, int32_t n, int32_t k, int32_t m
                  void* stream);
 
 /*
+ * moe_route_qb_noalloc -- moe_route_qb for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the same arguments and results without
+ * workspace/workspace_bytes.  The scratch is a device array of
+ * MOE_ROUTE_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the call allocates nothing.  Batches whose
+ * moe_route_workspace_bytes(T, n, k) exceeds that size are rejected with
+ * MOE_EWORKSPACE (at n = 896, k = 16: up to about 6600 tokens).  All calls on
+ * one GPU share its array: calls that overlap on one GPU (concurrent
+ * streams, threads) race and give undefined results.
+ */
+#define MOE_ROUTE_SCRATCH_BYTES (32u << 20)
+int moe_route_qb_noalloc(const float* scores, int32_t T, int32_t n, int32_t k, int32_t mode,
+                         int32_t max_rounds, double* bias, int32_t* topk_idx, float* topk_w,
+                         int32_t* loads, int32_t* qb_info, void* stream);
+
+/*
  * moe_route_sign -- the fixed-step sign update of the routing bias
  * (DeepSeek-V3's rule), run on one batch as the baseline Quantile Balancing
  * is compared with: sign descent on the same dual objective with a

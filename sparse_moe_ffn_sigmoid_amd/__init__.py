@@ -26,7 +26,7 @@ MOE_QB_FROZEN, MOE_QB_BATCH = 0, 1
 EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_route_sign",
             "moe_forward_workspace_bytes",
             "moe_latent_forward", "moe_status_str", "moe_stage_timing", "moe_stage_times",
-            "moe_stage_name", "moe_mxfp8_quantize")
+            "moe_stage_name", "moe_mxfp8_quantize", "moe_route_qb_noalloc")
 
 
 class MoeShape(ctypes.Structure):
@@ -66,6 +66,9 @@ _lib.moe_stage_times.argtypes = [_vp, _vp, _i32]
 _lib.moe_stage_times.restype = ctypes.c_int
 _lib.moe_stage_name.argtypes = [ctypes.c_int]
 _lib.moe_stage_name.restype = ctypes.c_char_p
+_lib.moe_route_qb_noalloc.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                      _vp]
+_lib.moe_route_qb_noalloc.restype = ctypes.c_int
 _lib.moe_mxfp8_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
 _lib.moe_mxfp8_quantize.restype = ctypes.c_int
 
@@ -129,6 +132,27 @@ def route_qb(scores: torch.Tensor, k: int, bias: torch.Tensor | None = None,
                            _ptr(loads), _ptr(info), _ptr(ws), ws.numel(), _stream())
     if st != 0:
         raise MoeError(st, "moe_route_qb")
+    return dict(idx=idx, w=w, loads=loads, bias=b, info=info)
+
+
+def route_qb_noalloc(scores: torch.Tensor, k: int, bias: torch.Tensor | None = None,
+                     mode: int = MOE_QB_BATCH, max_rounds: int = 64):
+    """:func:`route_qb` through moe_route_qb_noalloc: the library's own
+    per-device scratch array instead of a workspace (outputs are still
+    allocated here, by torch)."""
+    dev = scores.device
+    T, n = scores.shape
+    _check(scores, "scores", torch.float32, (T, n), dev)
+    b = torch.zeros(n, dtype=torch.float64, device=dev) if bias is None else bias.clone()
+    _check(b, "bias", torch.float64, (n,), dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    loads = torch.empty(n, dtype=torch.int32, device=dev)
+    info = torch.zeros(4, dtype=torch.int32, device=dev)
+    st = _lib.moe_route_qb_noalloc(_ptr(scores), T, n, k, mode, max_rounds, _ptr(b), _ptr(idx),
+                                   _ptr(w), _ptr(loads), _ptr(info), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_route_qb_noalloc")
     return dict(idx=idx, w=w, loads=loads, bias=b, info=info)
 
 

@@ -1933,3 +1933,50 @@ extern "C" int moe_route_sign(const float* scores, int32_t T, int32_t n, int32_t
                            static_cast<int64_t>(sf), bias, bias, topk_idx, topk_w, loads, qb_info,
                            ws, static_cast<hipStream_t>(stream), 1);
 }
+
+// ---------------------------------------------------------------------------
+// Routing without a caller workspace: the scratch lives in a file-scope
+// device array of MOE_ROUTE_SCRATCH_BYTES, one per GPU, whose device address
+// is looked up once per device.  Every call on a GPU reuses that GPU's array
+// (the routing kernels clear what must start at zero), so calls that overlap
+// on one GPU race.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[MOE_ROUTE_SCRATCH_BYTES];
+
+// Device address of this device's scratch array (null when the lookup fails).
+void* route_scratch() {
+  static void* addr[64] = {};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" int moe_route_qb_noalloc(const float* scores, int32_t T, int32_t n, int32_t k,
+                                    int32_t mode, int32_t max_rounds, double* bias,
+                                    int32_t* topk_idx, float* topk_w, int32_t* loads,
+                                    int32_t* qb_info, void* stream) {
+  int st = moe::route_validate(T, n, k);
+  if (st != MOE_OK) return st;
+  if (mode != MOE_QB_BATCH && mode != MOE_QB_FROZEN) return MOE_EINVAL;
+  if ((T > 0 && (!scores || !topk_idx || !topk_w)) || !bias) return MOE_EINVAL;
+  if (moe::route_workspace_layout(T, n, nullptr, nullptr) > MOE_ROUTE_SCRATCH_BYTES)
+    return MOE_EWORKSPACE;
+  void* base = route_scratch();
+  if (!base) return MOE_EHIP;
+  moe::RouteWorkspace ws;
+  moe::route_workspace_layout(T, n, &ws, base);
+  moe::prof::Scope sc(moe::prof::ST_ROUTING, static_cast<hipStream_t>(stream));
+  return moe::route_run(scores, T, n, k, mode, max_rounds, bias, topk_idx, topk_w, loads, qb_info,
+                        ws, static_cast<hipStream_t>(stream), 1);
+}

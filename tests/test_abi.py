@@ -61,6 +61,18 @@ def test_route_validation_on_host():
     assert lib.moe_route_qb(*args(100, 64, 4, wsb=need - 1)) == -3
 
 
+def test_route_noalloc_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    args = lambda T, n, k, mode=1: (fake, T, n, k, mode, 64, fake, fake, fake, fake, fake, None)
+    assert lib.moe_route_qb_noalloc(*args(100, 64, 65)) == -1          # k > n
+    assert lib.moe_route_qb_noalloc(*args(100, 2048, 4)) == -2         # n > 1024
+    assert lib.moe_route_qb_noalloc(*args(100, 64, 4, mode=7)) == -1
+    assert lib.moe_route_qb_noalloc(*args(8192, 896, 16)) == -3        # beyond the scratch array
+    assert lib.moe_route_workspace_bytes(6000, 896, 16) <= 32 << 20    # the K3 decode / prefill sizes fit
+
+
 def test_mxfp8_quantize_validation_on_host():
     import sparse_moe_ffn_sigmoid_amd as moe
     lib = moe.lib()
