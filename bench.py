@@ -25,15 +25,19 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0   # dense fp8 MFMA (the W4A8 experts' E4M3 x E2M1 products)
-# HBM bytes per launch of the routed gate/up kernel, from rocprofv3 FETCH_SIZE
-# and WRITE_SIZE runs scaled by a 1 GiB device copy (profiles/
-# routed_gemm_hbm_traffic.txt); None where not measured for the current
-# kernel.
-TRAFFIC = {"k3_prefill": 27.019e9,      # gemm_pipe<96, 256, 1, SITU, 64, 3, nt>
-           "k3_decode": 26.312e9,       # gemm_pipe<32, 256, 1, SITU, 64, 3, nt>
-           "k3_mxfp4": 9.928e9,         # gemm_pipe_fp4<320, 256, 2, SITU, 8 waves, scale ring>
-           "k3_mxfp4_a8": 9.290e9,      # gemm_pipe_fp4<320, 256, 2, SITU, 8 waves, MXFP8 A, 2 x 128-element stages>
-           "k3_prefill_16k": 29.243e9}  # gemm_pipe<320, 256, 2, SITU, 64, 2, nt, 8 waves>
+# HBM bytes per launch of the dominant kernel (the routed gate/up launch of a
+# layer, the routing loop of the qb workload), from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs scaled by a 1 GiB device copy (profiles/layer_<workload>.txt,
+# profiles/routing_qb_57344x896.txt); None where not measured for the current
+# kernel.  Keyed by (workload, qb mode).
+TRAFFIC = {("k3_prefill", "batch"): 27.026e9,      # gemm_pipe<96, 256, 1, 3, 64, 3, true, 4>
+           ("k3_decode", "batch"): 26.313e9,       # gemm_pipe<32, 256, 1, 3, 64, 3, true, 4>
+           ("k3_prefill_16k", "batch"): 29.243e9,  # gemm_pipe<320, 256, 2, 3, 64, 2, true, 8>
+           ("k3_mxfp4", "batch"): 9.928e9,         # gemm_pipe_fp4<320, 256, 2, 3, 8, true, false, 3>
+           ("k3_mxfp4", "frozen"): 12.920e9,       # the same kernel, skewed loads (several tiles per expert)
+           ("k3_mxfp4_a8", "batch"): 9.290e9,      # gemm_pipe_fp4<320, 256, 2, 3, 8, true, true, 2>
+           ("tiny", "batch"): 2.363e6,             # gemm_f32<EPI_SITU>
+           ("qb", "batch"): 23.216e9}              # route_loop<14>
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
 
 
@@ -187,6 +191,17 @@ def cpu_model():
     return None
 
 
+def copy_reference(nbytes, dev):
+    """One plain device-to-device copy of nbytes: the reference that scales
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_qb(args):
     """Routing-only workload: Quantile Balancing of T=57344 tokens over n=896
     experts, k=16, scores from N(0,1) logits plus a per-expert N(0, 0.5^2)
@@ -230,7 +245,7 @@ def run_qb(args):
     roof = {"bound": "hbm", "achieved": algo / (avg_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
             "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = TRAFFIC.get(("qb", "batch"))
     rec = {
         "metric": QB_METRIC, "value": T / (ms_per_step / 1e3), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -242,6 +257,8 @@ def run_qb(args):
                          bytes_per_launch=algo, avg_ms=avg_ms, passes=passes),
         "qb_info": info,
     }
+    if args.copy_bytes > 0:
+        copy_reference(args.copy_bytes, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = qb_cpu_baseline(cfg, args.cpu_sample_qb_tokens)
     print(json.dumps(rec), flush=True)
@@ -254,7 +271,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="k3_prefill",
                     choices=["k3_prefill", "k3_decode", "k3_mxfp4", "k3_mxfp4_a8", "k3_prefill_16k",
-                             "qb"])
+                             "tiny", "qb"])
     ap.add_argument("--qb", default="batch", choices=["batch", "frozen"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=2)
     ap.add_argument("--cpu-sample-qb-tokens", type=int, default=8192,
@@ -350,7 +367,7 @@ def main():
         roof = {"bound": "hbm", "achieved": gu_bytes / (gu_avg_ms / 1e3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = TRAFFIC.get(args.workload)
+    roof["traffic"] = TRAFFIC.get((args.workload, args.qb))
     rec = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -368,7 +385,8 @@ def main():
         "config": {"workload": {"k3_prefill": "k3_prefill_bf16", "k3_decode": "k3_decode_bf16",
                                 "k3_mxfp4": "k3_prefill_mxfp4",
                                 "k3_mxfp4_a8": "k3_prefill_mxfp4_w4a8",
-                                "k3_prefill_16k": "k3_prefill_bf16_16k"}[args.workload],
+                                "k3_prefill_16k": "k3_prefill_bf16_16k",
+                                "tiny": "tiny_fp32_latency"}[args.workload],
                    "T": shape.T, "d": shape.d, "latent": shape.latent, "experts": shape.n,
                    "top_k": shape.k, "inter": shape.m, "shared_inter": shape.shared,
                    "routed_weights": shape.routed, "qb": args.qb},
@@ -387,11 +405,7 @@ def main():
     if args.sign_baseline:
         rec["routing_baseline"] = sign_baseline(moe, sh, w, x, bias0, ws, shape)
     if args.copy_bytes > 0:
-        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_reference(args.copy_bytes, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, shape, args.cpu_sample_tokens)
     print(json.dumps(rec), flush=True)

@@ -1372,16 +1372,16 @@ __global__ __launch_bounds__(NT) void route_loop(Args a) {
   // the previous staging.
   auto stage = [&](int buf) __attribute__((always_inline)) -> uint64_t {
     const int64_t* b = bias_buf(a, blockIdx.x % BIAS_COPIES, buf);
-    static_assert(2 * NT >= 1024, "two experts per thread cover n <= 1024");
-    int64_t v[2];
+    constexpr int SH = (1024 + NT - 1) / NT;  // experts per thread: n <= 1024
+    int64_t v[SH];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < SH; ++h) {
       const int e = tid + h * NT;
       v[h] = e < n ? ldc(&b[e]) : 0;
     }
     uint64_t dmax = 0, bmax = 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < SH; ++h) {
       const int e = tid + h * NT;
       if (e >= n && e < 64 * NJ) {
         F.kb[e] = 0;
