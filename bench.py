@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0   # dense fp8 MFMA (the W4A8 experts' E4M3 x E2M1 products)
+PEAK_FP4_TFLOPS = 10100.0  # dense fp4 MFMA (the W4A4 experts' E2M1 x E2M1 products)
 # HBM bytes per launch of the dominant kernel (the routed gate/up launch of a
 # layer, the routing loop of the qb workload), from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs scaled by a 1 GiB device copy (profiles/layer_<workload>.txt,
@@ -51,7 +52,7 @@ def layer_flops_per_token(s):
 
 def weight_bytes(s, touched):
     eb = 2 if s.act == "bf16" else 4
-    if s.routed in ("mxfp4", "mxfp4_a8"):
+    if s.routed in ("mxfp4", "mxfp4_a8", "mxfp4_a4"):
         per_expert = 3 * s.m * s.latent // 2 + 3 * s.m * s.latent // 32
     else:
         per_expert = 3 * s.m * s.latent * eb
@@ -64,12 +65,14 @@ def gate_up_bytes(s, touched, T):
     weights of every expert that received a token, the gathered latent rows
     it reads and the SiTU-GLU output it writes."""
     eb = 2 if s.act == "bf16" else 4
-    if s.routed in ("mxfp4", "mxfp4_a8"):
+    if s.routed in ("mxfp4", "mxfp4_a8", "mxfp4_a4"):
         w = touched * 2 * (s.m * s.latent // 2 + s.m * s.latent // 32)
     else:
         w = touched * 2 * s.m * s.latent * eb
     if s.routed == "mxfp4_a8":  # E4M3 codes and E8M0 scales of the gathered rows
         return w + T * s.k * (s.latent + s.latent // 32) + T * s.k * s.m * eb
+    if s.routed == "mxfp4_a4":  # E2M1 codes (two per byte) and E8M0 scales of the gathered rows
+        return w + T * s.k * (s.latent // 2 + s.latent // 32) + T * s.k * s.m * eb
     return w + T * s.k * s.latent * eb + T * s.k * s.m * eb
 
 
@@ -106,7 +109,8 @@ def cpu_baseline(inp, shape, sample_tokens):
                ws_down=inp["ws_down"].cpu())
     t1 = time.perf_counter()
     olayer.layer_forward(lay, r["idx"], r["w"], shape.eps, tokens=tokens,
-                         act_mxfp8=shape.routed == "mxfp4_a8")
+                         act_mxfp8=shape.routed == "mxfp4_a8",
+                         act_mxfp4=shape.routed == "mxfp4_a4")
     t_layer = time.perf_counter() - t1
     per_token = t_route / shape.T + t_layer / sample_tokens
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -270,7 +274,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="k3_prefill",
-                    choices=["k3_prefill", "k3_decode", "k3_mxfp4", "k3_mxfp4_a8", "k3_prefill_16k",
+                    choices=["k3_prefill", "k3_decode", "k3_mxfp4", "k3_mxfp4_a8", "k3_mxfp4_a4",
+                             "k3_prefill_16k",
                              "tiny", "qb"])
     ap.add_argument("--qb", default="batch", choices=["batch", "frozen"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=2)
@@ -316,7 +321,7 @@ def main():
         w["router_logit_offset"] = w.pop("logit_offset")
     act = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16}[shape.act]
     routed = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "mxfp4": moe.MOE_MXFP4,
-              "mxfp4_a8": moe.MOE_MXFP4_A8}[shape.routed]
+              "mxfp4_a8": moe.MOE_MXFP4_A8, "mxfp4_a4": moe.MOE_MXFP4_A4}[shape.routed]
     qb_mode = moe.MOE_QB_BATCH if args.qb == "batch" else moe.MOE_QB_FROZEN
     sh = moe.make_shape(shape.T, shape.d, shape.latent, shape.n, shape.k, shape.m, shape.shared,
                         act, routed, shape.eps, qb_mode, 64)
@@ -358,6 +363,10 @@ def main():
         # E4M3 x E2M1 on the scaled MFMA: priced at the fp8 MFMA peak
         roof = {"bound": "mfma", "achieved": gu_flops / (gu_avg_ms / 1e3) / 1e12,
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}
+    elif shape.routed == "mxfp4_a4":
+        # E2M1 x E2M1 on the scaled MFMA: priced at the fp4 MFMA peak
+        roof = {"bound": "mfma", "achieved": gu_flops / (gu_avg_ms / 1e3) / 1e12,
+                "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s"}
     elif shape.routed == "mxfp4" or shape.T * shape.k >= 32 * shape.n * 8:
         # codes decoded to bf16, or hundreds of rows per expert: compute-bound,
         # bf16 dense MFMA peak
@@ -380,11 +389,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("bf16; routed experts mxfp8 x mxfp4" if shape.routed == "mxfp4_a8"
+                  else "bf16; routed experts mxfp4 x mxfp4" if shape.routed == "mxfp4_a4"
                   else "bf16" if shape.act == "bf16" else "f32"),
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights, skewed router offsets)",
         "config": {"workload": {"k3_prefill": "k3_prefill_bf16", "k3_decode": "k3_decode_bf16",
                                 "k3_mxfp4": "k3_prefill_mxfp4",
                                 "k3_mxfp4_a8": "k3_prefill_mxfp4_w4a8",
+                                "k3_mxfp4_a4": "k3_prefill_mxfp4_w4a4",
                                 "k3_prefill_16k": "k3_prefill_bf16_16k",
                                 "tiny": "tiny_fp32_latency"}[args.workload],
                    "T": shape.T, "d": shape.d, "latent": shape.latent, "experts": shape.n,

@@ -73,10 +73,13 @@ typedef enum {
   MOE_F32 = 0,
   MOE_BF16 = 1,
   MOE_MXFP4 = 2,    /* routed weights: E2M1 codes + E8M0 scales per 32 (bf16 activations) */
-  MOE_MXFP4_A8 = 3  /* routed weights as MOE_MXFP4; the routed experts' inputs z and h are
+  MOE_MXFP4_A8 = 3, /* routed weights as MOE_MXFP4; the routed experts' inputs z and h are
                        quantised on the fly from bf16 to MXFP8 (E4M3 + E8M0 per 32) and
                        multiplied with gfx950's scaled MFMA (W4A8).  latent and inter must be
                        multiples of 128 (else MOE_EUNSUPPORTED) */
+  MOE_MXFP4_A4 = 4  /* as MOE_MXFP4_A8 with z and h quantised to MXFP4 (E2M1 + E8M0 per 32,
+                       shared exponent floor(log2 amax) - 2): W4A4 on the scaled MFMA with
+                       E2M1 on both operands; same size limits */
 } moe_dtype;
 
 typedef enum {
@@ -109,7 +112,7 @@ typedef struct {
   int32_t inter;         /* routed intermediate width m, multiple of 64 */
   int32_t shared_inter;  /* merged shared-expert intermediate (2 x 3072), multiple of 64 */
   int32_t act_dtype;     /* MOE_F32 or MOE_BF16: x, out and the dense weights */
-  int32_t routed_dtype;  /* act_dtype, or MOE_MXFP4 / MOE_MXFP4_A8 with MOE_BF16 activations */
+  int32_t routed_dtype;  /* act_dtype, or MOE_MXFP4 / _A8 / _A4 with MOE_BF16 activations */
   float rms_eps;         /* RMSNorm epsilon (1e-6) */
   int32_t qb_mode;       /* moe_qb_mode */
   int32_t qb_max_rounds; /* cap on quantile coordinate rounds (<= 0: 64) */
@@ -234,6 +237,24 @@ int moe_latent_forward(const moe_shape_t* shape, const moe_weights_t* weights, c
  * `stream`; returns MOE_EINVAL for bad sizes, NULL or misaligned pointers.
  */
 int moe_mxfp8_quantize(const void* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                       void* stream);
+
+/*
+ * moe_mxfp4_quantize -- the on-the-fly MXFP4 rounding of the routed experts'
+ * inputs in MOE_MXFP4_A4 (the same deployment passage and OCP format as the
+ * routed weights).
+ *   x      [rows][K] bf16 (raw 16-bit patterns), 16-byte aligned, read only
+ *   codes  [rows][K/2] u8 E2M1 codes, element 2i in the low nibble of byte i
+ *          (sign bit 3, magnitudes 0,.5,1,1.5,2,3,4,6), 4-byte aligned
+ *   scales [rows][K/32] u8 E8M0 (value 2^(byte-127))
+ *   K      a multiple of 32; rows >= 0 (0: nothing is launched)
+ * Per block of 32 consecutive elements of a row: X = floor(log2 amax) - 2,
+ * scale byte X + 127 clamped to [0, 254] (0 for an all-zero block); each
+ * element v / 2^(byte-127) rounded to the nearest E2M1 value, ties to the
+ * even code, magnitudes beyond 6 saturating to 6.  Enqueued on `stream`;
+ * returns MOE_EINVAL for bad sizes, NULL or misaligned pointers.
+ */
+int moe_mxfp4_quantize(const void* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
                        void* stream);
 
 /* Static description of a moe_status value; never NULL. */

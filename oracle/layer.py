@@ -211,8 +211,9 @@ def mxfp4_act_round(v):
 
 
 def w4a4_activation(v):
-    """What a W4A4 expert would read: the bf16-stored activation quantised
-    to MXFP4 (no HIP path implements this mode yet)."""
+    """What a W4A4 expert reads: the activation in its bf16 storage format,
+    quantised to MXFP4 (the same reading as for W4A8, with the weights'
+    element format)."""
     return mxfp4_act_round(bf16_round(v))
 
 
@@ -266,7 +267,7 @@ def route_layer(inp, k, mode=qb.MODE_BATCH, bias=None):
     return r
 
 
-def layer_forward(inp, idx, w, eps, tokens=None, act_mxfp8=False):
+def layer_forward(inp, idx, w, eps, tokens=None, act_mxfp8=False, act_mxfp4=False):
     """Layer output (float64) for the given routing ``idx``/``w`` [T, k].
 
     ``tokens`` restricts the computation to those token rows (experts are
@@ -275,7 +276,10 @@ def layer_forward(inp, idx, w, eps, tokens=None, act_mxfp8=False):
     experts and the SiTU-GLU outputs h entering their down-projections are
     rounded to bf16 (their storage format) and then to MXFP8 (per row,
     blocks of 32 along the row).
+    ``act_mxfp4``: W4A4 experts -- the same two places rounded to bf16 and
+    then to MXFP4 (E2M1 elements, E8M0 scale per 32).
     """
+    act = w4a8_activation if act_mxfp8 else w4a4_activation if act_mxfp4 else None
     x = as_f64(inp["x"])
     T = x.shape[0]
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
@@ -289,10 +293,10 @@ def layer_forward(inp, idx, w, eps, tokens=None, act_mxfp8=False):
         wg = expert_matrix(inp["w_gate"], int(e))
         wu = expert_matrix(inp["w_uproj"], int(e))
         wd = expert_matrix(inp["w_dn"], int(e))
-        ze = w4a8_activation(z[rows]) if act_mxfp8 else z[rows]
+        ze = act(z[rows]) if act else z[rows]
         h = situ_glu(ze @ wg.T, ze @ wu.T)
-        if act_mxfp8:
-            h = w4a8_activation(h)
+        if act:
+            h = act(h)
         y[rows] += w_s[rows, slots][:, None] * (h @ wd.T)
     yn = rmsnorm(y, as_f64(inp["rms_gamma"]), eps)
     out = yn @ as_f64(inp["w_up"]).T

@@ -21,12 +21,13 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python sparse_moe_ffn_sigmoid_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
-MOE_F32, MOE_BF16, MOE_MXFP4, MOE_MXFP4_A8 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_MXFP4, MOE_MXFP4_A8, MOE_MXFP4_A4 = 0, 1, 2, 3, 4
 MOE_QB_FROZEN, MOE_QB_BATCH = 0, 1
 EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_route_sign",
             "moe_forward_workspace_bytes",
             "moe_latent_forward", "moe_status_str", "moe_stage_timing", "moe_stage_times",
-            "moe_stage_name", "moe_mxfp8_quantize", "moe_route_qb_noalloc")
+            "moe_stage_name", "moe_mxfp8_quantize", "moe_mxfp4_quantize",
+            "moe_route_qb_noalloc")
 
 
 class MoeShape(ctypes.Structure):
@@ -69,6 +70,8 @@ _lib.moe_stage_name.restype = ctypes.c_char_p
 _lib.moe_route_qb_noalloc.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                       _vp]
 _lib.moe_route_qb_noalloc.restype = ctypes.c_int
+_lib.moe_mxfp4_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
+_lib.moe_mxfp4_quantize.restype = ctypes.c_int
 _lib.moe_mxfp8_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
 _lib.moe_mxfp8_quantize.restype = ctypes.c_int
 
@@ -193,6 +196,20 @@ def mxfp8_quantize(x: torch.Tensor):
     return codes, scales
 
 
+def mxfp4_quantize(x: torch.Tensor):
+    """bf16 rows [rows, K] (device, K a multiple of 32) -> (E2M1 codes uint8
+    [rows, K/2], two per byte, element 2i in the low nibble; E8M0 scales uint8
+    [rows, K/32])."""
+    rows, K = x.shape
+    _check(x, "x", torch.bfloat16, (rows, K), x.device)
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    st = _lib.moe_mxfp4_quantize(_ptr(x), rows, K, _ptr(codes), _ptr(scales), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_mxfp4_quantize")
+    return codes, scales
+
+
 def make_shape(T, d, latent, n, k, inter, shared_inter, act_dtype, routed_dtype,
                rms_eps=1e-6, qb_mode=MOE_QB_BATCH, qb_max_rounds=64) -> MoeShape:
     return MoeShape(T, d, latent, n, k, inter, shared_inter, act_dtype, routed_dtype, rms_eps,
@@ -224,7 +241,7 @@ def latent_forward(shape: MoeShape, weights: dict, x: torch.Tensor, bias=None,
         _check(weights["router_logit_offset"], "router_logit_offset", torch.float32, (n,), dev)
     _check(weights["w_down"], "w_down", adt, (l, d), dev)
     _check(weights["w_up"], "w_up", adt, (d, l), dev)
-    if shape.routed_dtype in (MOE_MXFP4, MOE_MXFP4_A8):
+    if shape.routed_dtype in (MOE_MXFP4, MOE_MXFP4_A8, MOE_MXFP4_A4):
         for nm, sn, rows, K in (("w_gate", "s_gate", m, l), ("w_uproj", "s_uproj", m, l),
                                 ("w_dn", "s_dn", l, m)):
             _check(weights[nm], nm, torch.uint8, (n, rows, K // 2), dev)

@@ -764,17 +764,23 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 // per B row per stage: the scale bytes of this stage and its neighbour)
 // instead of a per-block panel of the whole K range, which leaves room for
 // 320-row tiles at any K.
-// A8 (with SR): A holds MXFP8 codes, one byte per element, and a stage spans
-// 128 K elements: 128 bytes of A per row (laid out like a bf16 stage of 64),
-// 64 bytes of B codes per row (16-byte chunks XOR-swizzled by (row / 2) mod 4)
-// and one 4-byte word of E8M0 scales per row for each of A and B.  Two scaled
-// MFMAs (v_mfma_scale_f32_32x32x64_f8f6f4) per fragment pair and stage.
-template <int BM, int BN, int WM, int EPI, int NW, bool SR, bool A8 = false, int NSF = 3>
+// AF (with SR): the format of quantised A operands, 8 for MXFP8 (E4M3 codes,
+// one byte per element) or 4 for MXFP4 (E2M1 codes, two per byte, element 2i
+// in the low nibble); 0 for bf16 A.  With quantised A a stage spans 128 K
+// elements: 128 bytes of E4M3 A per row (laid out like a bf16 stage of 64) or
+// 64 bytes of E2M1 A (laid out like the B codes), 64 bytes of B codes per row
+// (16-byte chunks XOR-swizzled by (row / 2) mod 4) and one 4-byte word of E8M0
+// scales per row for each of A and B.  Two scaled MFMAs
+// (v_mfma_scale_f32_32x32x64_f8f6f4) per fragment pair and stage.
+template <int BM, int BN, int WM, int EPI, int NW, bool SR, int AF = 0, int NSF = 3>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_pipe_fp4(Params p) {
-  static_assert(!A8 || SR, "MXFP8 A needs the scale ring");
+  static_assert(AF == 0 || AF == 8 || AF == 4, "A format: bf16, E4M3 or E2M1");
+  constexpr bool A4 = AF == 4, AQ = AF != 0;
+  static_assert(!AQ || SR, "quantised A needs the scale ring");
   static_assert(NSF >= 2 && NSF <= 6, "ring depth");
   constexpr int BKP = 64;              // bf16 elements of A per row and stage (128 bytes)
-  constexpr int KST = A8 ? 128 : 64;   // K elements per stage
+  constexpr int KST = AQ ? 128 : 64;   // K elements per stage
+  constexpr int AROW = A4 ? 64 : 128;  // bytes of A per row and stage
   constexpr int QROW = KST / 2;        // E2M1 code bytes per B row and stage
   constexpr int NTH = 64 * NW;
   constexpr int WN = NW / WM;
@@ -783,8 +789,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold 32x32 blocks");
   static_assert(EPI != EPI_SITU || FN % 2 == 0, "SiTU needs gate/up fragment pairs");
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
-  // A: 8 rows of 128 bytes per instruction; B: 1 KB of codes per instruction
-  constexpr int A_RPI = 8, Q_RPI = 1024 / QROW;
+  // A: 8 rows of 128 bytes (16 of 64) per instruction; B: 1 KB of codes per
+  // instruction
+  constexpr int A_RPI = 1024 / AROW, Q_RPI = 1024 / QROW;
   constexpr int NA = BM / A_RPI, NQ = BN / Q_RPI;
   static_assert(NA * A_RPI == BM && NQ * Q_RPI == BN, "tile rows per instruction");
   constexpr int MA = (NA + NW - 1) / NW, MQ = NQ / NW;
@@ -792,19 +799,19 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   // surplus A instructions repeat the wave's own instruction i-1
   auto a_ins = [](int w, int i) { const int x = w + NW * i; return x < NA ? x : x - NW; };
   // A scales: 64 rows per instruction, waves past them repeat a neighbour's
-  constexpr int NSA = A8 ? (BM + 63) / 64 : 1;
-  static_assert(!A8 || NSA <= NW, "one A scale instruction per wave");
+  constexpr int NSA = AQ ? (BM + 63) / 64 : 1;
+  static_assert(!AQ || NSA <= NW, "one A scale instruction per wave");
   // scale ring: one 4-byte piece per B row and stage, 64 rows per instruction;
   // waves past the BN / 64 that are needed repeat a neighbour's instruction
   constexpr int NS = BN / 64;
-  constexpr int MS = (SR ? 1 : 0) + (A8 ? 1 : 0);
+  constexpr int MS = (SR ? 1 : 0) + (AQ ? 1 : 0);
   static_assert(!SR || (NS <= NW && NS * 64 == BN), "one scale instruction per wave");
 
   // NSF ring stages: A rows (bf16 or E4M3 codes), B codes, B scales, A scales
-  __shared__ __attribute__((aligned(1024))) bf16_t sA[NSF][BM * BKP];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA[NSF][BM * AROW / 2];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ[NSF][BN * QROW];
   __shared__ __attribute__((aligned(16))) uint8_t sS[NSF][SR ? BN * 4 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sT[NSF][A8 ? NSA * 256 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sT[NSF][AQ ? NSA * 256 : 16];
   // scale panel [BN][K/32], sized by the launch (not used with SR)
   extern __shared__ __attribute__((aligned(16))) uint8_t sP[];
 
@@ -851,8 +858,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   int a_chunk[MA];
 #pragma unroll
   for (int i = 0; i < MA; ++i) {
-    int r = a_ins(wave, i) * 8 + (lane >> 3);
-    a_chunk[i] = (lane & 7) ^ (r & 7);
+    int r;
+    if (A4) {  // 64-byte rows: four 16-byte chunks, swizzled by (row / 2) mod 4
+      r = a_ins(wave, i) * 16 + (lane >> 2);
+      a_chunk[i] = (lane & 3) ^ ((r >> 1) & 3);
+    } else {
+      r = a_ins(wave, i) * 8 + (lane >> 3);
+      a_chunk[i] = (lane & 7) ^ (r & 7);
+    }
     r = r < tile.rows ? r : 0;
     const int slot = tile.row0 + r;
     a_off[i] = p.a_rows ? p.a_rows[slot] : slot;
@@ -861,9 +874,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   const bf16_t* pa[MA];
   const uint8_t* ps = nullptr;  // this lane's scale row (SR)
   const int s_ins = wave % NS;  // scale instruction of this wave (SR)
-  const uint8_t* pt = nullptr;  // this lane's A scale row (A8)
+  const uint8_t* pt = nullptr;  // this lane's A scale row (quantised A)
   const int t_ins = wave % NSA;
-  if (A8) {
+  if (AQ) {
     int r = t_ins * 64 + lane;
     r = r < tile.rows ? r : 0;
     const int slot = tile.row0 + r;
@@ -876,13 +889,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
     const uint8_t* Q2 = static_cast<const uint8_t*>(g.B2) + static_cast<int64_t>(tile.expert) * p.b_expert_stride;
 #pragma unroll
     for (int i = 0; i < MA; ++i)
-      pa[i] = A8 ? reinterpret_cast<const bf16_t*>(reinterpret_cast<const uint8_t*>(g.A) +
+      pa[i] = AQ ? reinterpret_cast<const bf16_t*>(reinterpret_cast<const uint8_t*>(g.A) +
                                                    a_off[i] * g.lda + a_chunk[i] * 16)
                  : A + a_off[i] * g.lda + a_chunk[i] * 8;
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
       bool up;
-      if (A8) {  // 64-byte rows: four 16-byte chunks, swizzled by (row / 2) mod 4
+      if (AQ) {  // 64-byte rows: four 16-byte chunks, swizzled by (row / 2) mod 4
         const int r = (wave + NW * i) * 16 + (lane >> 2);
         const int chunk = (lane & 3) ^ ((r >> 1) & 3);
         const int64_t row = b_row_of(r, up);
@@ -905,15 +918,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   int issued = 0;  // stages issued so far
   // the scale word of a stage: bytes 2kt .. 2kt+1 inside the aligned word at
   // (2kt) & ~3 (64-element stages), or exactly bytes 4kt .. 4kt+3 (128)
-  auto scale_word = [&]() { return A8 ? 4 * issued : (2 * issued) & ~3; };
+  auto scale_word = [&]() { return AQ ? 4 * issued : (2 * issued) & ~3; };
   auto issue = [&](bf16_t* As, uint8_t* Qs, uint8_t* Ss, uint8_t* Ts) {
 #pragma unroll
     for (int i = 0; i < MA; ++i) {
-      // one instruction fills 1 KB: 8 bf16 rows or 16 E4M3 rows of the stage
+      // one instruction fills 1 KB: 8 rows of 128 bytes (bf16, E4M3) or 16
+      // rows of 64 (E2M1)
       load_lds16_raw(pa[i], As + a_ins(wave, i) * 512);
-      pa[i] += BKP;  // 128 bytes
+      pa[i] += AROW / 2;
     }
-    if (A8) load_lds4_asm(pt + scale_word(), Ts + t_ins * 256);
+    if (AQ) load_lds4_asm(pt + scale_word(), Ts + t_ins * 256);
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
       load_lds16_raw(pq[i], Qs + (wave + NW * i) * 1024);
@@ -935,9 +949,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
   auto compute = [&](int kt, const bf16_t* As, const uint8_t* Qs, const uint8_t* Ss,
                      const uint8_t* Ts) {
     const int hi = lane >> 5, sw = lane & 7;
-    if constexpr (A8) {
-      // lane (r, h): B codes of K [32h, 32h+32), A codes of K [16h, 16h+16)
-      // and [32+16h, 32+16h+16); scale registers of block h on both sides
+    if constexpr (AQ) {
+      // lane (r, h): B codes of K [32h, 32h+32); E4M3 A codes of K
+      // [16h, 16h+16) and [32+16h, 32+16h+16), or E2M1 A codes of K
+      // [32h, 32h+32) like B; scale registers of block h on both sides
       typedef int v8i_t __attribute__((ext_vector_type(8)));
       typedef int v4i_t __attribute__((ext_vector_type(4)));
       const uint8_t* Ab = reinterpret_cast<const uint8_t*>(As);
@@ -957,20 +972,27 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BM < 160) ? 2 : 1) void gemm_p
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int ra = wm * WTM + i * 32 + (lane & 31);
-          const int s = ra & 7;
-          const u32x4_t lo =
-              *reinterpret_cast<const u32x4_t*>(Ab + ra * 128 + (((4 * q2 + hi) ^ s) * 16));
-          const u32x4_t up =
-              *reinterpret_cast<const u32x4_t*>(Ab + ra * 128 + (((4 * q2 + 2 + hi) ^ s) * 16));
-          const v8i_t aq = {static_cast<int>(lo[0]), static_cast<int>(lo[1]),
-                            static_cast<int>(lo[2]), static_cast<int>(lo[3]),
-                            static_cast<int>(up[0]), static_cast<int>(up[1]),
-                            static_cast<int>(up[2]), static_cast<int>(up[3])};
+          v8i_t aq;
+          if constexpr (A4) {
+            const v4i_t qa = *reinterpret_cast<const v4i_t*>(
+                Ab + ra * 64 + (((2 * q2 + hi) ^ ((ra >> 1) & 3)) * 16));
+            aq = __builtin_shufflevector(qa, qa, 0, 1, 2, 3, -1, -1, -1, -1);
+          } else {
+            const int s = ra & 7;
+            const u32x4_t lo =
+                *reinterpret_cast<const u32x4_t*>(Ab + ra * 128 + (((4 * q2 + hi) ^ s) * 16));
+            const u32x4_t up =
+                *reinterpret_cast<const u32x4_t*>(Ab + ra * 128 + (((4 * q2 + 2 + hi) ^ s) * 16));
+            aq = v8i_t{static_cast<int>(lo[0]), static_cast<int>(lo[1]),
+                       static_cast<int>(lo[2]), static_cast<int>(lo[3]),
+                       static_cast<int>(up[0]), static_cast<int>(up[1]),
+                       static_cast<int>(up[2]), static_cast<int>(up[3])};
+          }
           const int sa = Ts[ra * 4 + 2 * q2 + hi];
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq, bq[j], acc[i][j], 0, 4,
-                                                                       0, sa, 0, sb[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                aq, bq[j], acc[i][j], A4 ? 4 : 0, 4, 0, sa, 0, sb[j]);
         }
       }
       return;
@@ -1337,17 +1359,18 @@ bool fp4_tile320_fits(int K) { return K > 0 && K % 128 == 0; }
 // Returns 1 when the shape does not fit the pipelined MXFP4 kernel (the caller
 // then uses the register-staged kernel).  SR: scales through the ring (K a
 // multiple of 128, so that every stage's scale word lies inside its row).
-template <int BM, int BN, int WM, int EPI, int NW = 4, bool SR = false, bool A8 = false>
+template <int BM, int BN, int WM, int EPI, int NW = 4, bool SR = false, int AF = 0>
 static int run_pipe_fp4(const Params& p, hipStream_t stream) {
-  // W4A8: two 128-element stages (117 KB); bf16-A: three 64-element stages
-  constexpr int NSF = A8 ? 2 : 3;
+  // W4A8: two 128-element stages (117 KB); W4A4: three 128-element stages
+  // (114 KB); bf16-A: three 64-element stages
+  constexpr int NSF = AF == 8 ? 2 : 3;
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   if (p.nseg != 1 || p.seg[0].K % (SR ? 128 : 512) != 0) return 1;
   const Seg& g = p.seg[0];
   const uintptr_t align = reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B) |
                           reinterpret_cast<uintptr_t>(g.B2) | reinterpret_cast<uintptr_t>(g.Bs) |
                           reinterpret_cast<uintptr_t>(g.Bs2) | reinterpret_cast<uintptr_t>(g.As) |
-                          static_cast<uintptr_t>(g.lda * (A8 ? 1 : 2)) |
+                          static_cast<uintptr_t>(g.lda * (AF ? 1 : 2)) |
                           static_cast<uintptr_t>(p.b_expert_stride) |
                           static_cast<uintptr_t>(p.bs_expert_stride);
   if (align % 16 != 0) return 1;
@@ -1360,14 +1383,14 @@ static int run_pipe_fp4(const Params& p, hipStream_t stream) {
   const int64_t G8 = (G + 7) / 8 * 8;
   static bool configured = false;
   if (!SR && !configured) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, A8, NSF>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, AF, NSF>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(fp4_lds_budget<BM>() - fp4_static_lds<BM, BN>())) !=
         hipSuccess)
       return MOE_EHIP;
     configured = true;
   }
-  hipLaunchKernelGGL((gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, A8, NSF>), dim3(static_cast<unsigned>(G8)),
+  hipLaunchKernelGGL((gemm_pipe_fp4<BM, BN, WM, EPI, NW, SR, AF, NSF>), dim3(static_cast<unsigned>(G8)),
                      dim3(64 * NW), panel, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -1455,16 +1478,23 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
       default: return MOE_EUNSUPPORTED;
     }
   }
-  if (bfmt == B_MXFP4_A8) {
-    // W4A8: 320-row tiles on 8 waves, E4M3 A and E2M1 B multiplied by the
-    // scaled MFMA; no other tile height takes these operands
+  if (bfmt == B_MXFP4_A8 || bfmt == B_MXFP4_A4) {
+    // W4A8 / W4A4: 320-row tiles on 8 waves, E4M3 or E2M1 A and E2M1 B
+    // multiplied by the scaled MFMA; no other tile height takes these operands
     if (bm_hint != 320) return MOE_EUNSUPPORTED;
-    int rc8 = 1;
-    if (epi == EPI_SITU)
-      rc8 = run_pipe_fp4<320, 256, 2, EPI_SITU, 8, true, true>(p, stream);
-    else if (epi == EPI_F32)
-      rc8 = run_pipe_fp4<320, 256, 2, EPI_F32, 8, true, true>(p, stream);
-    return rc8 == 1 ? MOE_EUNSUPPORTED : rc8;
+    int rcq = 1;
+    if (bfmt == B_MXFP4_A8) {
+      if (epi == EPI_SITU)
+        rcq = run_pipe_fp4<320, 256, 2, EPI_SITU, 8, true, 8>(p, stream);
+      else if (epi == EPI_F32)
+        rcq = run_pipe_fp4<320, 256, 2, EPI_F32, 8, true, 8>(p, stream);
+    } else {
+      if (epi == EPI_SITU)
+        rcq = run_pipe_fp4<320, 256, 2, EPI_SITU, 8, true, 4>(p, stream);
+      else if (epi == EPI_F32)
+        rcq = run_pipe_fp4<320, 256, 2, EPI_F32, 8, true, 4>(p, stream);
+    }
+    return rcq == 1 ? MOE_EUNSUPPORTED : rcq;
   }
   // MXFP4 routed experts: codes straight to LDS, scales in a per-block panel,
   // decoded per fragment; shapes outside that kernel's limits use the

@@ -13,8 +13,9 @@ enum Epilogue : int {
   EPI_SITU = 3,     // C (act)  = SiTU-GLU(acc_gate, acc_up); B rows come in gate/up pairs
 };
 
-// B_MXFP4_A8: MXFP4 B with MXFP8 (E4M3) A codes and E8M0 A scales (W4A8)
-enum BFormat : int { B_DENSE = 0, B_MXFP4 = 1, B_MXFP4_A8 = 2 };
+// B_MXFP4_A8: MXFP4 B with MXFP8 (E4M3) A codes and E8M0 A scales (W4A8);
+// B_MXFP4_A4: MXFP4 B with MXFP4 (E2M1, two per byte) A codes (W4A4)
+enum BFormat : int { B_DENSE = 0, B_MXFP4 = 1, B_MXFP4_A8 = 2, B_MXFP4_A4 = 3 };
 
 // One K segment: A [rows][K] (K contiguous, leading dim lda), B [N][K] (ldb).
 struct Seg {
@@ -24,7 +25,8 @@ struct Seg {
   const void* B2;  // EPI_SITU: the "up" matrix paired with B (the gate matrix)
   const uint8_t* Bs;   // MXFP4 scales [N][K/32] for B
   const uint8_t* Bs2;  // MXFP4 scales for B2
-  const uint8_t* As;   // B_MXFP4_A8: E8M0 scales of A [rows][K/32] (A holds E4M3 codes, lda in bytes)
+  const uint8_t* As;   // B_MXFP4_A8 / _A4: E8M0 scales of A [rows][K/32] (A holds E4M3 or
+                       // E2M1 codes, lda in bytes)
   int64_t ldb;         // elements (dense) or bytes (MXFP4 codes)
   int K;
 };

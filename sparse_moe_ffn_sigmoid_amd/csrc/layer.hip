@@ -199,6 +199,58 @@ __global__ __launch_bounds__(256) void mx8_quantize(const bf16_t* __restrict__ i
   }
 }
 
+// One element q = v / 2^X -> E2M1 code: the nearest of 0, .5, 1, 1.5, 2, 3,
+// 4, 6, ties to the even code (the one with a zero mantissa bit), magnitudes
+// above 6 saturating to 6; bit 3 carries q's sign.  The comparisons are exact:
+// q is a bf16 value scaled by a power of two.
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  const float a = fabsf(q);
+  uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return c | ((__float_as_uint(q) >> 31) << 3);
+}
+
+// bf16 rows -> MXFP4 (OCP Microscaling: E2M1 elements, two per byte with
+// element 2i in the low nibble, one E8M0 scale per 32 consecutive elements of
+// a row).  Per block: X = floor(log2 amax) - 2 (2 = E2M1's largest exponent),
+// stored as X + 127 clamped to [0, 254] (0 for an all-zero block).  Each lane
+// takes 8 consecutive elements (one 16-byte load, one 4-byte store), four
+// lanes a block.
+__global__ __launch_bounds__(256) void mx4_quantize(const bf16_t* __restrict__ in, int64_t nblk,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales) {
+  const int64_t tot = nblk * 4;  // 8-element pieces
+  const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  // the stride is a multiple of 4, so the four lanes of a block stay together
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < tot; g += step) {
+    const uint4 raw = reinterpret_cast<const uint4*>(in)[g];
+    float v[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 4));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 4));
+    int sb = 0;
+    if (amax > 0.f) {
+      const uint32_t ab = __float_as_uint(amax);
+      const int e = static_cast<int>((ab >> 23) & 255u);
+      const int fl = e ? e - 127 : (31 - __clz(ab & 0x7fffffu)) - 149;  // floor(log2 amax)
+      sb = min(max(fl - 2 + 127, 0), 254);
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= e2m1_code(ldexpf(v[i], 127 - sb)) << (4 * i);
+    reinterpret_cast<uint32_t*>(codes)[g] = word;
+    if ((g & 3) == 0) scales[g >> 2] = static_cast<uint8_t>(sb);
+  }
+}
+
 // y_t = sum_j w[t][j] * yp[inv[t][j]] in fp32 (j ascending), then
 // RMSNorm: y * rsqrt(mean(y^2) + eps) * gamma.  One block per token.  With
 // bf16 output, out_lo (when given) receives bf16(v - bf16(v)), so that the
@@ -281,10 +333,10 @@ struct ForwardWorkspace {
   void* yp;           // [T*k][latent]
   void* yhat;         // [T][latent]
   bf16_t* yhat_lo;    // [T][latent] bf16 residue of yhat (bf16 activations)
-  uint8_t* zq;        // W4A8: z as E4M3 codes [T][latent] and E8M0 scales [T][latent/32]
-  uint8_t* zq_scale;
-  uint8_t* hq;        // W4A8: h as E4M3 codes [T*k][inter] and scales [T*k][inter/32]
-  uint8_t* hq_scale;
+  uint8_t* zq;        // W4A8 / W4A4: z as E4M3 codes [T][latent] (E2M1: [T][latent/2])
+  uint8_t* zq_scale;  //   and E8M0 scales [T][latent/32]
+  uint8_t* hq;        // W4A8 / W4A4: h as E4M3 codes [T*k][inter] (E2M1: [T*k][inter/2])
+  uint8_t* hq_scale;  //   and scales [T*k][inter/32]
   int bm;
   int max_mtiles;
   float* partial;     // split-K partial sums of the dense GEMMs (used one at a time)
@@ -298,7 +350,8 @@ struct ForwardWorkspace {
 static int grouped_bm(const moe_shape_t& s) {
   const int64_t avg = (static_cast<int64_t>(s.T) * s.top_k + s.n_experts - 1) / s.n_experts;
   if (s.act_dtype != MOE_BF16) return 64;
-  if (s.routed_dtype == MOE_MXFP4_A8) return 320;  // the only W4A8 tile
+  if (s.routed_dtype == MOE_MXFP4_A8 || s.routed_dtype == MOE_MXFP4_A4)
+    return 320;  // the only tile of quantised activations
   if (avg <= 32) return 32;
   if (s.routed_dtype == MOE_MXFP4) {
     // MFMA-bound: 320-row tiles on 8 waves for 161 - 320 rows per expert,
@@ -345,11 +398,12 @@ static size_t forward_layout(const moe_shape_t& s, ForwardWorkspace* fw, void* b
   f.yp = cv.take<float>(T * k * s.latent);  // fp32: the combine sums unrounded products
   f.yhat = cv.take<char>(T * s.latent * es);
   f.yhat_lo = cv.take<bf16_t>(es == 2 ? T * s.latent : 0);
-  const bool a8 = s.routed_dtype == MOE_MXFP4_A8;
-  f.zq = cv.take<uint8_t>(a8 ? T * s.latent : 0);
-  f.zq_scale = cv.take<uint8_t>(a8 ? T * s.latent / 32 : 0);
-  f.hq = cv.take<uint8_t>(a8 ? T * k * s.inter : 0);
-  f.hq_scale = cv.take<uint8_t>(a8 ? T * k * s.inter / 32 : 0);
+  const bool a8 = s.routed_dtype == MOE_MXFP4_A8, a4 = s.routed_dtype == MOE_MXFP4_A4;
+  const int64_t qdiv = a4 ? 2 : 1;  // elements per code byte
+  f.zq = cv.take<uint8_t>(a8 || a4 ? T * s.latent / qdiv : 0);
+  f.zq_scale = cv.take<uint8_t>(a8 || a4 ? T * s.latent / 32 : 0);
+  f.hq = cv.take<uint8_t>(a8 || a4 ? T * k * s.inter / qdiv : 0);
+  f.hq_scale = cv.take<uint8_t>(a8 || a4 ? T * k * s.inter / 32 : 0);
   // The dense GEMMs that may split K never overlap in time: the router runs
   // before the shared branch forks, the two shared-branch products run in
   // order on one stream, and the up-projection runs after the join.
@@ -377,10 +431,13 @@ static int validate(const moe_shape_t* sp, const moe_weights_t* w) {
   if (s.d % 64 || s.latent % 64 || s.inter % 64 || s.shared_inter % 64) return MOE_EUNSUPPORTED;
   if (s.latent > 256 * 16) return MOE_EUNSUPPORTED;
   if (s.act_dtype != MOE_F32 && s.act_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-  const bool mx = s.routed_dtype == MOE_MXFP4 || s.routed_dtype == MOE_MXFP4_A8;
+  const bool mx = s.routed_dtype == MOE_MXFP4 || s.routed_dtype == MOE_MXFP4_A8 ||
+                  s.routed_dtype == MOE_MXFP4_A4;
   if (!(s.routed_dtype == s.act_dtype || (mx && s.act_dtype == MOE_BF16))) return MOE_EUNSUPPORTED;
   // W4A8 scale words stay inside their rows when K is a multiple of 128
-  if (s.routed_dtype == MOE_MXFP4_A8 && (s.latent % 128 || s.inter % 128)) return MOE_EUNSUPPORTED;
+  if ((s.routed_dtype == MOE_MXFP4_A8 || s.routed_dtype == MOE_MXFP4_A4) &&
+      (s.latent % 128 || s.inter % 128))
+    return MOE_EUNSUPPORTED;
   if (s.qb_mode != MOE_QB_BATCH && s.qb_mode != MOE_QB_FROZEN) return MOE_EINVAL;
   if (!(s.rms_eps >= 0.f)) return MOE_EINVAL;
   if (w) {
@@ -532,11 +589,16 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     {
       prof::Scope sc(prof::ST_LATENT_DOWN, sst);
       if ((rc = gemm::launch(p, store_epi, gemm::B_DENSE, bf, side_hint, sst)) != MOE_OK) return rc;
-      if (s.routed_dtype == MOE_MXFP4_A8) {  // z -> MXFP8 for the routed experts
+      if (s.routed_dtype == MOE_MXFP4_A8 || s.routed_dtype == MOE_MXFP4_A4) {
+        // z -> MXFP8 / MXFP4 for the routed experts
         const int64_t nblk = static_cast<int64_t>(T) * (L / 32);
-        hipLaunchKernelGGL(mx8_quantize,
-                           dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 63) / 64, 8192))),
-                           dim3(256), 0, sst, static_cast<const bf16_t*>(f.z), nblk, f.zq, f.zq_scale);
+        const dim3 grid(static_cast<unsigned>(std::min<int64_t>((nblk + 63) / 64, 8192)));
+        if (s.routed_dtype == MOE_MXFP4_A8)
+          hipLaunchKernelGGL(mx8_quantize, grid, dim3(256), 0, sst,
+                             static_cast<const bf16_t*>(f.z), nblk, f.zq, f.zq_scale);
+        else
+          hipLaunchKernelGGL(mx4_quantize, grid, dim3(256), 0, sst,
+                             static_cast<const bf16_t*>(f.z), nblk, f.zq, f.zq_scale);
         MOE_LAUNCH_CHECK();
       }
     }
@@ -579,9 +641,11 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     MOE_HIP_CHECK(hipStreamWaitEvent(st, side->join, 0));
     side_join.joined = true;
   }
-  const bool a8 = s.routed_dtype == MOE_MXFP4_A8;
-  const bool mx = s.routed_dtype == MOE_MXFP4 || a8;
-  const int bfmt = a8 ? gemm::B_MXFP4_A8 : mx ? gemm::B_MXFP4 : gemm::B_DENSE;
+  const bool a8 = s.routed_dtype == MOE_MXFP4_A8, a4 = s.routed_dtype == MOE_MXFP4_A4;
+  const bool mx = s.routed_dtype == MOE_MXFP4 || a8 || a4;
+  const int bfmt = a8 ? gemm::B_MXFP4_A8
+                 : a4 ? gemm::B_MXFP4_A4
+                 : mx ? gemm::B_MXFP4 : gemm::B_DENSE;
   // 5. routed gate/up with SiTU-GLU: h[slot] = SiTU(z[perm[slot]] Wg_e^T, z[perm[slot]] Wu_e^T)
   {
     gemm::Params p{};
@@ -589,6 +653,8 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     p.nseg = 1;
     if (a8)  // W4A8: the E4M3 codes of z, one byte per element
       p.seg[0] = seg(f.zq, L, wt.w_gate, L / 2, L);
+    else if (a4)  // W4A4: the E2M1 codes of z, two per byte
+      p.seg[0] = seg(f.zq, L / 2, wt.w_gate, L / 2, L);
     else
       p.seg[0] = seg(f.z, L, wt.w_gate, mx ? L / 2 : L, L);
     p.seg[0].As = f.zq_scale;
@@ -606,10 +672,15 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     prof::Scope sc(prof::ST_ROUTED_GATE_UP, st);
     if ((rc = gemm::launch(p, gemm::EPI_SITU, bfmt, bf, f.bm, st)) != MOE_OK) return rc;
   }
-  if (a8) {  // h -> MXFP8 for the down-projection
+  if (a8 || a4) {  // h -> MXFP8 / MXFP4 for the down-projection
     const int64_t nblk = static_cast<int64_t>(T) * k * (m / 32);
-    hipLaunchKernelGGL(mx8_quantize, dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 63) / 64, 8192))),
-                       dim3(256), 0, st, static_cast<const bf16_t*>(f.h), nblk, f.hq, f.hq_scale);
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>((nblk + 63) / 64, 8192)));
+    if (a8)
+      hipLaunchKernelGGL(mx8_quantize, grid, dim3(256), 0, st, static_cast<const bf16_t*>(f.h), nblk,
+                         f.hq, f.hq_scale);
+    else
+      hipLaunchKernelGGL(mx4_quantize, grid, dim3(256), 0, st, static_cast<const bf16_t*>(f.h), nblk,
+                         f.hq, f.hq_scale);
     MOE_LAUNCH_CHECK();
   }
   // 6. routed down: yp[slot] = h[slot] Wd_e^T
@@ -619,6 +690,8 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     p.nseg = 1;
     if (a8)
       p.seg[0] = seg(f.hq, m, wt.w_dn, m / 2, m);
+    else if (a4)
+      p.seg[0] = seg(f.hq, m / 2, wt.w_dn, m / 2, m);
     else
       p.seg[0] = seg(f.h, m, wt.w_dn, mx ? m / 2 : m, m);
     p.seg[0].As = f.hq_scale;
@@ -711,6 +784,24 @@ extern "C" int moe_mxfp8_quantize(const void* x, int64_t rows, int64_t K, uint8_
   if (rows == 0) return MOE_OK;
   const int64_t nblk = rows * (K / 32);
   hipLaunchKernelGGL(moe::layer::mx8_quantize,
+                     dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 63) / 64, 8192))), dim3(256),
+                     0, static_cast<hipStream_t>(stream), static_cast<const moe::bf16_t*>(x), nblk,
+                     codes, scales);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" int moe_mxfp4_quantize(const void* x, int64_t rows, int64_t K, uint8_t* codes,
+                                  uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_EINVAL;
+  if (rows > 0 && (!x || !codes || !scales)) return MOE_EINVAL;
+  if (rows > 0 && (reinterpret_cast<uintptr_t>(x) % 16 != 0 ||
+                   reinterpret_cast<uintptr_t>(codes) % 4 != 0))
+    return MOE_EINVAL;
+  if (rows > (int64_t(1) << 56) / K) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  const int64_t nblk = rows * (K / 32);
+  hipLaunchKernelGGL(moe::layer::mx4_quantize,
                      dim3(static_cast<unsigned>(std::min<int64_t>((nblk + 63) / 64, 8192))), dim3(256),
                      0, static_cast<hipStream_t>(stream), static_cast<const moe::bf16_t*>(x), nblk,
                      codes, scales);

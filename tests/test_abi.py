@@ -73,6 +73,18 @@ def test_route_noalloc_validation_on_host():
     assert lib.moe_route_workspace_bytes(6000, 896, 16) <= 32 << 20    # the K3 decode / prefill sizes fit
 
 
+def test_mxfp4_quantize_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    assert lib.moe_mxfp4_quantize(fake, 4, 48, fake, fake, None) == -1       # K % 32
+    assert lib.moe_mxfp4_quantize(fake, -1, 64, fake, fake, None) == -1
+    assert lib.moe_mxfp4_quantize(None, 4, 64, fake, fake, None) == -1
+    assert lib.moe_mxfp4_quantize(ctypes.c_void_p((1 << 20) + 8), 4, 64, fake, fake, None) == -1
+    assert lib.moe_mxfp4_quantize(fake, 4, 64, ctypes.c_void_p((1 << 20) + 2), fake, None) == -1
+    assert lib.moe_mxfp4_quantize(None, 0, 64, None, None, None) == 0
+
+
 def test_mxfp8_quantize_validation_on_host():
     import sparse_moe_ffn_sigmoid_amd as moe
     lib = moe.lib()
@@ -147,6 +159,9 @@ def test_forward_workspace_sizing_on_host():
     assert ws(routed=moe.MOE_MXFP4_A8) > ws(routed=moe.MOE_MXFP4)   # room for the MXFP8 rows
     assert ws(routed=moe.MOE_MXFP4_A8, latent=3584 + 64) == 0       # W4A8 widths: multiples of 128
     assert ws(routed=moe.MOE_MXFP4_A8, m=2048 + 64) == 0
+    assert ws(routed=moe.MOE_MXFP4_A8) > ws(routed=moe.MOE_MXFP4_A4) > ws(routed=moe.MOE_MXFP4)
+    assert ws(routed=moe.MOE_MXFP4_A4, latent=3584 + 64) == 0       # W4A4: the same limits
+    assert ws(routed=moe.MOE_MXFP4_A4, act=moe.MOE_F32) == 0
     assert ws(act=moe.MOE_F32, routed=moe.MOE_BF16) == 0
     assert ws(mode=5) == 0
 

@@ -11,13 +11,13 @@ import numpy as np
 import pytest
 
 import workloads
-from layer_cases import announce, oracle_scores, rel_err, run_gpu
+from layer_cases import announce, oracle_scores, rel_err, run_gpu, w4a4_check
 from oracle import layer as olayer
 from oracle import qb
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 1e-1, "mxfp4_a8": 1e-1}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 1e-1, "mxfp4_a8": 1e-1, "mxfp4_a4": 1e-1}
 
 
 def check_layer(shape, seed=0, qb_mode=qb.MODE_BATCH, bias=None, name="", edit=None):
@@ -35,10 +35,15 @@ def check_layer(shape, seed=0, qb_mode=qb.MODE_BATCH, bias=None, name="", edit=N
     if qb_mode == qb.MODE_BATCH:
         assert (got["bias"] == ref["bias"]).all()
     out_ref = olayer.layer_forward(inp, ref["idx"], ref["w"], shape.eps,
-                                   act_mxfp8=shape.routed == "mxfp4_a8")
+                                   act_mxfp8=shape.routed == "mxfp4_a8",
+                                   act_mxfp4=shape.routed == "mxfp4_a4")
     err = rel_err(got["out"], out_ref)
     print(f"  max|diff|/rms = {err:.3e}", flush=True)
-    assert err <= TOL[shape.routed if shape.routed.startswith("mxfp4") else shape.act], err
+    tol = TOL[shape.routed if shape.routed.startswith("mxfp4") else shape.act]
+    if shape.routed == "mxfp4_a4":
+        w4a4_check(inp, ref["idx"], ref["w"], shape.eps, got["out"], out_ref, tol)
+    else:
+        assert err <= tol, err
     # the HIP router on its own
     announce(f"router {name}")
     own = run_gpu(moe, shape, inp, bias=bias, qb_mode=qb_mode)
@@ -159,6 +164,33 @@ def test_w4a8_layer_extreme_scale_bytes():
 ])
 def test_w4a8_layer(kw):
     check_layer(workloads.small_shape(routed="mxfp4_a8", **kw), seed=11, name=f"w4a8 {kw}")
+
+
+# W4A4: MXFP4 weights times MXFP4 activations on the scaled MFMA (320-row
+# tiles only, E2M1 on both operands), against the oracle that rounds z and h
+# to bf16 and then MXFP4
+@pytest.mark.parametrize("kw", [
+    dict(T=300, n=16, k=4, d=1024, latent=512, m=512, shared=256),   # 75 rows per expert
+    dict(T=1200, n=16, k=4, d=1024, latent=512, m=512, shared=256),  # 300 rows per expert
+    dict(T=1000, n=16, k=4, d=1024, latent=640, m=384, shared=256),  # 20 / 12 scale bytes per row
+    dict(T=200, n=40, k=6, d=512, latent=256, m=256, shared=320),    # ragged loads, column tails
+    dict(T=16, n=64, k=4, d=256, latent=128, m=128, shared=128),     # decode-like: 1 row per expert
+])
+def test_w4a4_layer(kw):
+    check_layer(workloads.small_shape(routed="mxfp4_a4", **kw), seed=13, name=f"w4a4 {kw}")
+
+
+def test_w4a4_layer_frozen_uneven_tiles():
+    shape = workloads.small_shape(routed="mxfp4_a4", T=1000, n=16, k=4, d=1024, latent=512, m=512,
+                                  shared=256, offset_std=1.0)
+    check_layer(shape, seed=14, qb_mode=qb.MODE_FROZEN, bias=np.zeros(shape.n),
+                name="w4a4 frozen, uneven 320-row tiles")
+
+
+def test_w4a4_layer_extreme_scale_bytes():
+    shape = workloads.small_shape(routed="mxfp4_a4", T=300, n=16, k=4, d=1024, latent=512,
+                                  m=512, shared=256)
+    check_layer(shape, seed=4, name="w4a4 extreme scales", edit=extreme_scale_bytes)
 
 
 def test_w4a8_layer_empty_batch():

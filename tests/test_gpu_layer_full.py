@@ -19,13 +19,13 @@ import pytest
 import torch
 
 import workloads
-from layer_cases import announce, rel_err
+from layer_cases import announce, rel_err, w4a4_check
 from oracle import layer as olayer
 from oracle import qb
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "mxfp4": 1e-1, "mxfp4_a8": 1e-1}
+TOL = {"bf16": 2e-2, "mxfp4": 1e-1, "mxfp4_a8": 1e-1, "mxfp4_a4": 1e-1}
 SCALES = {"w_gate": "s_gate", "w_uproj": "s_uproj", "w_dn": "s_dn"}
 
 
@@ -42,7 +42,8 @@ def forward_as_benchmarked(shape, qb_mode, calls=1):
         else:
             w[key] = v
     w["router_logit_offset"] = w.pop("logit_offset")
-    routed = {"bf16": moe.MOE_BF16, "mxfp4": moe.MOE_MXFP4, "mxfp4_a8": moe.MOE_MXFP4_A8}[shape.routed]
+    routed = {"bf16": moe.MOE_BF16, "mxfp4": moe.MOE_MXFP4, "mxfp4_a8": moe.MOE_MXFP4_A8,
+              "mxfp4_a4": moe.MOE_MXFP4_A4}[shape.routed]
     sh = moe.make_shape(shape.T, shape.d, shape.latent, shape.n, shape.k, shape.m, shape.shared,
                         moe.MOE_BF16, routed, shape.eps, qb_mode, 64)
     ws = torch.empty(moe.forward_workspace_bytes(sh), dtype=torch.uint8, device=dev)
@@ -97,6 +98,7 @@ def check_routing(shape, got, qb_mode):
     ("k3_mxfp4", qb.MODE_FROZEN, 6, False),
     ("k3_prefill_16k", qb.MODE_BATCH, 16, True),
     ("k3_mxfp4_a8", qb.MODE_BATCH, 6, False),
+    ("k3_mxfp4_a4", qb.MODE_BATCH, 6, False),
 ])
 def test_full_size_layer_sampled(wl, qb_mode, last, cover):
     check_sampled(workloads.SHAPES[wl], qb_mode, wl, last=last, cover=cover)
@@ -178,9 +180,14 @@ def check_sampled(shape, qb_mode, name, last=4, cover=False):
     sub = dict(inp)
     sub["x"] = inp["x"][torch.from_numpy(tokens).cuda()]
     out_ref = olayer.layer_forward(sub, got["idx"][tokens], w_ref[tokens], shape.eps,
-                                   act_mxfp8=shape.routed == "mxfp4_a8")
+                                   act_mxfp8=shape.routed == "mxfp4_a8",
+                                   act_mxfp4=shape.routed == "mxfp4_a4")
     err = rel_err(got["out"][tokens], out_ref)
     print(f"  info={got['info'].tolist()} sampled max|diff|/rms = {err:.3e}", flush=True)
-    assert err <= TOL[shape.routed]
+    if shape.routed == "mxfp4_a4":
+        w4a4_check(sub, got["idx"][tokens], w_ref[tokens], shape.eps, got["out"][tokens], out_ref,
+                   TOL[shape.routed])
+    else:
+        assert err <= TOL[shape.routed]
     del inp, sub
     torch.cuda.empty_cache()

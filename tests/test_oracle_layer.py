@@ -140,14 +140,16 @@ def test_layer_token_sampling_matches_full():
     assert np.allclose(full[[3, 17, 40]], some, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("w4a8,mx", [(False, False), (True, False), (False, True), (True, True)])
-def test_layer_composition_with_permutation_weights(w4a8, mx):
+@pytest.mark.parametrize("act_fmt,mx", [(None, False), ("mxfp8", False), (None, True),
+                                        ("mxfp8", True), ("mxfp4", True)])
+def test_layer_composition_with_permutation_weights(act_fmt, mx):
     """The whole layer on scaled permutation weights against its output
-    written out by hand (``tests/perm_layer.py``).  With ``w4a8`` the expert
-    inputs z and the SiTU-GLU outputs h (rows of 64, two MXFP8 blocks) are
-    rounded to bf16 and then MXFP8 at exactly those two places, with the
-    separately pinned codec.  With ``mx`` the routed experts are given as
-    MXFP4 codes and E8M0 scales whose values E2M1 x 2^E holds exactly."""
+    written out by hand (``tests/perm_layer.py``).  With ``act_fmt`` the
+    expert inputs z and the SiTU-GLU outputs h (rows of 64, two blocks) are
+    rounded to bf16 and then MXFP8 (W4A8) or MXFP4 (W4A4) at exactly those
+    two places, with the separately pinned codecs.  With ``mx`` the routed
+    experts are given as MXFP4 codes and E8M0 scales whose values E2M1 x 2^E
+    holds exactly."""
     inp, par = perm_layer.build(exact_mxfp4=mx)
     if mx:
         for key in ("w_gate", "w_uproj", "w_dn"):
@@ -159,8 +161,10 @@ def test_layer_composition_with_permutation_weights(w4a8, mx):
     sc = 1.0 / (1.0 + np.exp(-perm_layer.LOGIT_OFFSET))
     top = sc[perm_layer.TOP]
     assert np.allclose(r["w"], (top / top.sum())[None, :], rtol=1e-6, atol=0)
-    out = layer.layer_forward(inp, r["idx"], r["w"], perm_layer.EPS, act_mxfp8=w4a8)
-    act = (lambda v: layer.w4a8_activation(v[None, :])[0]) if w4a8 else (lambda v: v)
+    out = layer.layer_forward(inp, r["idx"], r["w"], perm_layer.EPS,
+                              act_mxfp8=act_fmt == "mxfp8", act_mxfp4=act_fmt == "mxfp4")
+    fn = {"mxfp8": layer.w4a8_activation, "mxfp4": layer.w4a4_activation}.get(act_fmt)
+    act = (lambda v: fn(v[None, :])[0]) if fn else (lambda v: v)
     want = perm_layer.expected(inp, par, r["idx"], r["w"], act)
     assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
 
@@ -316,6 +320,28 @@ def test_w4a8_layer_moves_by_the_activation_rounding():
     z = layer.as_f64(inp["x"]) @ layer.as_f64(inp["w_down"]).T
     q = layer.w4a8_activation(z)
     assert np.array_equal(layer.w4a8_activation(q), q)
+
+
+def test_w4a4_layer_moves_by_the_activation_rounding():
+    shape = workloads.small_shape(routed="mxfp4", T=48, k=4, n=16, d=256, latent=128, m=128,
+                                  shared=128)
+    inp = workloads.layer_inputs(shape, "cpu", seed=4)
+    s = layer.router_scores(layer.as_f64(inp["x"]), layer.as_f64(inp["w_router"]),
+                            layer.as_f64(inp["logit_offset"]))
+    r = qb.route_qb(s, shape.k)
+    a16 = layer.layer_forward(inp, r["idx"], r["w"], shape.eps)
+    a8 = layer.layer_forward(inp, r["idx"], r["w"], shape.eps, act_mxfp8=True)
+    a4 = layer.layer_forward(inp, r["idx"], r["w"], shape.eps, act_mxfp4=True)
+    # E2M1 keeps one mantissa bit: relative rounding error up to 1/6 near the
+    # top of a binade, rms around 8% of each element of z and h, and values
+    # below 1/8 of the block maximum mostly rounded to 0 or 0.5.  The routed half
+    # of the output moves by several times the W4A8 change, but well under 100%
+    e4 = np.sqrt(np.mean((a4 - a16) ** 2) / np.mean(a16 ** 2))
+    e8 = np.sqrt(np.mean((a8 - a16) ** 2) / np.mean(a16 ** 2))
+    assert 2 * e8 < e4 < 0.5
+    z = layer.as_f64(inp["x"]) @ layer.as_f64(inp["w_down"]).T
+    q = layer.w4a4_activation(z)
+    assert np.array_equal(layer.w4a4_activation(q), q)
 
 
 def test_bf16_round_ties_to_even():

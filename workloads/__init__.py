@@ -44,7 +44,8 @@ class LayerShape:
     m: int
     shared: int            # merged shared-expert intermediate width
     act: str               # "f32" | "bf16"
-    routed: str            # "f32" | "bf16" | "mxfp4" | "mxfp4_a8" (same weights as mxfp4)
+    routed: str            # "f32" | "bf16" | "mxfp4" | "mxfp4_a8" | "mxfp4_a4" (same weights
+                           # as mxfp4)
     router_std: float      # std of the router weights
     offset_std: float      # std of the per-expert logit offset (0: none)
     eps: float = 1e-6
@@ -60,6 +61,9 @@ SHAPES = {
                            7168 ** -0.5, 1.0),
     # the MXFP4 batch with the routed experts' activations in MXFP8 (W4A8)
     "k3_mxfp4_a8": LayerShape(16384, 7168, 3584, 896, 16, 2048, 6144, "bf16", "mxfp4_a8",
+                              7168 ** -0.5, 1.0),
+    # ... and in MXFP4 (W4A4)
+    "k3_mxfp4_a4": LayerShape(16384, 7168, 3584, 896, 16, 2048, 6144, "bf16", "mxfp4_a4",
                               7168 ** -0.5, 1.0),
     # the bf16 prefill layer at 16384 tokens: compute-bound (MFMA) instead of
     # bound by streaming the routed weights
@@ -171,7 +175,7 @@ def layer_inputs(shape: LayerShape, device="cpu", seed=0, random_gamma=False, T=
     T = shape.T if T is None else T
     adt = torch.float32 if shape.act == "f32" else torch.bfloat16
     rdt = torch.float32 if shape.routed == "f32" else torch.bfloat16
-    mx = shape.routed in ("mxfp4", "mxfp4_a8")
+    mx = shape.routed in ("mxfp4", "mxfp4_a8", "mxfp4_a4")
     d, l, n, m, ms = shape.d, shape.latent, shape.n, shape.m, shape.shared
     inp = dict(
         x=normal((T, d), 1.0, device, seed, "x", dtype=adt),
