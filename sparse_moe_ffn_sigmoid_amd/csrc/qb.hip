@@ -1067,6 +1067,7 @@ __device__ __attribute__((always_inline)) inline void sap_move(const Args& a, Fi
     // sources' edge counts -> offsets (exclusive scan over the experts)
     {
       int c0 = 0, c1 = 0;
+      static_assert(2 * NT >= 1024, "two experts per thread cover n <= 1024");
       const int e0 = 2 * tid, e1 = 2 * tid + 1;  // two experts per thread: n <= 1024
       if (e0 < n) c0 = ldc(&a.cnt[N_DEG0 + e0]);
       if (e1 < n) c1 = ldc(&a.cnt[N_DEG0 + e1]);
