@@ -121,6 +121,42 @@ def cpu_baseline(inp, shape, sample_tokens):
                        f"({t_layer:.1f} s); tokens/s = 1 / (route_s/T + layer_s/sample)")}
 
 
+def time_backward(moe, sh, w, x, bias0, ws, shape, args):
+    """moe_latent_backward on this batch's routing (from one forward call) and
+    a seeded N(0,1) output gradient: ms per call, timed like the forward."""
+    import torch
+    fwd = moe.latent_forward(sh, w, x, bias=bias0, workspace=ws, want_scores=True)
+    g = torch.Generator(device=x.device)
+    g.manual_seed(1234)
+    dout = torch.randn(x.shape, generator=g, device=x.device, dtype=torch.float32).to(x.dtype)
+    bws = torch.empty(moe.lib().moe_backward_workspace_bytes(ctypes_ref(sh)), dtype=torch.uint8,
+                      device=x.device)
+
+    def step():
+        return moe.latent_backward(sh, w, x, fwd["scores"], fwd["idx"], fwd["w"], dout,
+                                   workspace=bws)
+
+    r = step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        r = step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    del r, bws
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "tokens_per_s": shape.T / (ms / 1e3),
+            "what": "gradients of x and every weight for one forward call (forward activations "
+                    "recomputed inside), selection held fixed"}
+
+
+def ctypes_ref(obj):
+    import ctypes
+    return ctypes.byref(obj)
+
+
 def sign_baseline(moe, sh, w, x, bias0, ws, shape):
     """QB and the fixed-step sign update on the router scores of this batch:
     updates made, status, max |load - target| and the routing time."""
@@ -285,6 +321,9 @@ def main():
     ap.add_argument("--sign-baseline", action="store_true",
                     help="also route this batch's scores with the fixed-step sign update "
                          "(DeepSeek-V3's bias rule) and report rounds / imbalance / time beside QB")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time moe_latent_backward (bf16 layers) on this batch's routing and "
+                         "a random output gradient; reported under 'backward'")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many bytes "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -415,6 +454,8 @@ def main():
     }
     if args.sign_baseline:
         rec["routing_baseline"] = sign_baseline(moe, sh, w, x, bias0, ws, shape)
+    if args.backward:
+        rec["backward"] = time_backward(moe, sh, w, x, bias0, ws, shape, args)
     if args.copy_bytes > 0:
         copy_reference(args.copy_bytes, dev)
     if not args.no_cpu_baseline:

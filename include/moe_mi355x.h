@@ -257,6 +257,55 @@ int moe_mxfp8_quantize(const void* x, int64_t rows, int64_t K, uint8_t* codes, u
 int moe_mxfp4_quantize(const void* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
                        void* stream);
 
+/* Gradients written by moe_latent_backward (DEVICE pointers, caller-owned).
+ * Weight gradients are fp32 in the layout of the weights; dx has the
+ * activation dtype.  d_router_logit_offset must be NULL exactly when the
+ * weights have no router_logit_offset. */
+typedef struct {
+  void* dx;                     /* [T][d] */
+  float* d_w_router;            /* [n][d] */
+  float* d_router_logit_offset; /* [n] or NULL */
+  float* d_w_down;              /* [latent][d] */
+  float* d_w_up;                /* [d][latent] */
+  float* d_w_gate;              /* [n][inter][latent] */
+  float* d_w_uproj;             /* [n][inter][latent] */
+  float* d_w_dn;                /* [n][latent][inter] */
+  float* d_rms_gamma;           /* [latent] */
+  float* d_ws_gate;             /* [shared_inter][d] */
+  float* d_ws_up;               /* [shared_inter][d] */
+  float* d_ws_down;             /* [d][shared_inter] */
+} moe_grads_t;
+
+/* Bytes of device workspace moe_latent_backward needs; 0 on a shape it does
+ * not take (bf16 activations and bf16 routed weights only). */
+size_t moe_backward_workspace_bytes(const moe_shape_t* shape);
+
+/*
+ * moe_latent_backward -- gradients of sum(out * dout) for one forward call,
+ * the expert selection held fixed: the QB bias acts on selection only, so
+ * gradients reach the router through the renormalised raw scores of the
+ * chosen experts, and every step after routing is differentiated as written
+ * (xhh.club page above, Q&A on routing, SiTU-GLU, RMSNorm and the shared
+ * expert).
+ *   shape, weights : as for the forward call (act_dtype and routed_dtype
+ *                    MOE_BF16, else MOE_EUNSUPPORTED; qb_mode is ignored)
+ *   x        [T][d] bf16, the forward's input
+ *   scores   [T][n] f32, the forward's router scores (its scores_out)
+ *   topk_idx [T][k] i32 and topk_w [T][k] f32, the forward's routing
+ *   dout     [T][d] bf16, the gradient of the output
+ *   grads    host pointer to the gradient buffers (overwritten, not
+ *            accumulated)
+ *   workspace: >= moe_backward_workspace_bytes(shape) bytes, 256-byte aligned
+ * The forward activations are recomputed from x and the routing.  Products
+ * run on the bf16 MFMA with fp32 accumulation; intermediate gradients that
+ * feed a product are rounded to bf16.  Results are deterministic (fixed
+ * reduction orders, no floating-point atomics).  Enqueued on `stream`.
+ */
+int moe_latent_backward(const moe_shape_t* shape, const moe_weights_t* weights, const void* x,
+                        const float* scores, const int32_t* topk_idx, const float* topk_w,
+                        const void* dout, const moe_grads_t* grads, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* Static description of a moe_status value; never NULL. */
 const char* moe_status_str(int status);
 

@@ -27,7 +27,7 @@ EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_route_sign",
             "moe_forward_workspace_bytes",
             "moe_latent_forward", "moe_status_str", "moe_stage_timing", "moe_stage_times",
             "moe_stage_name", "moe_mxfp8_quantize", "moe_mxfp4_quantize",
-            "moe_route_qb_noalloc")
+            "moe_route_qb_noalloc", "moe_backward_workspace_bytes", "moe_latent_backward")
 
 
 class MoeShape(ctypes.Structure):
@@ -46,6 +46,12 @@ class MoeWeights(ctypes.Structure):
 
 
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in (
+        "dx", "d_w_router", "d_router_logit_offset", "d_w_down", "d_w_up", "d_w_gate",
+        "d_w_uproj", "d_w_dn", "d_rms_gamma", "d_ws_gate", "d_ws_up", "d_ws_down")]
+
+
 _lib.moe_route_workspace_bytes.argtypes = [_i32, _i32, _i32]
 _lib.moe_route_workspace_bytes.restype = _sz
 _lib.moe_route_qb.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -70,6 +76,11 @@ _lib.moe_stage_name.restype = ctypes.c_char_p
 _lib.moe_route_qb_noalloc.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                       _vp]
 _lib.moe_route_qb_noalloc.restype = ctypes.c_int
+_lib.moe_backward_workspace_bytes.argtypes = [ctypes.POINTER(MoeShape)]
+_lib.moe_backward_workspace_bytes.restype = _sz
+_lib.moe_latent_backward.argtypes = [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _vp, _vp,
+                                     _vp, _vp, _vp, ctypes.POINTER(MoeGrads), _vp, _sz, _vp]
+_lib.moe_latent_backward.restype = ctypes.c_int
 _lib.moe_mxfp4_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
 _lib.moe_mxfp4_quantize.restype = ctypes.c_int
 _lib.moe_mxfp8_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
@@ -208,6 +219,56 @@ def mxfp4_quantize(x: torch.Tensor):
     if st != 0:
         raise MoeError(st, "moe_mxfp4_quantize")
     return codes, scales
+
+
+GRAD_SHAPES = {  # gradient name -> (weight key, shape from (T, d, L, n, k, m, ms))
+    "d_w_router": ("w_router", lambda T, d, L, n, k, m, ms: (n, d)),
+    "d_router_logit_offset": ("router_logit_offset", lambda T, d, L, n, k, m, ms: (n,)),
+    "d_w_down": ("w_down", lambda T, d, L, n, k, m, ms: (L, d)),
+    "d_w_up": ("w_up", lambda T, d, L, n, k, m, ms: (d, L)),
+    "d_w_gate": ("w_gate", lambda T, d, L, n, k, m, ms: (n, m, L)),
+    "d_w_uproj": ("w_uproj", lambda T, d, L, n, k, m, ms: (n, m, L)),
+    "d_w_dn": ("w_dn", lambda T, d, L, n, k, m, ms: (n, L, m)),
+    "d_rms_gamma": ("rms_gamma", lambda T, d, L, n, k, m, ms: (L,)),
+    "d_ws_gate": ("ws_gate", lambda T, d, L, n, k, m, ms: (ms, d)),
+    "d_ws_up": ("ws_up", lambda T, d, L, n, k, m, ms: (ms, d)),
+    "d_ws_down": ("ws_down", lambda T, d, L, n, k, m, ms: (d, ms)),
+}
+
+
+def latent_backward(shape: MoeShape, weights: dict, x: torch.Tensor, scores: torch.Tensor,
+                    idx: torch.Tensor, w: torch.Tensor, dout: torch.Tensor, workspace=None):
+    """Gradients of sum(out * dout) for a forward call with routing (scores
+    [T,n] f32, idx [T,k] i32, w [T,k] f32), the selection held fixed.  Returns
+    dict(dx, d_w_router, ...): fp32 weight gradients, dx in the activation
+    dtype (bf16 layers only)."""
+    dev = x.device
+    T, d, l, n, k = shape.T, shape.d, shape.latent, shape.n_experts, shape.top_k
+    m, ms = shape.inter, shape.shared_inter
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(dout, "dout", torch.bfloat16, (T, d), dev)
+    _check(scores, "scores", torch.float32, (T, n), dev)
+    _check(idx, "idx", torch.int32, (T, k), dev)
+    _check(w, "w", torch.float32, (T, k), dev)
+    wts = MoeWeights(*[None if weights.get(f) is None else weights[f].data_ptr()
+                       for f, _ in MoeWeights._fields_])
+    out = {"dx": torch.empty((T, d), dtype=torch.bfloat16, device=dev)}
+    for name, (key, fn) in GRAD_SHAPES.items():
+        if weights.get(key) is None:
+            out[name] = None
+        else:
+            out[name] = torch.empty(fn(T, d, l, n, k, m, ms), dtype=torch.float32, device=dev)
+    grads = MoeGrads(*[None if out[f] is None else out[f].data_ptr() for f, _ in MoeGrads._fields_])
+    need = _lib.moe_backward_workspace_bytes(ctypes.byref(shape))
+    if need == 0:
+        raise MoeError(-2, "moe_backward_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _lib.moe_latent_backward(ctypes.byref(shape), ctypes.byref(wts), _ptr(x), _ptr(scores),
+                                  _ptr(idx), _ptr(w), _ptr(dout), ctypes.byref(grads), _ptr(ws),
+                                  ws.numel(), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_latent_backward")
+    return out
 
 
 def make_shape(T, d, latent, n, k, inter, shared_inter, act_dtype, routed_dtype,

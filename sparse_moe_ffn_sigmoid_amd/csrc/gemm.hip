@@ -43,6 +43,20 @@ struct Tile {
 template <int BM>
 __device__ __forceinline__ bool locate_tile(const Params& p, int ntn, int bn_out, Tile& t) {
   const int b = blockIdx.x;
+  if (p.kgroups > 0) {  // one M x N problem per group, tiles column by column
+    const int G = gridDim.x;
+    const int tau = (b & 7) * (G >> 3) + (b >> 3);
+    const int ntm = (p.M + BM - 1) / BM;
+    const int per = ntm * ntn;
+    if (tau >= p.kgroups * per) return false;
+    const int grp = tau / per, r = tau - grp * per;
+    const int mt = r % ntm, nt = r / ntm;
+    t.expert = grp;
+    t.row0 = mt * BM;
+    t.rows = min(BM, p.M - t.row0);
+    t.n0 = nt * bn_out;
+    return true;
+  }
   if (p.tiles) {
     const int nt_m = *p.ntiles;
     const int gv = nt_m * ntn;
@@ -570,6 +584,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
 
   int kall = 0;
   for (int sg = 0; sg < p.nseg; ++sg) kall += p.seg[sg].K / BKP;
+  // K-grouped problems: this group's K range of the single segment
+  const int64_t kbase = p.kgroups > 0 ? p.kofs[tile.expert] : 0;
+  if (p.kgroups > 0) kall = (p.kofs[tile.expert + 1] - p.kofs[tile.expert]) / BKP;
+  // stages of segment sg (a K-grouped problem's one segment spans its range)
+  auto seg_stages = [&](int sg) { return p.kgroups > 0 ? kall : p.seg[sg].K / BKP; };
   // this block's K stages [k_begin, k_begin + ktot) of the concatenated segments
   const int k_begin = (ks * kall) / kn;
   const int ktot = ((ks + 1) * kall) / kn - k_begin;
@@ -581,11 +600,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
   int seg_i = -1, seg_end = 0, next_kt = k_begin;
   auto start_segment = [&](int sg, int skip) {
     const Seg& g = p.seg[sg];
-    const bf16_t* A = static_cast<const bf16_t*>(g.A) + skip;
+    const bf16_t* A = static_cast<const bf16_t*>(g.A) + kbase + skip;
     const bf16_t* B = static_cast<const bf16_t*>(g.B) +
-                      static_cast<int64_t>(tile.expert) * p.b_expert_stride + skip;
+                      static_cast<int64_t>(tile.expert) * p.b_expert_stride + kbase + skip;
     const bf16_t* B2 = static_cast<const bf16_t*>(g.B2) +
-                       static_cast<int64_t>(tile.expert) * p.b_expert_stride + skip;
+                       static_cast<int64_t>(tile.expert) * p.b_expert_stride + kbase + skip;
 #pragma unroll
     for (int i = 0; i < MA; ++i)
       pa[i] = A + a_off[i] * g.lda + a_chunk[i] * 8;
@@ -597,7 +616,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
     do {
       ++seg_i;
       seg_start = seg_end;
-      seg_end += p.seg[seg_i].K / BKP;
+      seg_end += seg_stages(seg_i);
     } while (seg_end <= k_begin);
     start_segment(seg_i, (k_begin - seg_start) * BKP);
   }
@@ -605,7 +624,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
     if (next_kt == seg_end) {
       ++seg_i;
       start_segment(seg_i, 0);
-      seg_end += p.seg[seg_i].K / BKP;
+      seg_end += seg_stages(seg_i);
     }
     ++next_kt;
 #pragma unroll
@@ -674,6 +693,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
   }
 
   // ---- epilogue straight from the accumulators ----
+  const int64_t cgrp = p.kgroups > 0 ? tile.expert * p.c_group_stride : 0;
   if (kn > 1) {  // fp32 partials, columns in B-row order of the tile
     const int64_t nv = static_cast<int64_t>(ntn) * BN;
     const int64_t cb = static_cast<int64_t>(tile.n0 / BN_OUT) * BN + wn * WTN + (lane & 31);
@@ -714,7 +734,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
             if (p.col_add) x += p.col_add[col];
             static_cast<float*>(p.C)[orow * p.ldc + col] = 1.0f / (1.0f + expf(-x));
           } else if (EPI == EPI_F32) {
-            static_cast<float*>(p.C)[orow * p.ldc + col] = acc[i][j][r];
+            static_cast<float*>(p.C)[cgrp + orow * p.ldc + col] = acc[i][j][r];
           } else {
             store_bf16(p, orow * p.ldc + col, acc[i][j][r]);
           }
@@ -1293,7 +1313,8 @@ static int run_pipe(const Params& p, hipStream_t stream, size_t pad_lds = 0) {
     if (p.seg[s].K % BKP != 0) return MOE_EUNSUPPORTED;
   const int ntn = (p.N + BN_OUT - 1) / BN_OUT;
   const int mt = p.tiles ? p.max_mtiles : (p.M + BM - 1) / BM;
-  const int64_t G = static_cast<int64_t>(mt) * ntn * (p.ksplit > 1 ? p.ksplit : 1);
+  const int64_t G = static_cast<int64_t>(mt) * ntn * (p.ksplit > 1 ? p.ksplit : 1) *
+                    (p.kgroups > 0 ? p.kgroups : 1);
   if (G <= 0) return MOE_OK;
   const int64_t G8 = (G + 7) / 8 * 8;
   if (pad_lds > 0) {  // unused dynamic LDS that caps the blocks per CU
@@ -1433,6 +1454,16 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
   }
   for (int s = 0; s < p.nseg; ++s)
     if (p.seg[s].K % BK != 0) return MOE_EUNSUPPORTED;
+  if (p.kgroups > 0) {
+    // K-grouped weight gradients: fp32 outputs, one segment, no gather or
+    // split; 256 x 256 tiles on 8 waves
+    if (bfmt != B_DENSE || epi != EPI_F32 || p.nseg != 1 || p.tiles || p.a_rows || !p.kofs ||
+        p.C2)
+      return MOE_EUNSUPPORTED;
+    Params q = p;
+    q.ksplit = 1;
+    return dispatch_pipe<256, 256, 2, 64, false, 8>(q, epi, stream);
+  }
   if (bfmt == B_DENSE && p.tiles) {
     // grouped problems stream expert weights: tiles as tall as the expected
     // rows per expert and 256 columns wide (fewer re-reads of the gathered

@@ -44,6 +44,13 @@ struct Params {
   const int32_t* ntiles;     // device count of tiles
   int max_mtiles;            // grid bound on M tiles
   const int32_t* a_rows;     // slot -> A row (null: identity)
+  // K-grouped problems (weight gradients of the routed experts): group g
+  // multiplies A[:, kofs[g], kofs[g+1]) by B[:, the same range]^T into
+  // C + g * c_group_stride, kgroups groups of M x N each.  The K offsets are
+  // multiples of 64 (zero-padded ranges); kgroups = 0: off.
+  const int32_t* kofs;
+  int kgroups;
+  int64_t c_group_stride;
   void* C;
   void* C2;                  // bf16 outputs of dense problems: the rounding residue
                              // bf16(v - bf16(v)) of each value, or null

@@ -15,6 +15,7 @@
 
 #include "common.hpp"
 #include "gemm.hpp"
+#include "layer_kernels.hpp"
 #include "prof.hpp"
 #include "route.hpp"
 
@@ -347,7 +348,7 @@ struct ForwardWorkspace {
 // (exact under QB): 32 for decode-like batches, then 96, 160 or 320 rows
 // (one tile per expert up to 320 rows), else 256; MXFP4 takes 160 when its
 // pipelined kernel applies, else 128.
-static int grouped_bm(const moe_shape_t& s) {
+int grouped_bm(const moe_shape_t& s) {
   const int64_t avg = (static_cast<int64_t>(s.T) * s.top_k + s.n_experts - 1) / s.n_experts;
   if (s.act_dtype != MOE_BF16) return 64;
   if (s.routed_dtype == MOE_MXFP4_A8 || s.routed_dtype == MOE_MXFP4_A4)
@@ -490,15 +491,6 @@ static SideStream* side_stream() {
   return &ss;
 }
 
-static gemm::Seg seg(const void* A, int64_t lda, const void* B, int64_t ldb, int K) {
-  gemm::Seg g{};
-  g.A = A;
-  g.lda = lda;
-  g.B = B;
-  g.ldb = ldb;
-  g.K = K;
-  return g;
-}
 
 static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x, void* out,
                    double* bias, const float* scores_in, float* scores_out, int32_t* idx_out,

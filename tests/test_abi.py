@@ -73,6 +73,32 @@ def test_route_noalloc_validation_on_host():
     assert lib.moe_route_workspace_bytes(6000, 896, 16) <= 32 << 20    # the K3 decode / prefill sizes fit
 
 
+def test_backward_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    ws = lambda **kw: lib.moe_backward_workspace_bytes(ctypes.byref(_shape(moe, **kw)))
+    assert ws() > 0 and ws(T=0) > 0
+    assert ws(routed=moe.MOE_MXFP4) == 0                      # bf16 layers only
+    assert ws(act=moe.MOE_F32, routed=moe.MOE_F32) == 0
+    assert ws(k=897) == 0 and ws(d=7168 + 32) == 0
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    sh = _shape(moe, T=64)
+    wts = moe.MoeWeights(*([1 << 20] * len(moe.MoeWeights._fields_)))
+    grads = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    need = ws(T=64)
+    call = lambda g=grads, w=wts, ws_=fake, nbytes=need: lib.moe_latent_backward(
+        ctypes.byref(sh), ctypes.byref(w), fake, fake, fake, fake, fake, ctypes.byref(g), ws_,
+        nbytes, None)
+    assert call(nbytes=need - 1) == -3
+    assert call(ws_=ctypes.c_void_p((1 << 20) + 8)) == -1
+    no_off = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    no_off.d_router_logit_offset = None                    # the weights have an offset
+    assert call(g=no_off) == -1
+    no_dx = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    no_dx.dx = None
+    assert call(g=no_dx) == -1
+
+
 def test_mxfp4_quantize_validation_on_host():
     import sparse_moe_ffn_sigmoid_amd as moe
     lib = moe.lib()
