@@ -14,6 +14,7 @@
 // slots (zero-padded to 64).  MFMA operands are bf16, accumulations and
 // gradients fp32.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "gemm.hpp"
@@ -80,6 +81,48 @@ __global__ __launch_bounds__(256) void transpose_k(const TI* __restrict__ in, in
   for (int i = ty; i < TB; i += 4) {
     const int64_t c = c0 + i, r = r0 + tx;
     if (c < C && r < R) dst[c * ldo + r] = f32_to_bf16(tile[tx][i]);
+  }
+}
+
+// bf16 -> bf16 transpose with 16-byte accesses: 64 x 64 tiles, each lane
+// loads 8 consecutive elements of a row and stores 8 consecutive elements of
+// an output row (R, C multiples of 8 and 16-byte aligned rows; the launcher
+// checks and otherwise uses transpose_k).
+__global__ __launch_bounds__(256) void transpose16_k(const bf16_t* __restrict__ in, int64_t R,
+                                                     int64_t C, int64_t ldi, int64_t bsi,
+                                                     bf16_t* __restrict__ out, int64_t ldo,
+                                                     int64_t bso) {
+  __shared__ uint16_t tile[TB][TB + 2];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * TB, c0 = static_cast<int64_t>(blockIdx.x) * TB;
+  const bf16_t* src = in + static_cast<int64_t>(blockIdx.z) * bsi;
+  bf16_t* dst = out + static_cast<int64_t>(blockIdx.z) * bso;
+  // load: lane -> (row r0 + tid / 8 + 32 i, columns c0 + 8 (tid % 8) .. +8)
+  const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t r = r0 + lr + 32 * i, c = c0 + lc;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(src + r * ldi + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[lr + 32 * i][lc + 2 * j] = static_cast<uint16_t>(w[j] & 0xFFFFu);
+      tile[lr + 32 * i][lc + 2 * j + 1] = static_cast<uint16_t>(w[j] >> 16);
+    }
+  }
+  __syncthreads();
+  // store: lane -> (output row c0 + tid / 8 + 32 i, output columns r0 + 8 (tid % 8) .. +8)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t c = c0 + lr + 32 * i, r = r0 + lc;
+    if (c < C && r < R) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = static_cast<uint32_t>(tile[lc + 2 * j][lr + 32 * i]) |
+               (static_cast<uint32_t>(tile[lc + 2 * j + 1][lr + 32 * i]) << 16);
+      *reinterpret_cast<uint4*>(dst + c * ldo + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
@@ -302,12 +345,23 @@ __global__ __launch_bounds__(256) void router_wgrad_k(const ACT* __restrict__ x,
   if (doff && blockIdx.x == 0 && threadIdx.x == 0) doff[e] = o;
 }
 
-// dgamma[c] = sum_t q[t][c] (t ascending); one thread per column.
-__global__ void gamma_grad_k(const float* __restrict__ q, int64_t T, int L, float* __restrict__ dg) {
+// dgamma[c] = sum_t q[t][c] in two fixed-order passes: partial sums over
+// chunks of 64 tokens (one thread per (chunk, column)), then over the chunks.
+__global__ void gamma_part_k(const float* __restrict__ q, int64_t T, int L, float* __restrict__ part) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * 64;
+  if (c >= L) return;
+  float a = 0.f;
+  for (int64_t t = t0; t < t0 + 64 && t < T; ++t) a += q[t * L + c];
+  part[blockIdx.y * static_cast<int64_t>(L) + c] = a;
+}
+
+__global__ void gamma_grad_k(const float* __restrict__ part, int64_t chunks, int L,
+                             float* __restrict__ dg) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= L) return;
   float a = 0.f;
-  for (int64_t t = 0; t < T; ++t) a += q[t * L + c];
+  for (int64_t i = 0; i < chunks; ++i) a += part[i * L + c];
   dg[c] = a;
 }
 
@@ -323,7 +377,8 @@ struct BackwardWorkspace {
   uint8_t* sel;
   bf16_t *w_upT, *w_dsT, *w_gsT, *w_usT, *w_downT, *w_dnT, *w_gT, *w_uT;
   bf16_t *z, *h, *hs, *yhat, *dy_slot, *dg, *du, *dgs, *dus, *dz;
-  float *g, *u, *yp, *gs, *us, *dyhat, *dh, *dz_slot, *dhs, *dx_acc, *q, *dw, *dlogit, *dlogit_slot;
+  float *g, *u, *yp, *gs, *us, *dyhat, *dh, *dz_slot, *dhs, *dx_acc, *q, *gpart, *dw, *dlogit,
+      *dlogit_slot;
   bf16_t *xT, *doutT, *yhatT, *hsT, *dgsT, *dusT, *dzT;     // [.][Tp]
   bf16_t *z_slotT, *hT, *dy_slotT, *dgT, *duT;              // [.][Sp]
   int bm, max_mtiles;
@@ -378,6 +433,7 @@ static size_t backward_layout(const moe_shape_t& s, BackwardWorkspace* out, void
   f.dhs = cv.take<float>(T * ms);
   f.dx_acc = cv.take<float>(T * d);
   f.q = cv.take<float>(T * L);
+  f.gpart = cv.take<float>((T + 63) / 64 * L);
   f.dw = cv.take<float>(S);
   f.dlogit = cv.take<float>(S);
   f.dlogit_slot = cv.take<float>(S);
@@ -419,7 +475,15 @@ static void transpose(const TI* in, int64_t R, int64_t C, int64_t ldi, bf16_t* o
                       int batch, int64_t bsi, int64_t bso, hipStream_t st) {
   dim3 grid(static_cast<unsigned>((C + TB - 1) / TB), static_cast<unsigned>((R + TB - 1) / TB),
             static_cast<unsigned>(batch));
-  hipLaunchKernelGGL(transpose_k<TI>, grid, dim3(256), 0, st, in, R, C, ldi, bsi, out, ldo, bso);
+  const bool vec = std::is_same<TI, bf16_t>::value && R % 8 == 0 && C % 8 == 0 && ldi % 8 == 0 &&
+                   ldo % 8 == 0 && bsi % 8 == 0 && bso % 8 == 0 &&
+                   reinterpret_cast<uintptr_t>(in) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(out) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(transpose16_k, grid, dim3(256), 0, st,
+                       reinterpret_cast<const bf16_t*>(in), R, C, ldi, bsi, out, ldo, bso);
+  else
+    hipLaunchKernelGGL(transpose_k<TI>, grid, dim3(256), 0, st, in, R, C, ldi, bsi, out, ldo, bso);
 }
 
 template <typename TI>
@@ -571,8 +635,11 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
                      wt.w_router, k, d, static_cast<bf16_t*>(gr.dx));
   hipLaunchKernelGGL(router_wgrad_k<bf16_t>, dim3((d + 255) / 256, n), dim3(256), 0, st, x, f.offs,
                      f.perm, f.dlogit_slot, d, gr.d_w_router, gr.d_router_logit_offset);
-  hipLaunchKernelGGL(gamma_grad_k, dim3((L + 255) / 256), dim3(256), 0, st, f.q,
-                     static_cast<int64_t>(T), L, gr.d_rms_gamma);
+  const int64_t chunks = (static_cast<int64_t>(T) + 63) / 64;
+  hipLaunchKernelGGL(gamma_part_k, dim3((L + 255) / 256, static_cast<unsigned>(chunks)), dim3(256),
+                     0, st, f.q, static_cast<int64_t>(T), L, f.gpart);
+  hipLaunchKernelGGL(gamma_grad_k, dim3((L + 255) / 256), dim3(256), 0, st, f.gpart, chunks, L,
+                     gr.d_rms_gamma);
   MOE_LAUNCH_CHECK();
 
   // 6. dense weight gradients: [out][in] = sum over tokens (K = T, padded)
