@@ -103,8 +103,14 @@ enum {
   MOE_QB_STATUS_ABORTED = 3 /* a grid-barrier wait timed out: outputs undefined */
 };
 
+/* Largest batch any entry point takes (2^20 tokens; larger T returns
+ * MOE_EUNSUPPORTED).  Far above what one GPU's memory holds for the K3 layer,
+ * and small enough that every slot, tile and edge count of the kernels fits in
+ * 32 bits. */
+#define MOE_MAX_TOKENS (1 << 20)
+
 typedef struct {
-  int32_t T;             /* tokens in the batch (>= 0) */
+  int32_t T;             /* tokens in the batch, 0..MOE_MAX_TOKENS */
   int32_t d;             /* model width (7168 for K3), multiple of 64 */
   int32_t latent;        /* latent width (d/2 = 3584 for K3), multiple of 64 */
   int32_t n_experts;     /* routed experts (896), 1..1024 */

@@ -459,7 +459,8 @@ static int validate(const moe_shape_t* sp) {
   if (s.T < 0 || s.n_experts < 1 || s.top_k < 1 || s.top_k > s.n_experts) return MOE_EINVAL;
   if (s.d <= 0 || s.latent <= 0 || s.inter <= 0 || s.shared_inter <= 0) return MOE_EINVAL;
   if (s.d % 64 || s.latent % 64 || s.inter % 64 || s.shared_inter % 64) return MOE_EINVAL;
-  if (s.n_experts > 1024 || s.top_k > 64 || s.latent > 256 * MAXV) return MOE_EUNSUPPORTED;
+  if (s.n_experts > 1024 || s.top_k > 64 || s.latent > 256 * MAXV || s.T > MOE_MAX_TOKENS)
+    return MOE_EUNSUPPORTED;
   if (s.act_dtype != MOE_BF16 || s.routed_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if (!(s.rms_eps >= 0.f)) return MOE_EINVAL;
   return MOE_OK;

@@ -1728,8 +1728,10 @@ __global__ void prep_scores(const float* __restrict__ in, float* __restrict__ ou
 // ---------------------------------------------------------------------------
 
 // Edge list: 16 per token on average plus, in every segment, room for the
-// largest list one token can emit (64 x 64).
+// largest list one token can emit (64 x 64); T <= MOE_MAX_TOKENS keeps it in
+// 32 bits.
 static int32_t edge_capacity(int32_t T) { return 16 * T + qb::EDGE_SEGS * 4096; }
+static_assert(16ll * MOE_MAX_TOKENS + qb::EDGE_SEGS * 4096ll < (1ll << 31), "edge count in 32 bits");
 
 size_t route_workspace_layout(int32_t T, int32_t n, RouteWorkspace* ws, void* base) {
   Carver cv(base);
@@ -1750,7 +1752,7 @@ size_t route_workspace_layout(int32_t T, int32_t n, RouteWorkspace* ws, void* ba
 
 int route_validate(int32_t T, int32_t n, int32_t k) {
   if (T < 0 || n < 1 || k < 1 || k > n) return MOE_EINVAL;
-  if (n > 1024 || k > qb::MAX_K) return MOE_EUNSUPPORTED;
+  if (n > 1024 || k > qb::MAX_K || T > MOE_MAX_TOKENS) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
