@@ -14,6 +14,7 @@ import torch
 import workloads
 from layer_cases import announce, oracle_scores, rel_err, to_device, make_shape
 from oracle import grad as ograd
+from oracle import layer as olayer
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +87,7 @@ def check_backward(shape, seed, name):
     dict(T=37, n=24, k=3, d=448, latent=192, m=128, shared=192),
     dict(T=16, n=64, k=4),                                    # ~1 row per expert, unused experts
     dict(T=1000, n=16, k=4, seed=7),                          # 250 rows per expert
+    dict(T=584, n=64, k=8, seed=4),                           # 73 rows: the 96-row tiles
 ])
 def test_bf16_backward(kw):
     kw = dict(kw)
@@ -123,3 +125,60 @@ def test_backward_deterministic():
             assert torch.equal(a[key].view(torch.uint8) if a[key].dtype == torch.bfloat16
                                else a[key], b[key].view(torch.uint8)
                                if b[key].dtype == torch.bfloat16 else b[key]), key
+
+
+def test_backward_k3_prefill_full_size_dx_sampled():
+    """The full K3 prefill layer (T = 4096, 896 experts, k = 16), forward and
+    backward as the benchmark runs them; dx of sampled tokens (first, thirds,
+    last and the last token of the first and last expert) against the
+    gradient oracle on each token alone.  Tokens are independent once the
+    selection is fixed, so a token's dx needs only its own 16 experts: the
+    oracle runs on the token with those experts' weights (router rows, gate,
+    up, down) and the full dense weights."""
+    import sparse_moe_ffn_sigmoid_amd as moe
+    shape = workloads.SHAPES["k3_prefill"]
+    announce(f"backward full size {shape}")
+    dev = torch.device("cuda:0")
+    inp = workloads.layer_inputs(shape, dev, seed=0)
+    w = {key: v for key, v in inp.items() if key != "x" and v is not None}
+    w["router_logit_offset"] = w.pop("logit_offset")
+    sh = moe.make_shape(shape.T, shape.d, shape.latent, shape.n, shape.k, shape.m, shape.shared,
+                        moe.MOE_BF16, moe.MOE_BF16, shape.eps, moe.MOE_QB_BATCH, 64)
+    fwd = moe.latent_forward(sh, w, inp["x"], want_scores=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    dout = torch.randn(inp["x"].shape, generator=g, device=dev, dtype=torch.float32).to(
+        torch.bfloat16)
+    got = moe.latent_backward(sh, w, inp["x"], fwd["scores"], fwd["idx"], fwd["w"], dout)
+    torch.cuda.synchronize()
+    idx = fwd["idx"].cpu().numpy()
+    dx = got["dx"].float().cpu().numpy()
+    del got
+    torch.cuda.empty_cache()
+    T = shape.T
+    flat = idx.ravel()
+    tokens = [0, T // 3, (2 * T) // 3, T - 1,
+              int(np.nonzero(flat == idx.min())[0].max()) // shape.k,
+              int(np.nonzero(flat == idx.max())[0].max()) // shape.k]
+    dense = {key: olayer.as_f64(inp[key]) for key in ("w_down", "w_up", "rms_gamma", "ws_gate",
+                                                       "ws_up", "ws_down")}
+    ref_rows, got_rows = [], []
+    for t in sorted(set(tokens)):
+        sel = torch.from_numpy(idx[t].astype(np.int64)).to(dev)
+        sub = dict(dense)
+        sub["x"] = olayer.as_f64(inp["x"][t:t + 1])
+        for key in ("w_router", "logit_offset", "w_gate", "w_uproj", "w_dn"):
+            sub[key] = olayer.as_f64(inp[key][sel])
+        ref = ograd.layer_grads(sub, np.arange(shape.k)[None, :], shape.eps,
+                                dout[t:t + 1].double().cpu().numpy())
+        ref_rows.append(ref["x"][0])
+        got_rows.append(dx[t])
+        row = float(np.linalg.norm(dx[t] - ref["x"][0]) / np.linalg.norm(ref["x"][0]))
+        print(f"  token {t}: dx rel. error {row:.2e}", flush=True)
+        assert row <= TOL_ROW
+    r, gv = np.stack(ref_rows), np.stack(got_rows)
+    fro = float(np.linalg.norm(gv - r) / np.linalg.norm(r))
+    print(f"  sampled dx rel. Frobenius {fro:.2e}", flush=True)
+    assert fro <= TOL_FRO
+    del inp, fwd, dout
+    torch.cuda.empty_cache()
