@@ -8,11 +8,12 @@
 //
 // The call recomputes the forward activations from x and the forward's
 // routing (scores, idx, w), then runs the backward products on the same
-// pipelined MFMA GEMM (C = A B^T with both operands K-contiguous).  Products
-// whose operands are not K-contiguous take transposed copies; the weight
-// gradients of the routed experts are K-grouped products over each expert's
-// slots (zero-padded to 64).  MFMA operands are bf16, accumulations and
-// gradients fp32.
+// pipelined MFMA GEMM (C = A B^T).  The experts' weights enter the products
+// through them as [K][N] B operands read in place (transposing LDS reads);
+// other operands that are not K-contiguous take transposed copies; the
+// weight gradients of the routed experts are K-grouped products over each
+// expert's slots (zero-padded to 64).  MFMA operands are bf16,
+// accumulations and gradients fp32.
 #include <algorithm>
 #include <type_traits>
 
@@ -375,7 +376,7 @@ __global__ void fill_f32(float* p, int64_t count) {
 struct BackwardWorkspace {
   int32_t *loads, *offs, *poffs, *tiles, *ntiles, *perm, *inv, *pcol;
   uint8_t* sel;
-  bf16_t *w_upT, *w_dsT, *w_gsT, *w_usT, *w_downT, *w_dnT, *w_gT, *w_uT;
+  bf16_t *w_upT, *w_dsT, *w_gsT, *w_usT, *w_downT;
   bf16_t *z, *h, *hs, *yhat, *dy_slot, *dg, *du, *dgs, *dus, *dz;
   float *g, *u, *yp, *gs, *us, *dyhat, *dh, *dz_slot, *dhs, *dx_acc, *q, *gpart, *dw, *dlogit,
       *dlogit_slot;
@@ -409,9 +410,6 @@ static size_t backward_layout(const moe_shape_t& s, BackwardWorkspace* out, void
   f.w_gsT = cv.take<bf16_t>(d * ms);
   f.w_usT = cv.take<bf16_t>(d * ms);
   f.w_downT = cv.take<bf16_t>(d * L);
-  f.w_dnT = cv.take<bf16_t>(n * m * L);
-  f.w_gT = cv.take<bf16_t>(n * L * m);
-  f.w_uT = cv.take<bf16_t>(n * L * m);
   f.z = cv.take<bf16_t>(T * L);
   f.h = cv.take<bf16_t>(S * m);
   f.hs = cv.take<bf16_t>(T * ms);
@@ -521,9 +519,11 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
     p.ldc = ldc;
     return gemm::launch(p, epi, gemm::B_DENSE, true, 128, st);
   };
+  // bfmt B_DENSE: B [N][K] per expert; B_DENSE_KN: B [K][N] per expert (the
+  // experts' weights read transposed in place)
   auto grouped = [&](const void* A, int64_t lda, const int32_t* rows, const void* B, int64_t ldb,
-                     int64_t bstride, int K, int N, float* C, int64_t ldc, const void* A2 = nullptr,
-                     const void* B2 = nullptr) {
+                     int64_t bstride, int K, int N, float* C, int64_t ldc, int bfmt = gemm::B_DENSE,
+                     const void* A2 = nullptr, const void* B2 = nullptr) {
     gemm::Params p{};
     p.N = N;
     p.nseg = A2 ? 2 : 1;
@@ -536,7 +536,7 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
     p.a_rows = rows;
     p.C = C;
     p.ldc = ldc;
-    return gemm::launch(p, gemm::EPI_F32, gemm::B_DENSE, true, f.bm, st);
+    return gemm::launch(p, gemm::EPI_F32, bfmt, true, f.bm, st);
   };
   auto kgrouped = [&](const bf16_t* A, const bf16_t* B, int M, int N, float* C) {
     gemm::Params p{};
@@ -565,7 +565,8 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
   hipLaunchKernelGGL(slot_cols, dim3(n), dim3(256), 0, st, f.offs, f.poffs, f.pcol);
   MOE_LAUNCH_CHECK();
 
-  // 1. transposed weights (B operands of the products through them)
+  // 1. transposed dense weights (B operands of the products through them;
+  // the experts' weights are read in place as [K][N] operands)
   const bf16_t* W_down = static_cast<const bf16_t*>(wt.w_down);
   const bf16_t* W_up = static_cast<const bf16_t*>(wt.w_up);
   const bf16_t* W_g = static_cast<const bf16_t*>(wt.w_gate);
@@ -580,9 +581,6 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
   transpose(W_us, ms, d, d, f.w_usT, ms, 1, 0, 0, st);        // [d][ms]
   transpose(W_down, L, d, d, f.w_downT, L, 1, 0, 0, st);      // [d][L]
   const int64_t es = static_cast<int64_t>(m) * L;
-  transpose(W_dn, L, m, m, f.w_dnT, L, n, es, es, st);        // [n][m][L]
-  transpose(W_g, m, L, L, f.w_gT, m, n, es, es, st);          // [n][L][m]
-  transpose(W_u, m, L, L, f.w_uT, m, n, es, es, st);          // [n][L][m]
   MOE_LAUNCH_CHECK();
 
   // 2. forward activations
@@ -607,11 +605,13 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
   MOE_LAUNCH_CHECK();
 
   // 4. routed experts: dh = dy_slot W_dn, SiTU-GLU, dz_slot = dg W_g + du W_u
-  if ((rc = grouped(f.dy_slot, L, nullptr, f.w_dnT, L, es, L, m, f.dh, m)) != MOE_OK) return rc;
+  if ((rc = grouped(f.dy_slot, L, nullptr, W_dn, m, es, L, m, f.dh, m, gemm::B_DENSE_KN)) != MOE_OK)
+    return rc;
   hipLaunchKernelGGL(situ_bwd_k, dim3(grid_of(S * m)), dim3(256), 0, st, f.g, f.u, f.dh, S * m,
                      f.dg, f.du);
   MOE_LAUNCH_CHECK();
-  if ((rc = grouped(f.dg, m, nullptr, f.w_gT, m, es, m, L, f.dz_slot, L, f.du, f.w_uT)) != MOE_OK)
+  if ((rc = grouped(f.dg, m, nullptr, W_g, L, es, m, L, f.dz_slot, L, gemm::B_DENSE_KN, f.du,
+                    W_u)) != MOE_OK)
     return rc;
   hipLaunchKernelGGL(dz_gather_k, dim3(T), dim3(256), 0, st, f.dz_slot, f.inv, k, L, f.dz);
 

@@ -487,7 +487,34 @@ __device__ __forceinline__ int swz(int r) {
   return BKP == 64 ? (r & 7) : ((r >> 1) & 3);
 }
 
-template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT, int NW>
+// B stored [K][N] (BKN): a stage holds BKP k-rows of BN columns (N
+// contiguous), 16-byte chunks swizzled by kn_swz(row) = 0, 6, 12, 10 for
+// row mod 4.  The B operand of an MFMA comes from two ds_read_b64_tr_b16
+// reads: within each 16-lane group, lane 4j + q addresses the 4 columns
+// n0 + 4q .. n0 + 4q + 3 of k-row k0 + j, and lane i receives column n0 + i
+// of k-rows k0 .. k0 + 3.  The swizzle keeps the 4 rows x 32 bytes of one
+// group, and the 4 rows x 64 bytes of two groups, on distinct LDS banks.
+__device__ __forceinline__ int kn_swz(int row) { return (6 * (row & 1)) ^ (12 * ((row >> 1) & 1)); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8_t read_b_kn(const bf16_t* lo, const bf16_t* hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lo));
+  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(hi));
+  const s16x8_t v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+#else
+  (void)lo;
+  (void)hi;
+  return bf16x8_t{};
+#endif
+}
+
+// BKN: B is stored [K][N] (see kn_swz); EPI_F32 / EPI_BF16 only.
+template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT, int NW, bool BKN = false>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 256) ? 2 : 1) void gemm_pipe(Params p) {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves per block");
   constexpr int WN = NW / WM;
@@ -496,6 +523,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold 32x32 blocks");
   static_assert(EPI != EPI_SITU || FN % 2 == 0, "SiTU needs gate/up fragment pairs");
   static_assert(BKP == 64 || BKP == 32, "stage depth");
+  static_assert(!BKN || (EPI != EPI_SITU && EPI != EPI_SIGMOID && BN % 128 == 0),
+                "[K][N] B operands: plain epilogues, 16 or more chunks per k-row");
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   constexpr int CH = BKP / 8;        // 16-byte chunks per row
   constexpr int RPI = 64 / CH;       // rows per load instruction
@@ -568,6 +597,17 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
   bool b_up[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
+    if constexpr (BKN) {  // k-row of the stage and the first column of this lane's chunk
+      constexpr int CPR = BN / 8;
+      const int slot = b_ins(wave, i) * 64 + lane;
+      const int kr = slot / CPR;
+      int col = tile.n0 + ((slot % CPR) ^ kn_swz(kr)) * 8;
+      col = col + 8 <= p.N ? col : p.N - 8;  // past N: a valid chunk, never stored
+      b_up[i] = false;
+      b_off[i] = kr;
+      b_chunk[i] = col;
+      continue;
+    }
     const int r = b_ins(wave, i) * RPI + lrow;
     b_chunk[i] = (lane % CH) ^ swz<BKP>(r);
     int row;
@@ -594,9 +634,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
   const int ktot = ((ks + 1) * kall) / kn - k_begin;
 
   // Per-lane source pointers of the next tile to issue; tiles are issued in
-  // order, so the pointers advance by BKP and are reset at segment starts.
+  // order, so the pointers advance by one stage of K and are reset at
+  // segment starts.
   const bf16_t* pa[MA];
   const bf16_t* pb[MB];
+  int64_t bstep = BKP;  // elements a B pointer advances per stage
   int seg_i = -1, seg_end = 0, next_kt = k_begin;
   auto start_segment = [&](int sg, int skip) {
     const Seg& g = p.seg[sg];
@@ -608,8 +650,18 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
 #pragma unroll
     for (int i = 0; i < MA; ++i)
       pa[i] = A + a_off[i] * g.lda + a_chunk[i] * 8;
+    if constexpr (BKN) {
+      // B [K][N]: k advances by rows
+      const bf16_t* Bk = static_cast<const bf16_t*>(g.B) +
+                         static_cast<int64_t>(tile.expert) * p.b_expert_stride +
+                         (kbase + skip) * g.ldb;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) pb[i] = (b_up[i] ? B2 : B) + b_off[i] * g.ldb + b_chunk[i] * 8;
+      for (int i = 0; i < MB; ++i) pb[i] = Bk + b_off[i] * g.ldb + b_chunk[i];
+      bstep = static_cast<int64_t>(BKP) * g.ldb;
+    } else {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) pb[i] = (b_up[i] ? B2 : B) + b_off[i] * g.ldb + b_chunk[i] * 8;
+    }
   };
   if (ktot > 0) {  // position the walk at k_begin
     int seg_start = 0;
@@ -635,7 +687,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       load_lds16(pb[i], Bs + b_ins(wave, i) * 512, BNT);
-      pb[i] += BKP;
+      pb[i] += bstep;
     }
   };
 
@@ -656,9 +708,23 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
 #pragma unroll
       for (int i = 0; i < FM; ++i)
         af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * WTM + i * 32 + (lane & 31)) * BKP + ch);
+      if constexpr (BKN) {
+        // lane (group g, 4j + q): k-rows kk*16 + (g/2)*8 + j (+4), columns
+        // (g%2)*16 + 4q of the fragment
+        const int grp = lane >> 4, jq = lane & 15;
+        const int r0 = kk * 16 + (grp >> 1) * 8 + (jq >> 2);
+        const int sw = kn_swz(r0);  // r0 + 4 has the same swizzle
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WTN + j * 32 + (lane & 31)) * BKP + ch);
+        for (int j = 0; j < FN; ++j) {
+          const int col = wn * WTN + j * 32 + (grp & 1) * 16 + (jq & 3) * 4;
+          const int off = ((col >> 3) ^ sw) * 8 + (col & 7);
+          bfr[j] = read_b_kn(Bs + r0 * BN + off, Bs + (r0 + 4) * BN + off);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WTN + j * 32 + (lane & 31)) * BKP + ch);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1306,7 +1372,7 @@ static int run_bf16(const Params& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT, int NW = 4>
+template <int BM, int BN, int WM, int EPI, int BKP, int NST, bool BNT, int NW = 4, bool BKN = false>
 static int run_pipe(const Params& p, hipStream_t stream, size_t pad_lds = 0) {
   constexpr int BN_OUT = (EPI == EPI_SITU) ? BN / 2 : BN;
   for (int s = 0; s < p.nseg; ++s)
@@ -1320,14 +1386,14 @@ static int run_pipe(const Params& p, hipStream_t stream, size_t pad_lds = 0) {
   if (pad_lds > 0) {  // unused dynamic LDS that caps the blocks per CU
     static std::atomic<bool> configured{false};
     if (!configured.load(std::memory_order_relaxed)) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT, NW>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT, NW, BKN>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(pad_lds)) != hipSuccess)
         return MOE_EHIP;
       configured.store(true, std::memory_order_relaxed);
     }
   }
-  hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT, NW>), dim3(static_cast<unsigned>(G8)),
+  hipLaunchKernelGGL((gemm_pipe<BM, BN, WM, EPI, BKP, NST, BNT, NW, BKN>), dim3(static_cast<unsigned>(G8)),
                      dim3(64 * NW), pad_lds, stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -1463,6 +1529,24 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
     Params q = p;
     q.ksplit = 1;
     return dispatch_pipe<256, 256, 2, 64, false, 8>(q, epi, stream);
+  }
+  if (bfmt == B_DENSE_KN) {
+    // grouped problems whose B is stored [K][N] (the experts' weights read
+    // transposed), fp32 outputs; the tiles of the B_DENSE grouped problems
+    if (!p.tiles || epi != EPI_F32 || p.C2 || p.N % 8 != 0 || p.b_expert_stride % 8 != 0)
+      return MOE_EUNSUPPORTED;
+    for (int s = 0; s < p.nseg; ++s)
+      if (p.seg[s].ldb % 8 != 0 || reinterpret_cast<uintptr_t>(p.seg[s].B) % 16 != 0 ||
+          p.seg[s].B2)
+        return MOE_EUNSUPPORTED;
+    Params q = p;
+    q.ksplit = 1;
+    if (bm_hint <= 32) return run_pipe<32, 256, 1, EPI_F32, 64, 3, true, 4, true>(q, stream);
+    if (bm_hint <= 96) return run_pipe<96, 256, 1, EPI_F32, 64, 3, true, 4, true>(q, stream);
+    if (bm_hint == 160) return run_pipe<160, 256, 1, EPI_F32, 64, 3, false, 4, true>(q, stream);
+    if (bm_hint == 320) return run_pipe<320, 256, 2, EPI_F32, 64, 2, true, 8, true>(q, stream);
+    if (bm_hint == 256) return run_pipe<256, 256, 2, EPI_F32, 64, 2, false, 8, true>(q, stream);
+    return run_pipe<128, 128, 2, EPI_F32, 32, 3, false, 4, true>(q, stream);
   }
   if (bfmt == B_DENSE && p.tiles) {
     // grouped problems stream expert weights: tiles as tall as the expected

@@ -14,8 +14,10 @@ enum Epilogue : int {
 };
 
 // B_MXFP4_A8: MXFP4 B with MXFP8 (E4M3) A codes and E8M0 A scales (W4A8);
-// B_MXFP4_A4: MXFP4 B with MXFP4 (E2M1, two per byte) A codes (W4A4)
-enum BFormat : int { B_DENSE = 0, B_MXFP4 = 1, B_MXFP4_A8 = 2, B_MXFP4_A4 = 3 };
+// B_MXFP4_A4: MXFP4 B with MXFP4 (E2M1, two per byte) A codes (W4A4);
+// B_DENSE_KN: bf16 B stored [K][N] (N contiguous, ldb = elements per k-row),
+// grouped problems with fp32 outputs only.
+enum BFormat : int { B_DENSE = 0, B_MXFP4 = 1, B_MXFP4_A8 = 2, B_MXFP4_A4 = 3, B_DENSE_KN = 4 };
 
 // One K segment: A [rows][K] (K contiguous, leading dim lda), B [N][K] (ldb).
 struct Seg {
