@@ -153,6 +153,50 @@ def time_backward(moe, sh, w, x, bias0, ws, shape, args):
                     "recomputed inside), selection held fixed"}
 
 
+def time_train(moe, sh, w, x, bias0, ws, shape, args, fused=True):
+    """One training step: forward with QB on the batch (the bias carried from
+    step to step), backward with a seeded N(0,1) output gradient, and the SGD
+    update of every weight in place (lr 1e-6): fused (moe_latent_backward_sgd,
+    the experts' gradients applied where they are formed) or as two calls
+    (moe_latent_backward, then moe_sgd_step).  Timed like the forward; the
+    weights change from step to step as in training."""
+    import torch
+    g = torch.Generator(device=x.device)
+    g.manual_seed(4321)
+    dout = torch.randn(x.shape, generator=g, device=x.device, dtype=torch.float32).to(x.dtype)
+    bws = torch.empty(moe.lib().moe_backward_workspace_bytes(ctypes_ref(sh)), dtype=torch.uint8,
+                      device=x.device)
+    bias = bias0.clone()
+
+    def step():
+        nonlocal bias
+        fwd = moe.latent_forward(sh, w, x, bias=bias, workspace=ws, want_scores=True)
+        bias = fwd["bias"]
+        if fused:
+            moe.latent_backward_sgd(sh, w, x, fwd["scores"], fwd["idx"], fwd["w"], dout, 1e-6,
+                                    workspace=bws)
+        else:
+            grads = moe.latent_backward(sh, w, x, fwd["scores"], fwd["idx"], fwd["w"], dout,
+                                        workspace=bws)
+            moe.sgd_step(sh, w, grads, 1e-6)
+
+    step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    del bws
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "tokens_per_s": shape.T / (ms / 1e3),
+            "what": "forward (QB on the batch) + backward + SGD update of every weight" +
+                    (" (update fused into the expert weight-gradient GEMMs)" if fused else
+                     " (backward and update as two calls)")}
+
+
 def ctypes_ref(obj):
     import ctypes
     return ctypes.byref(obj)
@@ -322,6 +366,10 @@ def main():
     ap.add_argument("--sign-baseline", action="store_true",
                     help="also route this batch's scores with the fixed-step sign update "
                          "(DeepSeek-V3's bias rule) and report rounds / imbalance / time beside QB")
+    ap.add_argument("--train", action="store_true",
+                    help="also time a training step (forward, backward, SGD update; bf16 layers); "
+                         "reported under 'train', after every other measurement (it changes "
+                         "the weights)")
     ap.add_argument("--backward", action="store_true",
                     help="also time moe_latent_backward (bf16 layers) on this batch's routing and "
                          "a random output gradient; reported under 'backward'")
@@ -461,6 +509,9 @@ def main():
         copy_reference(args.copy_bytes, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, shape, args.cpu_sample_tokens)
+    if args.train:  # last: it updates the weights in place
+        rec["train"] = time_train(moe, sh, w, x, bias0, ws, shape, args)
+        rec["train_separate"] = time_train(moe, sh, w, x, bias0, ws, shape, args, fused=False)
     print(json.dumps(rec), flush=True)
 
 

@@ -312,6 +312,44 @@ int moe_latent_backward(const moe_shape_t* shape, const moe_weights_t* weights, 
                         const void* dout, const moe_grads_t* grads, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * moe_sgd_step -- one plain gradient-descent step on every weight of the
+ * layer, in place: w <- w - lr * g, the optimizer step that completes a
+ * training step after moe_latent_backward (the pages place QB in training,
+ * where the bias is set again for every batch: dimsnsums.com "Kimi K3 --
+ * LatentMoE", Quantile Balancing paragraph; they name no optimizer for the
+ * layer's weights, and the plainest one is taken).
+ *   shape   : as for moe_latent_backward (bf16 layers only)
+ *   weights : the layer's weights; the buffers it points to are updated in
+ *             place (router, its offset when present, latent down and up,
+ *             routed gate, up and down, RMSNorm gain, shared gate, up, down)
+ *   grads   : their gradients (moe_latent_backward's output)
+ *   lr      : step size, finite
+ * Every element is computed as fp32 operations, each rounded to nearest
+ * even: t = lr * g, then w - t, then the weight's own type (fp32 for the
+ * router, its offset and the gain; bf16, round to nearest even, for the
+ * rest).  No contraction into a fused multiply-add, so results are exactly
+ * defined.  Enqueued on `stream`; NULL required buffers return MOE_EINVAL.
+ */
+int moe_sgd_step(const moe_shape_t* shape, const moe_weights_t* weights, const moe_grads_t* grads,
+                 float lr, void* stream);
+
+/*
+ * moe_latent_backward_sgd -- moe_latent_backward followed by moe_sgd_step,
+ * with the same results bit for bit, but the routed experts' weight
+ * gradients (the three largest tensors, fp32 [n][inter][latent] and
+ * [n][latent][inter]) are never stored: each is applied to its weight inside
+ * the kernel that forms it, after every read of that weight.  Arguments as
+ * for moe_latent_backward plus lr (finite); grads->d_w_gate, d_w_uproj and
+ * d_w_dn are not used (may be NULL), every other gradient is written and
+ * applied.  Every weight buffer is updated in place.  T = 0: the gradients
+ * are left as they are and no weight moves.
+ */
+int moe_latent_backward_sgd(const moe_shape_t* shape, const moe_weights_t* weights, const void* x,
+                            const float* scores, const int32_t* topk_idx, const float* topk_w,
+                            const void* dout, const moe_grads_t* grads, float lr, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Static description of a moe_status value; never NULL. */
 const char* moe_status_str(int status);
 

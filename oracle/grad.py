@@ -22,6 +22,12 @@ carries a gradient):
 
 Routed experts are dense (bf16-valued) matrices; MXFP4 weights are a
 deployment format and are not trained here.
+
+:func:`sgd_step` is the optimizer step that completes a training step: the
+pages name no optimizer for the layer's weights (the Kimi K3 pages' Per-Head
+Muon is outside this layer), so the plainest one, w <- w - lr * g, as
+stated fp32 operations (each rounded to nearest even) stored in the
+weight's own type.
 """
 from __future__ import annotations
 
@@ -86,3 +92,17 @@ def layer_grads(inp, idx, eps, dout):
     res = {key: (None if P[key] is None else P[key].grad.numpy()) for key in GRAD_KEYS}
     res["out"] = out.detach().numpy()
     return res
+
+
+def sgd_step(w, g, lr, dtype):
+    """One gradient-descent step on one weight tensor: t = fp32(lr * g), then
+    fp32(w - t), each rounded to nearest even (IEEE single precision, no
+    fused multiply-add), then stored as ``dtype`` ("f32", or "bf16" rounded
+    to nearest even).  Returns float64 values of the stored result."""
+    w32 = np.asarray(layer.as_f64(w), np.float64).astype(np.float32)
+    g32 = np.asarray(layer.as_f64(g), np.float64).astype(np.float32)
+    t = np.multiply(np.float32(lr), g32, dtype=np.float32)
+    r = np.subtract(w32, t, dtype=np.float32)
+    if dtype == "bf16":
+        return layer.bf16_round(r.astype(np.float64))
+    return r.astype(np.float64)

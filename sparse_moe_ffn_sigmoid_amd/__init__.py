@@ -27,7 +27,8 @@ EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_route_sign",
             "moe_forward_workspace_bytes",
             "moe_latent_forward", "moe_status_str", "moe_stage_timing", "moe_stage_times",
             "moe_stage_name", "moe_mxfp8_quantize", "moe_mxfp4_quantize",
-            "moe_route_qb_noalloc", "moe_backward_workspace_bytes", "moe_latent_backward")
+            "moe_route_qb_noalloc", "moe_backward_workspace_bytes", "moe_latent_backward",
+            "moe_sgd_step", "moe_latent_backward_sgd")
 
 
 class MoeShape(ctypes.Structure):
@@ -81,6 +82,13 @@ _lib.moe_backward_workspace_bytes.restype = _sz
 _lib.moe_latent_backward.argtypes = [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _vp, _vp,
                                      _vp, _vp, _vp, ctypes.POINTER(MoeGrads), _vp, _sz, _vp]
 _lib.moe_latent_backward.restype = ctypes.c_int
+_lib.moe_sgd_step.argtypes = [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights),
+                              ctypes.POINTER(MoeGrads), ctypes.c_float, _vp]
+_lib.moe_sgd_step.restype = ctypes.c_int
+_lib.moe_latent_backward_sgd.argtypes = [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _vp,
+                                         _vp, _vp, _vp, _vp, ctypes.POINTER(MoeGrads),
+                                         ctypes.c_float, _vp, _sz, _vp]
+_lib.moe_latent_backward_sgd.restype = ctypes.c_int
 _lib.moe_mxfp4_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
 _lib.moe_mxfp4_quantize.restype = ctypes.c_int
 _lib.moe_mxfp8_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
@@ -269,6 +277,66 @@ def latent_backward(shape: MoeShape, weights: dict, x: torch.Tensor, scores: tor
     if st != 0:
         raise MoeError(st, "moe_latent_backward")
     return out
+
+
+EXPERT_GRADS = ("d_w_gate", "d_w_uproj", "d_w_dn")
+
+
+def latent_backward_sgd(shape: MoeShape, weights: dict, x: torch.Tensor, scores: torch.Tensor,
+                        idx: torch.Tensor, w: torch.Tensor, dout: torch.Tensor, lr: float,
+                        workspace=None):
+    """latent_backward followed by sgd_step in one call, the routed experts'
+    weight gradients applied in place without being stored.  Updates every
+    weight tensor of `weights`; returns the other gradients (dx, d_w_router,
+    ...; the three expert entries are None)."""
+    dev = x.device
+    T, d, l, n, k = shape.T, shape.d, shape.latent, shape.n_experts, shape.top_k
+    m, ms = shape.inter, shape.shared_inter
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(dout, "dout", torch.bfloat16, (T, d), dev)
+    _check(scores, "scores", torch.float32, (T, n), dev)
+    _check(idx, "idx", torch.int32, (T, k), dev)
+    _check(w, "w", torch.float32, (T, k), dev)
+    wts = MoeWeights(*[None if weights.get(f) is None else weights[f].data_ptr()
+                       for f, _ in MoeWeights._fields_])
+    out = {"dx": torch.empty((T, d), dtype=torch.bfloat16, device=dev)}
+    for name, (key, fn) in GRAD_SHAPES.items():
+        if weights.get(key) is None or name in EXPERT_GRADS:
+            out[name] = None
+        else:
+            out[name] = torch.empty(fn(T, d, l, n, k, m, ms), dtype=torch.float32, device=dev)
+    grads = MoeGrads(*[None if out[f] is None else out[f].data_ptr() for f, _ in MoeGrads._fields_])
+    need = _lib.moe_backward_workspace_bytes(ctypes.byref(shape))
+    if need == 0:
+        raise MoeError(-2, "moe_backward_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _lib.moe_latent_backward_sgd(ctypes.byref(shape), ctypes.byref(wts), _ptr(x),
+                                      _ptr(scores), _ptr(idx), _ptr(w), _ptr(dout),
+                                      ctypes.byref(grads), ctypes.c_float(lr), _ptr(ws),
+                                      ws.numel(), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_latent_backward_sgd")
+    return out
+
+
+def sgd_step(shape: MoeShape, weights: dict, grads: dict, lr: float):
+    """One gradient-descent step in place on the weight tensors of `weights`
+    (w <- w - lr * g, fp32 operations, stored in each weight's type) from
+    `grads` as returned by latent_backward (dx is not used)."""
+    wts = MoeWeights(*[None if weights.get(f) is None else weights[f].data_ptr()
+                       for f, _ in MoeWeights._fields_])
+    gr = MoeGrads(*[None if f == "dx" or grads.get(f) is None else grads[f].data_ptr()
+                    for f, _ in MoeGrads._fields_])
+    for name, (key, _) in GRAD_SHAPES.items():
+        wt, g = weights.get(key), grads.get(name)
+        if (wt is None) != (g is None) or (g is not None and (
+                g.dtype != torch.float32 or g.shape != wt.shape or not g.is_contiguous()
+                or not wt.is_contiguous() or g.device != wt.device)):
+            raise ValueError(f"sgd_step: {name} does not match {key}")
+    st = _lib.moe_sgd_step(ctypes.byref(shape), ctypes.byref(wts), ctypes.byref(gr),
+                           ctypes.c_float(lr), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_sgd_step")
 
 
 def make_shape(T, d, latent, n, k, inter, shared_inter, act_dtype, routed_dtype,

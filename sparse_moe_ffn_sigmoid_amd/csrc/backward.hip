@@ -15,6 +15,7 @@
 // expert's slots (zero-padded to 64).  MFMA operands are bf16,
 // accumulations and gradients fp32.
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "common.hpp"
@@ -498,9 +499,13 @@ static void zero(void* p, int64_t bytes, hipStream_t st) {
                      static_cast<uint32_t*>(p), 0u, bytes / 4);
 }
 
+// sgd_lr: when not null, the routed experts' weight gradients are not
+// stored: each is applied to its weight in the GEMM epilogue (w <- w - lr * g,
+// the step of moe_sgd_step), after every read of those weights.
 static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* xv,
                     const float* scores, const int32_t* idx, const float* w, const void* doutv,
-                    const moe_grads_t& gr, const BackwardWorkspace& f, hipStream_t st) {
+                    const moe_grads_t& gr, const BackwardWorkspace& f, hipStream_t st,
+                    const float* sgd_lr = nullptr) {
   using layer::seg;
   const int T = s.T, n = s.n_experts, k = s.top_k, d = s.d, L = s.latent, m = s.inter,
             ms = s.shared_inter;
@@ -538,7 +543,7 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
     p.ldc = ldc;
     return gemm::launch(p, gemm::EPI_F32, bfmt, true, f.bm, st);
   };
-  auto kgrouped = [&](const bf16_t* A, const bf16_t* B, int M, int N, float* C) {
+  auto kgrouped = [&](const bf16_t* A, const bf16_t* B, int M, int N, void* C) {
     gemm::Params p{};
     p.M = M;
     p.N = N;
@@ -549,7 +554,8 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
     p.c_group_stride = static_cast<int64_t>(M) * N;
     p.C = C;
     p.ldc = N;
-    return gemm::launch(p, gemm::EPI_F32, gemm::B_DENSE, true, 0, st);
+    if (sgd_lr) p.sgd_lr = *sgd_lr;
+    return gemm::launch(p, sgd_lr ? gemm::EPI_SGD : gemm::EPI_F32, gemm::B_DENSE, true, 0, st);
   };
 
   // 0. the forward's token permutation, and each expert's padded K range
@@ -685,14 +691,123 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
   slot_transpose(f.dg, m, nullptr, f.pcol, S, m, f.dgT, Sp, st);
   slot_transpose(f.du, m, nullptr, f.pcol, S, m, f.duT, Sp, st);
   MOE_LAUNCH_CHECK();
-  if ((rc = kgrouped(f.dy_slotT, f.hT, L, m, gr.d_w_dn)) != MOE_OK) return rc;
-  if ((rc = kgrouped(f.dgT, f.z_slotT, m, L, gr.d_w_gate)) != MOE_OK) return rc;
-  if ((rc = kgrouped(f.duT, f.z_slotT, m, L, gr.d_w_uproj)) != MOE_OK) return rc;
+  void* g_dn = sgd_lr ? const_cast<void*>(wt.w_dn) : static_cast<void*>(gr.d_w_dn);
+  void* g_gate = sgd_lr ? const_cast<void*>(wt.w_gate) : static_cast<void*>(gr.d_w_gate);
+  void* g_up = sgd_lr ? const_cast<void*>(wt.w_uproj) : static_cast<void*>(gr.d_w_uproj);
+  if ((rc = kgrouped(f.dy_slotT, f.hT, L, m, g_dn)) != MOE_OK) return rc;
+  if ((rc = kgrouped(f.dgT, f.z_slotT, m, L, g_gate)) != MOE_OK) return rc;
+  if ((rc = kgrouped(f.duT, f.z_slotT, m, L, g_up)) != MOE_OK) return rc;
   return MOE_OK;
 }
 
 }  // namespace bwd
 }  // namespace moe
+
+namespace moe {
+namespace bwd {
+
+// w <- round(w - round(lr * g)) elementwise (sgd_value: fp32 operations
+// rounded to nearest even, no fused multiply-add), stored in the weight's
+// type; eight elements per thread and iteration when the count allows.
+template <typename W>
+__global__ __launch_bounds__(256) void sgd_k(W* __restrict__ w, const float* __restrict__ g,
+                                             int64_t count, float lr) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
+       i += stride) {
+    w[i] = from_f32<W>(sgd_value(to_f32<W>(w[i]), g[i], lr));
+  }
+}
+
+__global__ __launch_bounds__(256) void sgd_bf16x8_k(bf16_t* __restrict__ w,
+                                                    const float* __restrict__ g, int64_t groups,
+                                                    float lr) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < groups;
+       i += stride) {
+    uint4 wv = reinterpret_cast<const uint4*>(w)[i];
+    const float4 g0 = reinterpret_cast<const float4*>(g)[2 * i];
+    const float4 g1 = reinterpret_cast<const float4*>(g)[2 * i + 1];
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float lo = sgd_value(bf16_to_f32(static_cast<bf16_t>(words[q] & 0xFFFFu)), gv[2 * q], lr);
+      const float hi = sgd_value(bf16_to_f32(static_cast<bf16_t>(words[q] >> 16)), gv[2 * q + 1], lr);
+      words[q] = static_cast<uint32_t>(f32_to_bf16(lo)) |
+                 (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    }
+    reinterpret_cast<uint4*>(w)[i] = make_uint4(words[0], words[1], words[2], words[3]);
+  }
+}
+
+template <typename W>
+static void sgd(W* w, const float* g, int64_t count, float lr, hipStream_t st) {
+  if (count <= 0) return;
+  if constexpr (std::is_same<W, bf16_t>::value) {
+    if (count % 8 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0 &&
+        reinterpret_cast<uintptr_t>(g) % 32 == 0) {
+      hipLaunchKernelGGL(sgd_bf16x8_k, dim3(grid_of(count / 8)), dim3(256), 0, st, w, g, count / 8,
+                         lr);
+      return;
+    }
+  }
+  hipLaunchKernelGGL(sgd_k<W>, dim3(grid_of(count)), dim3(256), 0, st, w, g, count, lr);
+}
+
+}  // namespace bwd
+}  // namespace moe
+
+namespace moe {
+namespace bwd {
+
+// Weights and gradients present as the step needs them (experts: whether the
+// routed experts' gradients are read).
+static bool sgd_args_ok(const moe_weights_t& w, const moe_grads_t& g, bool experts) {
+  if (!w.w_router || !w.w_down || !w.w_up || !w.w_gate || !w.w_uproj || !w.w_dn || !w.rms_gamma ||
+      !w.ws_gate || !w.ws_up || !w.ws_down)
+    return false;
+  if (!g.d_w_router || !g.d_w_down || !g.d_w_up || !g.d_rms_gamma || !g.d_ws_gate || !g.d_ws_up ||
+      !g.d_ws_down)
+    return false;
+  if (experts && (!g.d_w_gate || !g.d_w_uproj || !g.d_w_dn)) return false;
+  return (w.router_logit_offset == nullptr) == (g.d_router_logit_offset == nullptr);
+}
+
+// The step on every weight (experts: the routed experts' weights too).
+static int apply_sgd(const moe_shape_t& s, const moe_weights_t& w, const moe_grads_t& g, float lr,
+                     bool experts, hipStream_t hs) {
+  const int64_t n = s.n_experts, d = s.d, L = s.latent, m = s.inter, ms = s.shared_inter;
+  auto f32 = [](const float* p) { return const_cast<float*>(p); };
+  auto b16 = [](const void* p) { return static_cast<bf16_t*>(const_cast<void*>(p)); };
+  sgd(f32(w.w_router), g.d_w_router, n * d, lr, hs);
+  if (w.router_logit_offset) sgd(f32(w.router_logit_offset), g.d_router_logit_offset, n, lr, hs);
+  sgd(b16(w.w_down), g.d_w_down, L * d, lr, hs);
+  sgd(b16(w.w_up), g.d_w_up, d * L, lr, hs);
+  if (experts) {
+    sgd(b16(w.w_gate), g.d_w_gate, n * m * L, lr, hs);
+    sgd(b16(w.w_uproj), g.d_w_uproj, n * m * L, lr, hs);
+    sgd(b16(w.w_dn), g.d_w_dn, n * L * m, lr, hs);
+  }
+  sgd(f32(w.rms_gamma), g.d_rms_gamma, L, lr, hs);
+  sgd(b16(w.ws_gate), g.d_ws_gate, ms * d, lr, hs);
+  sgd(b16(w.ws_up), g.d_ws_up, ms * d, lr, hs);
+  sgd(b16(w.ws_down), g.d_ws_down, d * ms, lr, hs);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace bwd
+}  // namespace moe
+
+extern "C" int moe_sgd_step(const moe_shape_t* shape, const moe_weights_t* weights,
+                            const moe_grads_t* grads, float lr, void* stream) {
+  int st = moe::bwd::validate(shape);
+  if (st != MOE_OK) return st;
+  if (!weights || !grads || !std::isfinite(lr)) return MOE_EINVAL;
+  if (!moe::bwd::sgd_args_ok(*weights, *grads, true)) return MOE_EINVAL;
+  return moe::bwd::apply_sgd(*shape, *weights, *grads, lr, true, static_cast<hipStream_t>(stream));
+}
 
 extern "C" size_t moe_backward_workspace_bytes(const moe_shape_t* shape) {
   if (moe::bwd::validate(shape) != MOE_OK) return 0;
@@ -736,4 +851,30 @@ extern "C" int moe_latent_backward(const moe_shape_t* shape, const moe_weights_t
     return MOE_OK;
   }
   return moe::bwd::backward(*shape, w, x, scores, topk_idx, topk_w, dout, g, f, s);
+}
+
+extern "C" int moe_latent_backward_sgd(const moe_shape_t* shape, const moe_weights_t* weights,
+                                       const void* x, const float* scores,
+                                       const int32_t* topk_idx, const float* topk_w,
+                                       const void* dout, const moe_grads_t* grads, float lr,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = moe::bwd::validate(shape);
+  if (st != MOE_OK) return st;
+  if (!weights || !grads || !workspace || !std::isfinite(lr)) return MOE_EINVAL;
+  const moe_weights_t& w = *weights;
+  const moe_grads_t& g = *grads;
+  if (!moe::bwd::sgd_args_ok(w, g, false)) return MOE_EINVAL;
+  if (shape->T > 0 && (!x || !scores || !topk_idx || !topk_w || !dout || !g.dx)) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MOE_EINVAL;
+  moe::bwd::BackwardWorkspace f;
+  const size_t need = moe::bwd::backward_layout(*shape, &f, workspace);
+  if (workspace_bytes < need) return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (shape->T == 0) return MOE_OK;  // no tokens: zero gradients, nothing moves
+  // the experts' gradient pointers are not used: their updates happen in place
+  moe_grads_t gx = g;
+  gx.d_w_gate = gx.d_w_uproj = gx.d_w_dn = nullptr;
+  st = moe::bwd::backward(*shape, w, x, scores, topk_idx, topk_w, dout, gx, f, s, &lr);
+  if (st != MOE_OK) return st;
+  return moe::bwd::apply_sgd(*shape, w, gx, lr, false, s);
 }

@@ -52,6 +52,15 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// One gradient-descent step on one value: w - lr * g as two fp32 operations,
+// each rounded to nearest even (no fused multiply-add), so that every kernel
+// that applies the step produces the same bits.
+__device__ __forceinline__ float sgd_value(float w, float g, float lr) {
+#pragma clang fp contract(off)
+  const float t = lr * g;
+  return w - t;
+}
+
 // tanh(x) = 1 - 2 / (e^(2x) + 1) with the hardware exponential: the limits
 // are exact (e^(2x) overflowing gives 1, underflowing gives -1), the result
 // stays in [-1, 1], and the absolute error near 0 is a few ulp of 1 -- far

@@ -760,6 +760,66 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
 
   // ---- epilogue straight from the accumulators ----
   const int64_t cgrp = p.kgroups > 0 ? tile.expert * p.c_group_stride : 0;
+  if constexpr (EPI == EPI_SGD) {
+    // The fp32 tile passes through the ring's two stages (128 rows x BN
+    // floats) in two halves, so that every lane updates eight consecutive
+    // weights with one 16-byte load and one 16-byte store.
+    static_assert(WM == 2 && WTM == 128 && NST == 2 && BN == 256 &&
+                      SW * sizeof(bf16_t) == 64 * BN * sizeof(float),
+                  "the staged update needs 256 x 256 tiles on two 64-element stages");
+    constexpr int CPW = BN / 8;  // 8-column chunks per row
+    constexpr int PER = 128 * CPW / (64 * NW);
+    float* const hb0 = reinterpret_cast<float*>(stg[0]);
+    float* const hb1 = reinterpret_cast<float*>(stg[1]);
+    lds_barrier();  // every wave is done with the ring
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int lr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            float* dst = ((lr >> 6) ? hb1 : hb0) + (lr & 63) * BN + wn * WTN + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) dst[j * 32] = acc[i][j][r];
+          }
+      }
+      lds_barrier();
+      uint4 wv[PER];
+      bf16_t* wp[PER];
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int c = tid + q * 64 * NW, lr = c / CPW, col = tile.n0 + (c % CPW) * 8;
+        const bool ok = h * 128 + lr < tile.rows && col < p.N;
+        wp[q] = ok ? static_cast<bf16_t*>(p.C) + cgrp + (tile.row0 + h * 128 + lr) * p.ldc + col
+                   : nullptr;
+        if (ok) wv[q] = *reinterpret_cast<const uint4*>(wp[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        if (!wp[q]) continue;
+        const int c = tid + q * 64 * NW, lr = c / CPW;
+        const float* src = ((lr >> 6) ? hb1 : hb0) + (lr & 63) * BN + (c % CPW) * 8;
+        const float4 g0 = *reinterpret_cast<const float4*>(src);
+        const float4 g1 = *reinterpret_cast<const float4*>(src + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        uint32_t words[4] = {wv[q].x, wv[q].y, wv[q].z, wv[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = sgd_value(bf16_to_f32(static_cast<bf16_t>(words[e] & 0xFFFFu)),
+                                     gv[2 * e], p.sgd_lr);
+          const float hi = sgd_value(bf16_to_f32(static_cast<bf16_t>(words[e] >> 16)),
+                                     gv[2 * e + 1], p.sgd_lr);
+          words[e] = static_cast<uint32_t>(f32_to_bf16(lo)) |
+                     (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+        }
+        *reinterpret_cast<uint4*>(wp[q]) = make_uint4(words[0], words[1], words[2], words[3]);
+      }
+      lds_barrier();
+    }
+    return;
+  }
   if (kn > 1) {  // fp32 partials, columns in B-row order of the tile
     const int64_t nv = static_cast<int64_t>(ntn) * BN;
     const int64_t cb = static_cast<int64_t>(tile.n0 / BN_OUT) * BN + wn * WTN + (lane & 31);
@@ -1523,11 +1583,16 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
   if (p.kgroups > 0) {
     // K-grouped weight gradients: fp32 outputs, one segment, no gather or
     // split; 256 x 256 tiles on 8 waves
-    if (bfmt != B_DENSE || epi != EPI_F32 || p.nseg != 1 || p.tiles || p.a_rows || !p.kofs ||
-        p.C2)
+    if (bfmt != B_DENSE || (epi != EPI_F32 && epi != EPI_SGD) || p.nseg != 1 || p.tiles ||
+        p.a_rows || !p.kofs || p.C2)
+      return MOE_EUNSUPPORTED;
+    // the in-place update writes 8 bf16 weights per 16-byte access
+    if (epi == EPI_SGD && (p.N % 8 != 0 || p.ldc % 8 != 0 || p.c_group_stride % 8 != 0 ||
+                           reinterpret_cast<uintptr_t>(p.C) % 16 != 0))
       return MOE_EUNSUPPORTED;
     Params q = p;
     q.ksplit = 1;
+    if (epi == EPI_SGD) return run_pipe<256, 256, 2, EPI_SGD, 64, 2, false, 8>(q, stream);
     return dispatch_pipe<256, 256, 2, 64, false, 8>(q, epi, stream);
   }
   if (bfmt == B_DENSE_KN) {

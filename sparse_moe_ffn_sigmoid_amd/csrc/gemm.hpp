@@ -11,6 +11,7 @@ enum Epilogue : int {
   EPI_F32 = 1,      // C (f32)  = acc
   EPI_SIGMOID = 2,  // C (f32)  = sigmoid(acc + col_add[col])
   EPI_SITU = 3,     // C (act)  = SiTU-GLU(acc_gate, acc_up); B rows come in gate/up pairs
+  EPI_SGD = 4,      // C (bf16, in place) = C - sgd_lr * acc (K-grouped weight gradients only)
 };
 
 // B_MXFP4_A8: MXFP4 B with MXFP8 (E4M3) A codes and E8M0 A scales (W4A8);
@@ -61,6 +62,7 @@ struct Params {
   // Split-K for dense problems with few output tiles: fp32 partial sums
   // [ksplit][M][tiles_n * BN] (set by launch(), room given by partial_bytes),
   // reduced with the epilogue by a second kernel.  Null: no split.
+  float sgd_lr;              // EPI_SGD: step size
   float* partial;
   size_t partial_bytes;
   int ksplit;

@@ -14,6 +14,7 @@
 //  * the status and stage-name strings for every small integer, and the
 //    stage-timing calls with NULL, zero and negative arguments.
 #include <climits>
+#include <limits>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -223,6 +224,29 @@ static void layer_validation() {
   CHECK(bwd(&s, &g2, fake(), bneed) == MOE_EINVAL);
   moe_shape_t mx = shape(64, 512, 256, 40, 6, 192, 320, MOE_BF16, MOE_MXFP4);
   CHECK(bwd(&mx, &g, fake(), bneed) == MOE_EUNSUPPORTED);
+
+  CHECK(moe_sgd_step(nullptr, &w, &g, 0.1f, nullptr) == MOE_EINVAL);
+  CHECK(moe_sgd_step(&s, nullptr, &g, 0.1f, nullptr) == MOE_EINVAL);
+  CHECK(moe_sgd_step(&s, &w, nullptr, 0.1f, nullptr) == MOE_EINVAL);
+  CHECK(moe_sgd_step(&s, &w, &g, std::numeric_limits<float>::quiet_NaN(), nullptr) == MOE_EINVAL);
+  CHECK(moe_sgd_step(&s, &w, &g, std::numeric_limits<float>::infinity(), nullptr) == MOE_EINVAL);
+  g2 = g;
+  g2.d_router_logit_offset = nullptr;
+  CHECK(moe_sgd_step(&s, &w, &g2, 0.1f, nullptr) == MOE_EINVAL);
+  CHECK(moe_sgd_step(&mx, &w, &g, 0.1f, nullptr) == MOE_EUNSUPPORTED);
+
+  auto fused = [&](const moe_shape_t* sh, const moe_grads_t* gr, float lr, void* ws, size_t wsb) {
+    return moe_latent_backward_sgd(sh, &w, fake(), static_cast<const float*>(fake()),
+                                   static_cast<const int32_t*>(fake()),
+                                   static_cast<const float*>(fake()), fake(), gr, lr, ws, wsb,
+                                   nullptr);
+  };
+  CHECK(fused(&s, &g, std::numeric_limits<float>::quiet_NaN(), fake(), bneed) == MOE_EINVAL);
+  CHECK(fused(&s, &g, 0.1f, fake(), bneed - 1) == MOE_EWORKSPACE);
+  CHECK(fused(&s, &g, 0.1f, fake(8), bneed) == MOE_EINVAL);
+  CHECK(fused(&s, nullptr, 0.1f, fake(), bneed) == MOE_EINVAL);
+  CHECK(fused(&mx, &g, 0.1f, fake(), bneed) == MOE_EUNSUPPORTED);
+  CHECK(fused(nullptr, &g, 0.1f, fake(), bneed) == MOE_EINVAL);
 
   for (auto q : {moe_mxfp8_quantize, moe_mxfp4_quantize}) {
     uint8_t* c = static_cast<uint8_t*>(fake());

@@ -223,3 +223,46 @@ def test_forward_validation_on_host():
                                  for f in names])
     assert call(shape=mx, weights=no_scales, wsb=need_mx) == -1
     assert call(shape=_shape(moe, T=64, d=250, latent=128, n=32, k=4, m=64, shared=128)) == -2
+
+
+def test_sgd_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    sh = _shape(moe, T=64)
+    wts = moe.MoeWeights(*([1 << 20] * len(moe.MoeWeights._fields_)))
+    grads = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    call = lambda s=sh, w=wts, g=grads, lr=0.1: lib.moe_sgd_step(
+        None if s is None else ctypes.byref(s), None if w is None else ctypes.byref(w),
+        None if g is None else ctypes.byref(g), ctypes.c_float(lr), None)
+    assert call(s=None) == -1 and call(w=None) == -1 and call(g=None) == -1
+    assert call(lr=float("nan")) == -1 and call(lr=float("inf")) == -1
+    no_off = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    no_off.d_router_logit_offset = None                    # the weights have an offset
+    assert call(g=no_off) == -1
+    no_gate = moe.MoeWeights(*([1 << 20] * len(moe.MoeWeights._fields_)))
+    no_gate.w_gate = None
+    assert call(w=no_gate) == -1
+    assert call(s=_shape(moe, T=64, routed=moe.MOE_MXFP4)) == -2   # bf16 layers only
+
+
+def test_fused_backward_sgd_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    sh = _shape(moe, T=64)
+    need = lib.moe_backward_workspace_bytes(ctypes.byref(sh))
+    wts = moe.MoeWeights(*([1 << 20] * len(moe.MoeWeights._fields_)))
+    grads = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    call = lambda g=grads, lr=0.1, ws_=fake, nbytes=need, s=sh: lib.moe_latent_backward_sgd(
+        ctypes.byref(s), ctypes.byref(wts), fake, fake, fake, fake, fake, ctypes.byref(g),
+        ctypes.c_float(lr), ws_, nbytes, None)
+    assert call(lr=float("nan")) == -1
+    assert call(nbytes=need - 1) == -3
+    assert call(ws_=ctypes.c_void_p((1 << 20) + 8)) == -1
+    assert call(s=_shape(moe, T=64, routed=moe.MOE_MXFP4)) == -2
+    no_dx = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    no_dx.dx = None
+    assert call(g=no_dx) == -1
+    no_router = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    no_router.d_w_router = None
+    assert call(g=no_router) == -1

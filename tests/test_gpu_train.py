@@ -1,0 +1,137 @@
+"""A training step on the GPU: forward with Quantile Balancing on the batch,
+backward with the selection held fixed, and the SGD update.
+
+* moe_sgd_step against the oracle's sgd_step, bit for bit on every weight
+  tensor (the update is elementwise fp32 arithmetic with stated rounding);
+* five training steps of a small layer regressing a fixed random target
+  (loss 0.5 * |out - target|^2, dout = out - target rounded to bf16), the
+  bias carried from batch to batch: the loss falls at every step and follows
+  the oracle's own five steps (float64 layer and gradients, the oracle's QB
+  on its own router scores, the same update) within 3% per step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from layer_cases import announce, make_shape, to_device
+from oracle import grad as ograd
+from oracle import layer as olayer
+from oracle import qb
+
+pytestmark = pytest.mark.gpu
+
+BF16 = {"w_down", "w_up", "w_gate", "w_uproj", "w_dn", "ws_gate", "ws_up", "ws_down"}
+LR = 1e-4
+
+
+def test_sgd_step_bit_exact():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    shape = workloads.small_shape(T=64)
+    announce(f"sgd step {shape}")
+    inp = workloads.layer_inputs(shape, "cpu", seed=4, random_gamma=True)
+    _, w = to_device(inp)
+    w["router_logit_offset"] = w.pop("logit_offset")
+    gen = torch.Generator().manual_seed(9)
+    grads = {}
+    for name, (key, _) in moe.GRAD_SHAPES.items():
+        g = torch.randn(tuple(w[key].shape), generator=gen) * 0.1
+        g.view(-1)[:7] = torch.tensor([0.0, -0.0, 1e4, -1e4, 1e-30, 3.0, -3.0])
+        grads[name] = g.float().cuda()
+    before = {key: w[key].clone() for key in w}
+    lr = 0.0123
+    moe.sgd_step(make_shape(moe, shape), w, grads, lr)
+    torch.cuda.synchronize()
+    for name, (key, _) in moe.GRAD_SHAPES.items():
+        ref = ograd.sgd_step(before[key].cpu(), grads[name].cpu(), lr,
+                             "bf16" if key in BF16 else "f32")
+        got = w[key].float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), key
+        assert not torch.equal(w[key], before[key]), key
+
+
+def oracle_losses(shape, inp, target, steps):
+    cur = {k: (None if v is None else olayer.as_f64(v)) for k, v in inp.items()}
+    bias = np.zeros(shape.n)
+    losses = []
+    for _ in range(steps):
+        s = olayer.router_scores(cur["x"], cur["w_router"], cur["logit_offset"]).astype(np.float32)
+        r = qb.route_qb(s, shape.k, bias=bias)
+        bias = r["bias"]
+        fwd = ograd.layer_grads(cur, r["idx"], shape.eps, np.zeros((shape.T, shape.d)))
+        out = olayer.bf16_round(fwd["out"])
+        losses.append(0.5 * float(np.sum((out - target) ** 2)))
+        g = ograd.layer_grads(cur, r["idx"], shape.eps, olayer.bf16_round(out - target))
+        for key in ograd.GRAD_KEYS:
+            if key != "x" and cur.get(key) is not None:
+                cur[key] = ograd.sgd_step(cur[key], g[key], LR, "bf16" if key in BF16 else "f32")
+    return losses
+
+
+def test_training_steps_reduce_loss():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    shape = workloads.small_shape(T=256, n=32, k=4)
+    announce(f"training steps {shape}")
+    inp = workloads.layer_inputs(shape, "cpu", seed=11, random_gamma=True)
+    target = np.random.default_rng(5).standard_normal((shape.T, shape.d))
+    x, w = to_device(inp)
+    w["router_logit_offset"] = w.pop("logit_offset")
+    sh = make_shape(moe, shape)
+    tgt = torch.from_numpy(target).cuda()
+    bias = torch.zeros(shape.n, dtype=torch.float64, device="cuda")
+    losses = []
+    for _ in range(5):
+        fwd = moe.latent_forward(sh, w, x, bias=bias, want_scores=True)
+        bias = fwd["bias"]
+        out = fwd["out"].double()
+        losses.append(0.5 * float(((out - tgt) ** 2).sum()))
+        dout = (out - tgt).to(torch.bfloat16)
+        grads = moe.latent_backward(sh, w, x, fwd["scores"], fwd["idx"], fwd["w"], dout)
+        moe.sgd_step(sh, w, grads, LR)
+    torch.cuda.synchronize()
+    ref = oracle_losses(shape, inp, target, 5)
+    print("  GPU losses   ", ["%.1f" % v for v in losses], flush=True)
+    print("  oracle losses", ["%.1f" % v for v in ref], flush=True)
+    assert all(b < a for a, b in zip(losses, losses[1:]))
+    assert losses[-1] < 0.5 * losses[0]
+    for a, b in zip(losses, ref):
+        assert abs(a - b) <= 0.03 * b
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=200),                                   # small widths, 30 rows per expert
+    dict(T=584, n=64, k=8),                        # the 96-row expert tiles
+])
+def test_fused_backward_sgd_matches_separate_calls(kw):
+    """moe_latent_backward_sgd = moe_latent_backward, then moe_sgd_step: the
+    updated weights and the returned gradients bit for bit."""
+    import sparse_moe_ffn_sigmoid_amd as moe
+    shape = workloads.small_shape(**kw)
+    announce(f"fused backward + sgd {shape}")
+    inp = workloads.layer_inputs(shape, "cpu", seed=6, random_gamma=True)
+    x, w1 = to_device(inp)
+    w1["router_logit_offset"] = w1.pop("logit_offset")
+    w2 = {key: v.clone() for key, v in w1.items()}
+    sh = make_shape(moe, shape)
+    fwd = moe.latent_forward(sh, w1, x, want_scores=True)
+    dout = torch.randn((shape.T, shape.d), generator=torch.Generator().manual_seed(2)).to(
+        torch.bfloat16).cuda()
+    lr = 3e-3
+    g1 = moe.latent_backward(sh, w1, x, fwd["scores"], fwd["idx"], fwd["w"], dout)
+    moe.sgd_step(sh, w1, g1, lr)
+    g2 = moe.latent_backward_sgd(sh, w2, x, fwd["scores"], fwd["idx"], fwd["w"], dout, lr)
+    torch.cuda.synchronize()
+    for key in w1:
+        assert torch.equal(w1[key].view(torch.uint8) if w1[key].dtype == torch.bfloat16 else w1[key],
+                           w2[key].view(torch.uint8) if w2[key].dtype == torch.bfloat16 else w2[key]), key
+    for name, v in g2.items():
+        if v is None:
+            assert name in moe.EXPERT_GRADS
+            continue
+        a = g1[name].view(torch.uint8) if g1[name].dtype == torch.bfloat16 else g1[name]
+        b = v.view(torch.uint8) if v.dtype == torch.bfloat16 else v
+        assert torch.equal(a, b), name
+    changed = sum(int(not torch.equal(w1[k], inp_v.to(w1[k].device)))
+                  for k, inp_v in ((k2, inp[k2 if k2 != "router_logit_offset" else "logit_offset"])
+                                   for k2 in w1))
+    assert changed == len(w1)

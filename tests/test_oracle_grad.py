@@ -101,3 +101,55 @@ def test_rms_gain_gradient_closed_form():
     yr = y / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + shape.eps)
     want = np.sum((dout @ inp["w_up"]) * yr, axis=0)
     assert np.allclose(g["rms_gamma"], want, rtol=1e-10, atol=1e-12)
+
+
+def _round_rne(x, mant_bits):
+    """Exact rational x rounded to the nearest binary float with `mant_bits`
+    significant bits (ties to even); normal range only."""
+    from fractions import Fraction
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(Fraction(x))
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - mant_bits + 1)
+    q, r = divmod(a, ulp)
+    q = int(q)
+    if r * 2 > ulp or (r * 2 == ulp and q % 2 == 1):
+        q += 1
+    return sign * q * ulp
+
+
+def test_sgd_step_hand_cases():
+    # exact: 1.5 - 1 * 0.25; ties to even at the bf16 grid of [1, 2) (spacing 2^-7)
+    w = np.array([1.5, 1 + 2 ** -7, 1 + 2 ** -6])
+    g = np.array([0.25, 2 ** -8, 2 ** -8])
+    assert ograd.sgd_step(w, g, 1.0, "bf16").tolist() == [1.25, 1.0, 1.015625]
+    # fp32 weights keep 1 + 2^-8
+    assert ograd.sgd_step(w, g, 1.0, "f32").tolist() == [1.25, 1 + 2 ** -8, 1 + 3 * 2 ** -8]
+
+
+def test_sgd_step_matches_exact_rounding():
+    """Against the definition in exact rational arithmetic: the product and
+    the difference each rounded to 24 bits, then (bf16) to 8 bits.  Some
+    samples would come out differently with a single rounding of w - lr*g
+    (a fused multiply-add), so that mistake fails here."""
+    from fractions import Fraction
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal(400) * 0.05).astype(np.float32)
+    g = (rng.standard_normal(400) * 3.0).astype(np.float32)
+    lr = np.float32(0.0123)
+    fused_differs = 0
+    for dtype, bits in (("f32", 24), ("bf16", 8)):
+        wd = w if dtype == "f32" else ograd.layer.bf16_round(w.astype(np.float64)).astype(np.float32)
+        got = ograd.sgd_step(wd, g, float(lr), dtype)
+        for i in range(w.size):
+            t = _round_rne(Fraction(float(lr)) * Fraction(float(g[i])), 24)
+            r = _round_rne(Fraction(float(wd[i])) - t, 24)
+            want = _round_rne(r, bits) if bits < 24 else r
+            assert Fraction(float(got[i])) == want, (dtype, i)
+            fused = _round_rne(Fraction(float(wd[i])) - Fraction(float(lr)) * Fraction(float(g[i])), 24)
+            fused_differs += int((_round_rne(fused, bits) if bits < 24 else fused) != want)
+    assert fused_differs > 0
