@@ -28,12 +28,32 @@ pytestmark = pytest.mark.gpu
 # expert of a stacked expert gradient, one output row of a weight gradient)
 # can be a sum of very few terms with cancellation between them (a router
 # row fed by a single token), so rows get TOL_ROW = 1e-1, still far below
-# the O(1) error of a wrong row, tile or expert.  Elementwise max|diff| / rms
-# is printed but not bounded: rounding z and h to bf16 alone moves a
-# rank-one expert gradient (one token per expert) by 12% of its rms at its
-# largest entries.
+# the O(1) error of a wrong row, tile or expert.  The roundings are relative
+# to the terms, not to their sum: a router row fed by one token is that
+# token's dlogit times x, and dlogit is dw_j minus the weighted mean of the
+# token's dw, so when the two nearly cancel the row's relative error has no
+# bound while its absolute error stays at the scale of the terms, about the
+# same for every row.  A row is therefore measured against ROW_FLOOR = 25% of
+# the median row norm of its tensor when its own norm is smaller (absolute
+# error <= 2.5% of the median, about six times the 0.4% a term carries).
+# Elementwise max|diff| / rms is printed but not bounded: rounding z and h to
+# bf16 alone moves a rank-one expert gradient (one token per expert) by 12%
+# of its rms at its largest entries.
 TOL_FRO = 1e-2
 TOL_ROW = 1e-1
+ROW_FLOOR = 0.25
+
+
+def worst_row(got, ref):
+    """max over rows of |got - ref| / max(|ref|, ROW_FLOOR * median row norm);
+    rows of an all-zero reference (experts no token chose) are skipped."""
+    gg, rr = got.reshape(ref.shape[0], -1), ref.reshape(ref.shape[0], -1)
+    nr = np.linalg.norm(rr, axis=1)
+    ok = nr > 0
+    if not ok.any():
+        return 0.0
+    floor = ROW_FLOOR * float(np.median(nr[ok]))
+    return float((np.linalg.norm(gg - rr, axis=1)[ok] / np.maximum(nr[ok], floor)).max())
 
 KEYS = {"dx": "x", "d_w_router": "w_router", "d_router_logit_offset": "logit_offset",
         "d_w_down": "w_down", "d_w_up": "w_up", "d_w_gate": "w_gate", "d_w_uproj": "w_uproj",
@@ -67,12 +87,7 @@ def check_backward(shape, seed, name):
         gv = g.float().cpu().numpy()
         r = ref[key]
         fro = float(np.linalg.norm(gv - r) / np.linalg.norm(r))
-        row = fro
-        if r.ndim >= 2:
-            gg, rr = gv.reshape(r.shape[0], -1), r.reshape(r.shape[0], -1)
-            nr = np.linalg.norm(rr, axis=1)
-            ok = nr > 0
-            row = float((np.linalg.norm(gg - rr, axis=1)[ok] / nr[ok]).max())
+        row = worst_row(gv, r) if r.ndim >= 2 else fro
         worst = max(worst, fro)
         print(f"  {gname:<24} rel. Frobenius {fro:.2e}, worst row {row:.2e}, "
               f"max|diff|/rms {rel_err(gv, r):.2e}", flush=True)
