@@ -153,13 +153,15 @@ def time_backward(moe, sh, w, x, bias0, ws, shape, args):
                     "recomputed inside), selection held fixed"}
 
 
-def time_train(moe, sh, w, x, bias0, ws, shape, args, fused=True):
+def time_train(moe, sh, w, x, bias0, ws, shape, args, mode="saved"):
     """One training step: forward with QB on the batch (the bias carried from
     step to step), backward with a seeded N(0,1) output gradient, and the SGD
-    update of every weight in place (lr 1e-6): fused (moe_latent_backward_sgd,
-    the experts' gradients applied where they are formed) or as two calls
-    (moe_latent_backward, then moe_sgd_step).  Timed like the forward; the
-    weights change from step to step as in training."""
+    update of every weight in place (lr 1e-6).  mode "saved": the training
+    forward keeps its activations and the backward reads them, the update
+    fused into the experts' weight-gradient GEMMs; "fused": the backward
+    recomputes the activations, update fused; "separate": moe_latent_backward,
+    then moe_sgd_step.  Timed like the forward; the weights change from step
+    to step as in training."""
     import torch
     g = torch.Generator(device=x.device)
     g.manual_seed(4321)
@@ -167,12 +169,17 @@ def time_train(moe, sh, w, x, bias0, ws, shape, args, fused=True):
     bws = torch.empty(moe.lib().moe_backward_workspace_bytes(ctypes_ref(sh)), dtype=torch.uint8,
                       device=x.device)
     bias = bias0.clone()
+    saved = (torch.empty(moe.saved_activations_bytes(sh), dtype=torch.uint8, device=x.device)
+             if mode == "saved" else None)
 
     def step():
         nonlocal bias
-        fwd = moe.latent_forward(sh, w, x, bias=bias, workspace=ws, want_scores=True)
+        fwd = moe.latent_forward(sh, w, x, bias=bias, workspace=ws, want_scores=True, saved=saved)
         bias = fwd["bias"]
-        if fused:
+        if mode == "saved":
+            moe.latent_backward_train(sh, w, x, fwd["scores"], fwd["idx"], fwd["w"], dout, saved,
+                                      lr=1e-6, workspace=bws)
+        elif mode == "fused":
             moe.latent_backward_sgd(sh, w, x, fwd["scores"], fwd["idx"], fwd["w"], dout, 1e-6,
                                     workspace=bws)
         else:
@@ -189,12 +196,14 @@ def time_train(moe, sh, w, x, bias0, ws, shape, args, fused=True):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    del bws
+    del bws, saved
     torch.cuda.empty_cache()
     return {"ms_per_step": ms, "tokens_per_s": shape.T / (ms / 1e3),
-            "what": "forward (QB on the batch) + backward + SGD update of every weight" +
-                    (" (update fused into the expert weight-gradient GEMMs)" if fused else
-                     " (backward and update as two calls)")}
+            "what": "forward (QB on the batch) + backward + SGD update of every weight" + {
+                "saved": " (activations kept by the forward; update fused into the expert "
+                         "weight-gradient GEMMs)",
+                "fused": " (activations recomputed; update fused)",
+                "separate": " (activations recomputed; backward and update as two calls)"}[mode]}
 
 
 def ctypes_ref(obj):
@@ -511,7 +520,9 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(inp, shape, args.cpu_sample_tokens)
     if args.train:  # last: it updates the weights in place
         rec["train"] = time_train(moe, sh, w, x, bias0, ws, shape, args)
-        rec["train_separate"] = time_train(moe, sh, w, x, bias0, ws, shape, args, fused=False)
+        rec["train_recompute"] = time_train(moe, sh, w, x, bias0, ws, shape, args, mode="fused")
+        rec["train_separate"] = time_train(moe, sh, w, x, bias0, ws, shape, args,
+                                           mode="separate")
     print(json.dumps(rec), flush=True)
 
 

@@ -350,6 +350,44 @@ int moe_latent_backward_sgd(const moe_shape_t* shape, const moe_weights_t* weigh
                             const void* dout, const moe_grads_t* grads, float lr, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/*
+ * Training forward and backward: the forward keeps the activations the
+ * backward would otherwise recompute (bf16 layers).
+ *
+ * moe_saved_activations_bytes -- size of the buffer they need (at least 256
+ * bytes); 0 on a shape the training calls do not take.  The buffer holds z [T][latent] bf16, the
+ * routed experts' gate and up pre-activations [T*k][inter] fp32 and h bf16,
+ * their outputs [T*k][latent] fp32, and the shared expert's pre-activations
+ * [T][shared_inter] fp32 and hs bf16, slots in the forward's permutation
+ * order.  Its content is private to these calls.
+ *
+ * moe_latent_forward_train -- moe_latent_forward (same arguments, same
+ * results bit for bit) that also fills `saved` (>= the size above, 256-byte
+ * aligned, caller-owned).
+ *
+ * moe_latent_backward_train -- moe_latent_backward (apply_sgd = 0) or
+ * moe_latent_backward_sgd (apply_sgd = 1, step size lr) for that forward
+ * call: x, scores, topk_idx, topk_w as it returned them, `saved` as it
+ * filled it (read only).  Workspace as for moe_latent_backward.  The
+ * results match those of the recomputing calls to within the rounding of
+ * the activations: the forward may split a small product's K range where
+ * the recompute does not, which can move a stored bf16 activation by one
+ * unit.
+ */
+size_t moe_saved_activations_bytes(const moe_shape_t* shape);
+
+int moe_latent_forward_train(const moe_shape_t* shape, const moe_weights_t* weights, const void* x,
+                             void* out, double* bias, const float* scores_in, float* scores_out,
+                             int32_t* topk_idx, float* topk_w, int32_t* loads, int32_t* qb_info,
+                             void* saved, size_t saved_bytes, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+int moe_latent_backward_train(const moe_shape_t* shape, const moe_weights_t* weights, const void* x,
+                              const float* scores, const int32_t* topk_idx, const float* topk_w,
+                              const void* dout, const void* saved, size_t saved_bytes,
+                              const moe_grads_t* grads, int apply_sgd, float lr, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Static description of a moe_status value; never NULL. */
 const char* moe_status_str(int status);
 

@@ -28,7 +28,8 @@ EXPORTED = ("moe_route_workspace_bytes", "moe_route_qb", "moe_route_sign",
             "moe_latent_forward", "moe_status_str", "moe_stage_timing", "moe_stage_times",
             "moe_stage_name", "moe_mxfp8_quantize", "moe_mxfp4_quantize",
             "moe_route_qb_noalloc", "moe_backward_workspace_bytes", "moe_latent_backward",
-            "moe_sgd_step", "moe_latent_backward_sgd")
+            "moe_sgd_step", "moe_latent_backward_sgd", "moe_saved_activations_bytes",
+            "moe_latent_forward_train", "moe_latent_backward_train")
 
 
 class MoeShape(ctypes.Structure):
@@ -89,6 +90,17 @@ _lib.moe_latent_backward_sgd.argtypes = [ctypes.POINTER(MoeShape), ctypes.POINTE
                                          _vp, _vp, _vp, _vp, ctypes.POINTER(MoeGrads),
                                          ctypes.c_float, _vp, _sz, _vp]
 _lib.moe_latent_backward_sgd.restype = ctypes.c_int
+_lib.moe_saved_activations_bytes.argtypes = [ctypes.POINTER(MoeShape)]
+_lib.moe_saved_activations_bytes.restype = _sz
+_lib.moe_latent_forward_train.argtypes = [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights),
+                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                          _vp, _sz, _vp]
+_lib.moe_latent_forward_train.restype = ctypes.c_int
+_lib.moe_latent_backward_train.argtypes = [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights),
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                           ctypes.POINTER(MoeGrads), ctypes.c_int, ctypes.c_float,
+                                           _vp, _sz, _vp]
+_lib.moe_latent_backward_train.restype = ctypes.c_int
 _lib.moe_mxfp4_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
 _lib.moe_mxfp4_quantize.restype = ctypes.c_int
 _lib.moe_mxfp8_quantize.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
@@ -319,6 +331,46 @@ def latent_backward_sgd(shape: MoeShape, weights: dict, x: torch.Tensor, scores:
     return out
 
 
+def latent_backward_train(shape: MoeShape, weights: dict, x: torch.Tensor, scores: torch.Tensor,
+                          idx: torch.Tensor, w: torch.Tensor, dout: torch.Tensor,
+                          saved: torch.Tensor, lr=None, workspace=None):
+    """The backward of a training forward (latent_forward with `saved`),
+    reading the activations it kept.  lr None: every gradient, as
+    latent_backward; else the SGD step is applied as in latent_backward_sgd
+    (the experts' gradients in place, not returned)."""
+    dev = x.device
+    T, d, l, n, k = shape.T, shape.d, shape.latent, shape.n_experts, shape.top_k
+    m, ms = shape.inter, shape.shared_inter
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(dout, "dout", torch.bfloat16, (T, d), dev)
+    _check(scores, "scores", torch.float32, (T, n), dev)
+    _check(idx, "idx", torch.int32, (T, k), dev)
+    _check(w, "w", torch.float32, (T, k), dev)
+    _check(saved, "saved", torch.uint8, (saved.numel(),), dev)
+    wts = MoeWeights(*[None if weights.get(f) is None else weights[f].data_ptr()
+                       for f, _ in MoeWeights._fields_])
+    out = {"dx": torch.empty((T, d), dtype=torch.bfloat16, device=dev)}
+    for name, (key, fn) in GRAD_SHAPES.items():
+        if weights.get(key) is None or (lr is not None and name in EXPERT_GRADS):
+            out[name] = None
+        else:
+            out[name] = torch.empty(fn(T, d, l, n, k, m, ms), dtype=torch.float32, device=dev)
+    grads = MoeGrads(*[None if out[f] is None else out[f].data_ptr() for f, _ in MoeGrads._fields_])
+    need = _lib.moe_backward_workspace_bytes(ctypes.byref(shape))
+    if need == 0:
+        raise MoeError(-2, "moe_backward_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _lib.moe_latent_backward_train(ctypes.byref(shape), ctypes.byref(wts), _ptr(x),
+                                        _ptr(scores), _ptr(idx), _ptr(w), _ptr(dout),
+                                        _ptr(saved), saved.numel(), ctypes.byref(grads),
+                                        0 if lr is None else 1,
+                                        ctypes.c_float(0.0 if lr is None else lr), _ptr(ws),
+                                        ws.numel(), _stream())
+    if st != 0:
+        raise MoeError(st, "moe_latent_backward_train")
+    return out
+
+
 def sgd_step(shape: MoeShape, weights: dict, grads: dict, lr: float):
     """One gradient-descent step in place on the weight tensors of `weights`
     (w <- w - lr * g, fp32 operations, stored in each weight's type) from
@@ -352,9 +404,17 @@ def forward_workspace_bytes(shape: MoeShape) -> int:
 _DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 
+def saved_activations_bytes(shape: MoeShape) -> int:
+    return int(_lib.moe_saved_activations_bytes(ctypes.byref(shape)))
+
+
 def latent_forward(shape: MoeShape, weights: dict, x: torch.Tensor, bias=None,
-                   scores_in=None, want_scores=False, workspace=None):
+                   scores_in=None, want_scores=False, workspace=None, saved=None):
     """One forward pass of the layer.
+
+    ``saved``: a device uint8 buffer of saved_activations_bytes(shape) bytes;
+    when given, the training forward also keeps there what
+    latent_backward_train needs (bf16 layers).
 
     ``weights`` holds device tensors keyed as in ``moe_weights_t`` (MXFP4
     routed weights as uint8 codes plus ``s_gate``/``s_uproj``/``s_dn``).
@@ -400,11 +460,21 @@ def latent_forward(shape: MoeShape, weights: dict, x: torch.Tensor, bias=None,
     if need == 0:
         raise MoeError(-1, "moe_forward_workspace_bytes")
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
-    st = _lib.moe_latent_forward(ctypes.byref(shape), ctypes.byref(wts), _ptr(x), _ptr(out),
-                                 _ptr(b), _ptr(scores_in), _ptr(scores), _ptr(idx), _ptr(w),
-                                 _ptr(loads), _ptr(info), _ptr(ws), ws.numel(), _stream())
-    if st != 0:
-        raise MoeError(st, "moe_latent_forward")
+    if saved is not None:
+        _check(saved, "saved", torch.uint8, (saved.numel(),), dev)
+        st = _lib.moe_latent_forward_train(ctypes.byref(shape), ctypes.byref(wts), _ptr(x),
+                                           _ptr(out), _ptr(b), _ptr(scores_in), _ptr(scores),
+                                           _ptr(idx), _ptr(w), _ptr(loads), _ptr(info),
+                                           _ptr(saved), saved.numel(), _ptr(ws), ws.numel(),
+                                           _stream())
+        if st != 0:
+            raise MoeError(st, "moe_latent_forward_train")
+    else:
+        st = _lib.moe_latent_forward(ctypes.byref(shape), ctypes.byref(wts), _ptr(x), _ptr(out),
+                                     _ptr(b), _ptr(scores_in), _ptr(scores), _ptr(idx), _ptr(w),
+                                     _ptr(loads), _ptr(info), _ptr(ws), ws.numel(), _stream())
+        if st != 0:
+            raise MoeError(st, "moe_latent_forward")
     res = dict(out=out, idx=idx, w=w, loads=loads, bias=b, info=info)
     if want_scores:
         res["scores"] = scores

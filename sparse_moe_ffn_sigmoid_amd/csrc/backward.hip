@@ -502,10 +502,23 @@ static void zero(void* p, int64_t bytes, hipStream_t st) {
 // sgd_lr: when not null, the routed experts' weight gradients are not
 // stored: each is applied to its weight in the GEMM epilogue (w <- w - lr * g,
 // the step of moe_sgd_step), after every read of those weights.
+// saved: the activations a training forward kept (else they are recomputed).
 static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* xv,
                     const float* scores, const int32_t* idx, const float* w, const void* doutv,
-                    const moe_grads_t& gr, const BackwardWorkspace& f, hipStream_t st,
-                    const float* sgd_lr = nullptr) {
+                    const moe_grads_t& gr, const BackwardWorkspace& fws, hipStream_t st,
+                    const float* sgd_lr = nullptr,
+                    const layer::SavedActivations* saved = nullptr) {
+  BackwardWorkspace f = fws;
+  if (saved) {  // read-only from here on
+    f.z = saved->z;
+    f.g = saved->g;
+    f.u = saved->u;
+    f.h = saved->h;
+    f.yp = saved->yp;
+    f.gs = saved->gs;
+    f.us = saved->us;
+    f.hs = saved->hs;
+  }
   using layer::seg;
   const int T = s.T, n = s.n_experts, k = s.top_k, d = s.d, L = s.latent, m = s.inter,
             ms = s.shared_inter;
@@ -589,7 +602,8 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
   const int64_t es = static_cast<int64_t>(m) * L;
   MOE_LAUNCH_CHECK();
 
-  // 2. forward activations
+  // 2. forward activations (unless the forward kept them)
+  if (!saved) {
   if ((rc = dense(x, d, W_down, d, d, T, L, f.z, L, gemm::EPI_BF16)) != MOE_OK) return rc;
   if ((rc = grouped(f.z, L, f.perm, W_g, L, es, L, m, f.g, m)) != MOE_OK) return rc;
   if ((rc = grouped(f.z, L, f.perm, W_u, L, es, L, m, f.u, m)) != MOE_OK) return rc;
@@ -601,6 +615,7 @@ static int backward(const moe_shape_t& s, const moe_weights_t& wt, const void* x
   hipLaunchKernelGGL(situ_fwd_k, dim3(grid_of(static_cast<int64_t>(T) * ms)), dim3(256), 0, st,
                      f.gs, f.us, static_cast<int64_t>(T) * ms, f.hs);
   MOE_LAUNCH_CHECK();
+  }
 
   // 3. up-projection and RMSNorm / combine, router
   if ((rc = dense(dout, d, f.w_upT, d, d, T, L, f.dyhat, L, gemm::EPI_F32)) != MOE_OK) return rc;
@@ -774,6 +789,20 @@ static bool sgd_args_ok(const moe_weights_t& w, const moe_grads_t& g, bool exper
   return (w.router_logit_offset == nullptr) == (g.d_router_logit_offset == nullptr);
 }
 
+// Every gradient of a batch without tokens: zero.
+static int zero_grads(const moe_shape_t& s, const moe_grads_t& g, hipStream_t st) {
+  const int64_t n = s.n_experts, d = s.d, L = s.latent, m = s.inter, ms = s.shared_inter;
+  float* outs[] = {g.d_w_router, g.d_router_logit_offset, g.d_w_down, g.d_w_up, g.d_w_gate,
+                   g.d_w_uproj, g.d_w_dn, g.d_rms_gamma, g.d_ws_gate, g.d_ws_up, g.d_ws_down};
+  const int64_t cnt[] = {n * d, n, L * d, d * L, n * m * L, n * m * L, n * L * m, L, ms * d, ms * d,
+                         d * ms};
+  for (int i = 0; i < 11; ++i)
+    if (outs[i])
+      hipLaunchKernelGGL(fill_f32, dim3(grid_of(cnt[i])), dim3(256), 0, st, outs[i], cnt[i]);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
 // The step on every weight (experts: the routed experts' weights too).
 static int apply_sgd(const moe_shape_t& s, const moe_weights_t& w, const moe_grads_t& g, float lr,
                      bool experts, hipStream_t hs) {
@@ -836,21 +865,43 @@ extern "C" int moe_latent_backward(const moe_shape_t* shape, const moe_weights_t
   const size_t need = moe::bwd::backward_layout(*shape, &f, workspace);
   if (workspace_bytes < need) return MOE_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (shape->T == 0) {  // no tokens: every gradient is zero
-    const int64_t n = shape->n_experts, d = shape->d, L = shape->latent, m = shape->inter,
-                  ms = shape->shared_inter;
-    float* outs[] = {g.d_w_router, g.d_router_logit_offset, g.d_w_down, g.d_w_up, g.d_w_gate,
-                     g.d_w_uproj, g.d_w_dn, g.d_rms_gamma, g.d_ws_gate, g.d_ws_up, g.d_ws_down};
-    const int64_t cnt[] = {n * d, n, L * d, d * L, n * m * L, n * m * L, n * L * m, L, ms * d, ms * d,
-                           d * ms};
-    for (int i = 0; i < 11; ++i)
-      if (outs[i])
-        hipLaunchKernelGGL(moe::bwd::fill_f32, dim3(moe::bwd::grid_of(cnt[i])), dim3(256), 0, s,
-                           outs[i], cnt[i]);
-    MOE_LAUNCH_CHECK();
-    return MOE_OK;
-  }
+  if (shape->T == 0) return moe::bwd::zero_grads(*shape, g, s);  // no tokens: zero gradients
   return moe::bwd::backward(*shape, w, x, scores, topk_idx, topk_w, dout, g, f, s);
+}
+
+extern "C" int moe_latent_backward_train(const moe_shape_t* shape, const moe_weights_t* weights,
+                                         const void* x, const float* scores,
+                                         const int32_t* topk_idx, const float* topk_w,
+                                         const void* dout, const void* saved, size_t saved_bytes,
+                                         const moe_grads_t* grads, int apply_sgd, float lr,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  int st = moe::bwd::validate(shape);
+  if (st != MOE_OK) return st;
+  if (!weights || !grads || !workspace || !saved) return MOE_EINVAL;
+  if (apply_sgd != 0 && apply_sgd != 1) return MOE_EINVAL;
+  if (apply_sgd && !std::isfinite(lr)) return MOE_EINVAL;
+  const moe_weights_t& w = *weights;
+  const moe_grads_t& g = *grads;
+  if (!moe::bwd::sgd_args_ok(w, g, !apply_sgd)) return MOE_EINVAL;
+  if (shape->T > 0 && (!x || !scores || !topk_idx || !topk_w || !dout || !g.dx)) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+      reinterpret_cast<uintptr_t>(saved) % 256 != 0)
+    return MOE_EINVAL;
+  moe::bwd::BackwardWorkspace f;
+  const size_t need = moe::bwd::backward_layout(*shape, &f, workspace);
+  if (workspace_bytes < need) return MOE_EWORKSPACE;
+  moe::layer::SavedActivations sv;
+  if (saved_bytes < moe::layer::saved_layout(*shape, &sv, const_cast<void*>(saved)))
+    return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (shape->T == 0) return apply_sgd ? MOE_OK : moe::bwd::zero_grads(*shape, g, s);
+  if (!apply_sgd) return moe::bwd::backward(*shape, w, x, scores, topk_idx, topk_w, dout, g, f, s,
+                                            nullptr, &sv);
+  moe_grads_t gx = g;  // the experts' gradients are applied where they are formed
+  gx.d_w_gate = gx.d_w_uproj = gx.d_w_dn = nullptr;
+  st = moe::bwd::backward(*shape, w, x, scores, topk_idx, topk_w, dout, gx, f, s, &lr, &sv);
+  if (st != MOE_OK) return st;
+  return moe::bwd::apply_sgd(*shape, w, gx, lr, false, s);
 }
 
 extern "C" int moe_latent_backward_sgd(const moe_shape_t* shape, const moe_weights_t* weights,

@@ -847,8 +847,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
         for (int j = 0; j < FN; j += 2) {
           const int grp = wn * FN + j;  // even: gate group, odd: its up group
           const int col = tile.n0 + (grp >> 1) * 32 + (lane & 31);
-          if (col < p.N)
+          if (col < p.N) {
             store_bf16(p, orow * p.ldc + col, situ_glu(acc[i][j][r], acc[i][j + 1][r]));
+            if (p.save_g) {
+              p.save_g[orow * p.ldc + col] = acc[i][j][r];
+              p.save_u[orow * p.ldc + col] = acc[i][j + 1][r];
+            }
+          }
         }
       } else {
 #pragma unroll
@@ -1308,7 +1313,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_f32(Params p) {
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ part, int kn, int M,
                                                       int N, int64_t nv, int bn, void* C, void* C2,
-                                                      int64_t ldc, const float* col_add) {
+                                                      int64_t ldc, const float* col_add,
+                                                      float* save_g, float* save_u) {
   const int64_t total = static_cast<int64_t>(M) * N;
   const int64_t plane = static_cast<int64_t>(M) * nv;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
@@ -1325,6 +1331,10 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
         u += pr[q * plane + vg + 32];
       }
       store_bf16(C, C2, row * ldc + c, situ_glu(g, u));
+      if (save_g) {
+        save_g[row * ldc + c] = g;
+        save_u[row * ldc + c] = u;
+      }
     } else {
       float x = 0.f;
       for (int q = 0; q < kn; ++q) x += pr[q * plane + c];
@@ -1403,7 +1413,8 @@ static int run_reduce(const Params& p, const DensePlan& d, hipStream_t stream) {
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)),
                      dim3(256), 0, stream, p.partial, d.ks, p.M, p.N,
-                     static_cast<int64_t>(d.ntn) * d.bn, d.bn, p.C, p.C2, p.ldc, p.col_add);
+                     static_cast<int64_t>(d.ntn) * d.bn, d.bn, p.C, p.C2, p.ldc, p.col_add,
+                     p.save_g, p.save_u);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -1568,6 +1579,10 @@ static int dispatch_epi(const Params& p, int epi, hipStream_t s) {
 int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipStream_t stream) {
   // low parts are written by the dense bf16 kernels and their split-K reduction
   if (p.C2 && !(act_bf16 && bfmt == B_DENSE && !p.tiles && (epi == EPI_BF16 || epi == EPI_SITU)))
+    return MOE_EUNSUPPORTED;
+  // pre-activations are stored by the pipelined bf16 kernels and their split-K reduction
+  if ((p.save_g != nullptr) != (p.save_u != nullptr) ||
+      (p.save_g && !(act_bf16 && bfmt == B_DENSE && epi == EPI_SITU)))
     return MOE_EUNSUPPORTED;
   if (!act_bf16) {
     if (bfmt != B_DENSE) return MOE_EUNSUPPORTED;

@@ -59,6 +59,10 @@ struct Params {
                              // bf16(v - bf16(v)) of each value, or null
   int64_t ldc;
   const float* col_add;      // EPI_SIGMOID: per-column logit offset or null
+  // EPI_SITU with bf16 dense B: also store the pre-activations (fp32, the
+  // output's row stride ldc), gate to save_g and up to save_u, or null
+  float* save_g;
+  float* save_u;
   // Split-K for dense problems with few output tiles: fp32 partial sums
   // [ksplit][M][tiles_n * BN] (set by launch(), room given by partial_bytes),
   // reduced with the epilogue by a second kernel.  Null: no split.

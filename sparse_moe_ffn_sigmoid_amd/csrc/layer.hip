@@ -342,7 +342,26 @@ struct ForwardWorkspace {
   int max_mtiles;
   float* partial;     // split-K partial sums of the dense GEMMs (used one at a time)
   size_t partial_bytes;
+  // training forward: pre-activations of the routed and shared SiTU-GLU
+  // (fp32), stored beside h and hs; null otherwise
+  float *save_g, *save_u, *save_gs, *save_us;
 };
+
+size_t saved_layout(const moe_shape_t& s, SavedActivations* out, void* base) {
+  Carver cv(base);
+  SavedActivations a{};
+  const int64_t T = s.T, S = static_cast<int64_t>(s.T) * s.top_k;
+  a.z = cv.take<bf16_t>(T * s.latent);
+  a.g = cv.take<float>(S * s.inter);
+  a.u = cv.take<float>(S * s.inter);
+  a.h = cv.take<bf16_t>(S * s.inter);
+  a.yp = cv.take<float>(S * s.latent);
+  a.gs = cv.take<float>(T * s.shared_inter);
+  a.us = cv.take<float>(T * s.shared_inter);
+  a.hs = cv.take<bf16_t>(T * s.shared_inter);
+  if (out) *out = a;
+  return cv.bytes();
+}
 
 // Tile height of the grouped expert GEMMs, from the mean rows per expert
 // (exact under QB): 32 for decode-like batches, then 96, 160 or 320 rows
@@ -603,6 +622,8 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     q.C = f.hs;
     q.C2 = bf ? f.hs_lo : nullptr;
     q.ldc = ms;
+    q.save_g = f.save_gs;
+    q.save_u = f.save_us;
     q.partial = f.partial;
     q.partial_bytes = f.partial_bytes;
     {
@@ -661,6 +682,8 @@ static int forward(const moe_shape_t& s, const moe_weights_t& wt, const void* x,
     p.a_rows = f.perm;
     p.C = f.h;
     p.ldc = m;
+    p.save_g = f.save_g;
+    p.save_u = f.save_u;
     prof::Scope sc(prof::ST_ROUTED_GATE_UP, st);
     if ((rc = gemm::launch(p, gemm::EPI_SITU, bfmt, bf, f.bm, st)) != MOE_OK) return rc;
   }
@@ -761,6 +784,47 @@ extern "C" int moe_latent_forward(const moe_shape_t* shape, const moe_weights_t*
   moe::layer::ForwardWorkspace fw;
   const size_t need = moe::layer::forward_layout(*shape, &fw, workspace);
   if (workspace_bytes < need) return MOE_EWORKSPACE;
+  return moe::layer::forward(*shape, *weights, x, out, bias, scores_in, scores_out, topk_idx,
+                             topk_w, loads, qb_info, fw, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t moe_saved_activations_bytes(const moe_shape_t* shape) {
+  if (moe::layer::validate(shape, nullptr) != MOE_OK || shape->act_dtype != MOE_BF16 ||
+      shape->routed_dtype != MOE_BF16)
+    return 0;
+  // never 0 for a shape the calls take (0 means "not taken"): at least 256 bytes
+  return std::max<size_t>(moe::layer::saved_layout(*shape, nullptr, nullptr), 256);
+}
+
+extern "C" int moe_latent_forward_train(const moe_shape_t* shape, const moe_weights_t* weights,
+                                        const void* x, void* out, double* bias,
+                                        const float* scores_in, float* scores_out,
+                                        int32_t* topk_idx, float* topk_w, int32_t* loads,
+                                        int32_t* qb_info, void* saved, size_t saved_bytes,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st = moe::layer::validate(shape, weights);
+  if (st != MOE_OK) return st;
+  if (shape->act_dtype != MOE_BF16 || shape->routed_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (!weights || !bias || !workspace || !saved) return MOE_EINVAL;
+  if (shape->T > 0 && (!x || !out)) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+      reinterpret_cast<uintptr_t>(saved) % 256 != 0)
+    return MOE_EINVAL;
+  moe::layer::ForwardWorkspace fw;
+  const size_t need = moe::layer::forward_layout(*shape, &fw, workspace);
+  if (workspace_bytes < need) return MOE_EWORKSPACE;
+  moe::layer::SavedActivations sv;
+  if (saved_bytes < moe::layer::saved_layout(*shape, &sv, saved)) return MOE_EWORKSPACE;
+  // z, h, the experts' outputs and hs live in the saved buffer; the SiTU-GLU
+  // GEMMs also store their pre-activations there
+  fw.z = sv.z;
+  fw.h = sv.h;
+  fw.yp = sv.yp;
+  fw.hs = sv.hs;
+  fw.save_g = sv.g;
+  fw.save_u = sv.u;
+  fw.save_gs = sv.gs;
+  fw.save_us = sv.us;
   return moe::layer::forward(*shape, *weights, x, out, bias, scores_in, scores_out, topk_idx,
                              topk_w, loads, qb_info, fw, static_cast<hipStream_t>(stream));
 }

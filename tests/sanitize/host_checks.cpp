@@ -248,6 +248,30 @@ static void layer_validation() {
   CHECK(fused(&mx, &g, 0.1f, fake(), bneed) == MOE_EUNSUPPORTED);
   CHECK(fused(nullptr, &g, 0.1f, fake(), bneed) == MOE_EINVAL);
 
+  const size_t sneed = moe_saved_activations_bytes(&s);
+  CHECK(sneed > 0 && moe_saved_activations_bytes(&mx) == 0 &&
+        moe_saved_activations_bytes(nullptr) == 0);
+  auto ftrain = [&](void* saved, size_t nsaved) {
+    return moe_latent_forward_train(&s, &w, fake(), fake(), static_cast<double*>(fake()), nullptr,
+                                    nullptr, static_cast<int32_t*>(fake()),
+                                    static_cast<float*>(fake()), static_cast<int32_t*>(fake()),
+                                    static_cast<int32_t*>(fake()), saved, nsaved, fake(), need,
+                                    nullptr);
+  };
+  CHECK(ftrain(nullptr, sneed) == MOE_EINVAL);
+  CHECK(ftrain(fake(8), sneed) == MOE_EINVAL);
+  CHECK(ftrain(fake(), sneed - 1) == MOE_EWORKSPACE);
+  auto btrain = [&](void* saved, size_t nsaved, int sgd, float lr) {
+    return moe_latent_backward_train(&s, &w, fake(), static_cast<const float*>(fake()),
+                                     static_cast<const int32_t*>(fake()),
+                                     static_cast<const float*>(fake()), fake(), saved, nsaved, &g,
+                                     sgd, lr, fake(), bneed, nullptr);
+  };
+  CHECK(btrain(nullptr, sneed, 0, 0.f) == MOE_EINVAL);
+  CHECK(btrain(fake(), sneed - 1, 0, 0.f) == MOE_EWORKSPACE);
+  CHECK(btrain(fake(), sneed, 2, 0.1f) == MOE_EINVAL);
+  CHECK(btrain(fake(), sneed, 1, std::numeric_limits<float>::infinity()) == MOE_EINVAL);
+
   for (auto q : {moe_mxfp8_quantize, moe_mxfp4_quantize}) {
     uint8_t* c = static_cast<uint8_t*>(fake());
     CHECK(q(fake(), 4, 48, c, c, nullptr) == MOE_EINVAL);

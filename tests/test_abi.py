@@ -266,3 +266,36 @@ def test_fused_backward_sgd_validation_on_host():
     no_router = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
     no_router.d_w_router = None
     assert call(g=no_router) == -1
+
+
+def test_training_calls_validation_on_host():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    lib = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: validation fails first
+    sb = lambda **kw: lib.moe_saved_activations_bytes(ctypes.byref(_shape(moe, **kw)))
+    assert sb(T=64) > 0 and sb(T=0) > 0
+    assert sb(routed=moe.MOE_MXFP4) == 0 and sb(act=moe.MOE_F32, routed=moe.MOE_F32) == 0
+    assert sb(T=-1) == 0 and sb(T=(1 << 20) + 1) == 0
+    sh = _shape(moe, T=64)
+    wts = moe.MoeWeights(*([1 << 20] * len(moe.MoeWeights._fields_)))
+    need_f = lib.moe_forward_workspace_bytes(ctypes.byref(sh))
+    need_s = sb(T=64)
+    fwd = lambda saved=fake, nsaved=need_s, s=sh: lib.moe_latent_forward_train(
+        ctypes.byref(s), ctypes.byref(wts), fake, fake, fake, None, None, fake, fake, fake, fake,
+        saved, nsaved, fake, need_f, None)
+    assert fwd(saved=None) == -1
+    assert fwd(saved=ctypes.c_void_p((1 << 20) + 8)) == -1
+    assert fwd(nsaved=need_s - 1) == -3
+    assert fwd(s=_shape(moe, T=64, routed=moe.MOE_MXFP4)) == -2
+    grads = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    need_b = lib.moe_backward_workspace_bytes(ctypes.byref(sh))
+    bwd = lambda saved=fake, nsaved=need_s, sgd=0, lr=0.1, g=grads: lib.moe_latent_backward_train(
+        ctypes.byref(sh), ctypes.byref(wts), fake, fake, fake, fake, fake, saved, nsaved,
+        ctypes.byref(g), sgd, ctypes.c_float(lr), fake, need_b, None)
+    assert bwd(saved=None) == -1
+    assert bwd(nsaved=need_s - 1) == -3
+    assert bwd(sgd=2) == -1
+    assert bwd(sgd=1, lr=float("nan")) == -1
+    no_gate = moe.MoeGrads(*([1 << 20] * len(moe.MoeGrads._fields_)))
+    no_gate.d_w_gate = None
+    assert bwd(g=no_gate) == -1                                 # plain gradients need all of them

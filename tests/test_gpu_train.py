@@ -135,3 +135,67 @@ def test_fused_backward_sgd_matches_separate_calls(kw):
                   for k, inp_v in ((k2, inp[k2 if k2 != "router_logit_offset" else "logit_offset"])
                                    for k2 in w1))
     assert changed == len(w1)
+
+
+TIGHT = 2e-3   # saved against recomputed activations (bf16 flips from split-K rounding only)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=200),
+    dict(T=584, n=64, k=8),
+    dict(T=16, n=64, k=4),
+])
+def test_training_forward_and_backward_with_saved_activations(kw):
+    """The training forward equals the forward bit for bit and keeps its
+    activations; the backward that reads them matches the recomputing
+    backward tightly and the float64 oracle at the backward's bar; with the
+    SGD step it moves the weights like the recomputing fused call."""
+    import sparse_moe_ffn_sigmoid_amd as moe
+    from test_gpu_backward import KEYS, TOL_FRO, TOL_ROW, worst_row
+    shape = workloads.small_shape(**kw)
+    announce(f"training forward / backward with saved activations {shape}")
+    inp = workloads.layer_inputs(shape, "cpu", seed=8, random_gamma=True)
+    x, w = to_device(inp)
+    w["router_logit_offset"] = w.pop("logit_offset")
+    sh = make_shape(moe, shape)
+    saved = torch.empty(moe.saved_activations_bytes(sh), dtype=torch.uint8, device="cuda")
+    f1 = moe.latent_forward(sh, w, x, want_scores=True)
+    f2 = moe.latent_forward(sh, w, x, want_scores=True, saved=saved)
+    for key in f1:
+        a, b = f1[key], f2[key]
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), key
+    dout = torch.randn((shape.T, shape.d), generator=torch.Generator().manual_seed(3)).to(
+        torch.bfloat16).cuda()
+    args = (sh, w, x, f2["scores"], f2["idx"], f2["w"], dout)
+    rec = moe.latent_backward(*args)
+    got = moe.latent_backward_train(*args, saved)
+    torch.cuda.synchronize()
+    idx = f2["idx"].cpu().numpy()
+    ref = ograd.layer_grads(inp, idx, shape.eps, dout.double().cpu().numpy())
+    for name, key in KEYS.items():
+        if got[name] is None:
+            assert ref[key] is None
+            continue
+        g = got[name].float().cpu().numpy()
+        r0 = rec[name].float().cpu().numpy()
+        t = float(np.linalg.norm(g - r0) / max(np.linalg.norm(r0), 1e-30))
+        fro = float(np.linalg.norm(g - ref[key]) / np.linalg.norm(ref[key]))
+        print(f"  {name:<24} against recompute {t:.1e}, against oracle {fro:.2e}", flush=True)
+        assert t <= TIGHT and fro <= TOL_FRO, name
+        if ref[key].ndim >= 2:
+            assert worst_row(g, ref[key]) <= TOL_ROW, name
+    # with the SGD step: the update applied to every weight matches the
+    # recomputing fused call's
+    w1 = {key: v.clone() for key, v in w.items()}
+    w2 = {key: v.clone() for key, v in w.items()}
+    moe.latent_backward_sgd(sh, w1, *args[2:], 1e-2)
+    moe.latent_backward_train(sh, w2, *args[2:], saved, lr=1e-2)
+    torch.cuda.synchronize()
+    for key in w:
+        d_ref = w1[key].double() - w[key].double()
+        d_got = w2[key].double() - w[key].double()
+        rel = float((d_got - d_ref).norm() / d_ref.norm())
+        print(f"  update of {key:<20} against the recomputing call's update {rel:.1e}", flush=True)
+        # the gradients differ by < TIGHT; bf16 weights add a rounding flip here and there
+        assert rel <= 1e-2, key
