@@ -93,3 +93,60 @@ def test_route_graph_replays_bit_identical():
         g.replay()
         torch.cuda.synchronize()
         assert_same(eager, host(r_g), f"replay {rep}")
+
+
+def test_training_step_graph_replays_match_eager_steps():
+    """One training step (training forward with QB on the batch, the bias
+    carried in a device buffer, then the backward with the fused SGD update
+    reading the saved activations) captured once: three replays from the
+    initial weights give the outputs and the weights of three eager steps,
+    bit for bit."""
+    import sparse_moe_ffn_sigmoid_amd as moe
+    shape = workloads.small_shape(T=200)
+    announce("graph training step")
+    inp = workloads.layer_inputs(shape, "cpu", seed=12, random_gamma=True)
+    x, w0 = to_device(inp)
+    w0["router_logit_offset"] = w0.pop("logit_offset")
+    sh = make_shape(moe, shape)
+    ws = torch.empty(moe.forward_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(moe.lib().moe_backward_workspace_bytes(ctypes_ref(moe, sh)),
+                      dtype=torch.uint8, device="cuda")
+    saved = torch.empty(moe.saved_activations_bytes(sh), dtype=torch.uint8, device="cuda")
+    dout = torch.randn((shape.T, shape.d), generator=torch.Generator().manual_seed(4)).to(
+        torch.bfloat16).cuda()
+    bias = torch.zeros(shape.n, dtype=torch.float64, device="cuda")
+
+    def step(wd):
+        f = moe.latent_forward(sh, wd, x, bias=bias, workspace=ws, want_scores=True, saved=saved)
+        bias.copy_(f["bias"])
+        moe.latent_backward_train(sh, wd, x, f["scores"], f["idx"], f["w"], dout, saved, lr=1e-3,
+                                  workspace=bws)
+        return f["out"]
+
+    w_e = {k: v.clone() for k, v in w0.items()}
+    outs = []
+    for _ in range(3):
+        outs.append(step(w_e).view(torch.int16).cpu().numpy())
+    torch.cuda.synchronize()
+    w_g = {k: v.clone() for k, v in w0.items()}
+    bias.zero_()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out_g = step(w_g)
+    torch.cuda.synchronize()
+    for i in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_g.view(torch.int16).cpu().numpy(), outs[i]), f"replay {i}"
+        torch.zeros(1 << 20, device="cuda").sum()  # other eager work between the replays
+    for k in w_e:
+        a, b = w_e[k], w_g[k]
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b), k
+    del g
+
+
+def ctypes_ref(moe, sh):
+    import ctypes
+    return ctypes.byref(sh)
