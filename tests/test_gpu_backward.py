@@ -142,14 +142,16 @@ def test_backward_deterministic():
                                if b[key].dtype == torch.bfloat16 else b[key]), key
 
 
-def test_backward_k3_prefill_full_size_dx_sampled():
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_k3_prefill_full_size_dx_sampled(saved):
     """The full K3 prefill layer (T = 4096, 896 experts, k = 16), forward and
-    backward as the benchmark runs them; dx of sampled tokens (first, thirds,
-    last and the last token of the first and last expert) against the
-    gradient oracle on each token alone.  Tokens are independent once the
-    selection is fixed, so a token's dx needs only its own 16 experts: the
-    oracle runs on the token with those experts' weights (router rows, gate,
-    up, down) and the full dense weights."""
+    backward as the benchmark runs them (saved: the training forward keeps
+    its activations and the backward reads them); dx of sampled tokens
+    (first, thirds, last and the last token of the first and last expert)
+    against the gradient oracle on each token alone.  Tokens are independent
+    once the selection is fixed, so a token's dx needs only its own 16
+    experts: the oracle runs on the token with those experts' weights
+    (router rows, gate, up, down) and the full dense weights."""
     import sparse_moe_ffn_sigmoid_amd as moe
     shape = workloads.SHAPES["k3_prefill"]
     announce(f"backward full size {shape}")
@@ -159,16 +161,22 @@ def test_backward_k3_prefill_full_size_dx_sampled():
     w["router_logit_offset"] = w.pop("logit_offset")
     sh = moe.make_shape(shape.T, shape.d, shape.latent, shape.n, shape.k, shape.m, shape.shared,
                         moe.MOE_BF16, moe.MOE_BF16, shape.eps, moe.MOE_QB_BATCH, 64)
-    fwd = moe.latent_forward(sh, w, inp["x"], want_scores=True)
+    sv = (torch.empty(moe.saved_activations_bytes(sh), dtype=torch.uint8, device=dev)
+          if saved else None)
+    fwd = moe.latent_forward(sh, w, inp["x"], want_scores=True, saved=sv)
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
     dout = torch.randn(inp["x"].shape, generator=g, device=dev, dtype=torch.float32).to(
         torch.bfloat16)
-    got = moe.latent_backward(sh, w, inp["x"], fwd["scores"], fwd["idx"], fwd["w"], dout)
+    if saved:
+        got = moe.latent_backward_train(sh, w, inp["x"], fwd["scores"], fwd["idx"], fwd["w"],
+                                        dout, sv)
+    else:
+        got = moe.latent_backward(sh, w, inp["x"], fwd["scores"], fwd["idx"], fwd["w"], dout)
     torch.cuda.synchronize()
     idx = fwd["idx"].cpu().numpy()
     dx = got["dx"].float().cpu().numpy()
-    del got
+    del got, sv
     torch.cuda.empty_cache()
     T = shape.T
     flat = idx.ravel()
