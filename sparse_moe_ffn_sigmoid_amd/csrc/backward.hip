@@ -7,12 +7,13 @@
 // shared expert).
 //
 // The call recomputes the forward activations from x and the forward's
-// routing (scores, idx, w), then runs the backward products on the same
-// pipelined MFMA GEMM (C = A B^T).  The experts' weights enter the products
+// routing (scores, idx, w), or reads those a training forward kept, then
+// runs the backward products on the same pipelined MFMA GEMM (C = A B^T).  The experts' weights enter the products
 // through them as [K][N] B operands read in place (transposing LDS reads);
 // other operands that are not K-contiguous take transposed copies; the
 // weight gradients of the routed experts are K-grouped products over each
-// expert's slots (zero-padded to 64).  MFMA operands are bf16,
+// expert's slots (zero-padded to 64), optionally applied to the weights in
+// their epilogue (the SGD step of a training step).  MFMA operands are bf16,
 // accumulations and gradients fp32.
 #include <algorithm>
 #include <cmath>
