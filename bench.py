@@ -206,6 +206,34 @@ def time_train(moe, sh, w, x, bias0, ws, shape, args, mode="saved"):
                 "separate": " (activations recomputed; backward and update as two calls)"}[mode]}
 
 
+def time_graph(step, shape, args):
+    """The timed forward step captured once in a HIP graph and replayed
+    (same inputs, same kernels; no host launch work per step)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    del g
+    return {"ms_per_step": ms, "tokens_per_s": shape.T / (ms / 1e3),
+            "what": "the same forward step captured once in a HIP graph and replayed"}
+
+
 def ctypes_ref(obj):
     import ctypes
     return ctypes.byref(obj)
@@ -375,6 +403,9 @@ def main():
     ap.add_argument("--sign-baseline", action="store_true",
                     help="also route this batch's scores with the fixed-step sign update "
                          "(DeepSeek-V3's bias rule) and report rounds / imbalance / time beside QB")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward step captured in a HIP graph and replayed; "
+                         "reported under 'graph'")
     ap.add_argument("--train", action="store_true",
                     help="also time a training step (forward, backward, SGD update; bf16 layers); "
                          "reported under 'train', after every other measurement (it changes "
@@ -514,6 +545,8 @@ def main():
         rec["routing_baseline"] = sign_baseline(moe, sh, w, x, bias0, ws, shape)
     if args.backward:
         rec["backward"] = time_backward(moe, sh, w, x, bias0, ws, shape, args)
+    if args.graph:
+        rec["graph"] = time_graph(step, shape, args)
     if args.copy_bytes > 0:
         copy_reference(args.copy_bytes, dev)
     if not args.no_cpu_baseline:
