@@ -27,6 +27,9 @@ Modules:
   Balancing (coordinate rounds + exact completion), outputs.
 * :mod:`oracle.layer`  -- router, SiTU-GLU, RMSNorm, MXFP4 decoding and the
   whole latent-MoE layer in float64.
+* :mod:`oracle.grad`   -- gradients of the layer (autograd over a float64
+  PyTorch CPU restatement of the forward pass, selection held fixed) and the
+  plain SGD weight update.
 
 Parity status of each function is stated in its docstring.  The pages print
 no worked numeric example of the whole layer; its composition is pinned on
