@@ -820,6 +820,63 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
     }
     return;
   }
+  // Staged output (grouped problems, see Params::stage_out): per 32-row
+  // fragment pass, every wave writes its results (fp32, or SiTU-GLU as bf16)
+  // into stage 0 of the ring, rows padded by 32 bytes so that the two row
+  // groups of one store land on different banks; then each lane copies 16
+  // bytes, a wave's store covering whole output rows, with the non-temporal
+  // policy (the outputs are read once, by the next kernel).  Bit-identical
+  // to the direct epilogue below; writing rows instead of 2- and 4-byte
+  // pieces, and keeping them out of L2, costs less of the weight stream's
+  // bandwidth.
+  constexpr int ST_ESZ = (EPI == EPI_SITU) ? 2 : 4;
+  constexpr int ST_RB = BN_OUT * ST_ESZ, ST_RBP = ST_RB + 32;
+  if constexpr ((EPI == EPI_F32 || EPI == EPI_SITU) && WM * 32 * ST_RBP <= SW * 2 &&
+                ST_RB % 16 == 0) {
+    if (p.stage_out && kn == 1) {
+      typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+      constexpr int CPR = ST_RB / 16;  // 16-byte chunks per output row
+      constexpr int ROWS = WM * 32;    // rows per pass
+      char* const sb = reinterpret_cast<char*>(stg[0]);
+      lds_barrier();  // every wave is done with the ring
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          if constexpr (EPI == EPI_SITU) {
+#pragma unroll
+            for (int j = 0; j < FN; j += 2) {
+              const int oc = ((wn * FN + j) >> 1) * 32 + (lane & 31);
+              *reinterpret_cast<bf16_t*>(sb + lr * ST_RBP + oc * 2) =
+                  f32_to_bf16(situ_glu(acc[i][j][r], acc[i][j + 1][r]));
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int oc = wn * WTN + j * 32 + (lane & 31);
+              *reinterpret_cast<float*>(sb + lr * ST_RBP + oc * 4) = acc[i][j][r];
+            }
+          }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int c0 = 0; c0 < ROWS * CPR; c0 += 64 * NW) {
+          const int c = c0 + tid;
+          const int lr = c / CPR, ch = c % CPR;
+          const int row = (lr >> 5) * WTM + i * 32 + (lr & 31);
+          const int col = tile.n0 + ch * (16 / ST_ESZ);
+          if (c < ROWS * CPR && row < tile.rows && col < p.N) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sb + lr * ST_RBP + ch * 16);
+            char* dst = static_cast<char*>(p.C) + ((tile.row0 + row) * p.ldc + col) * ST_ESZ;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
+          }
+        }
+        lds_barrier();
+      }
+      return;
+    }
+  }
   if (kn > 1) {  // fp32 partials, columns in B-row order of the tile
     const int64_t nv = static_cast<int64_t>(ntn) * BN;
     const int64_t cb = static_cast<int64_t>(tile.n0 / BN_OUT) * BN + wn * WTN + (lane & 31);
@@ -1576,6 +1633,14 @@ static int dispatch_epi(const Params& p, int epi, hipStream_t s) {
   }
 }
 
+// Whether a grouped launch may write its output rows 16 bytes per lane
+// (Params::stage_out): fp32 or SiTU-GLU outputs without residue or
+// pre-activation stores, whole 16-byte chunks per row, aligned rows.
+static int row_stores_ok(const Params& q, int epi) {
+  return (epi == EPI_F32 || epi == EPI_SITU) && !q.C2 && !q.save_g && q.N % 8 == 0 &&
+         q.ldc % 8 == 0 && reinterpret_cast<uintptr_t>(q.C) % 16 == 0;
+}
+
 int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipStream_t stream) {
   // low parts are written by the dense bf16 kernels and their split-K reduction
   if (p.C2 && !(act_bf16 && bfmt == B_DENSE && !p.tiles && (epi == EPI_BF16 || epi == EPI_SITU)))
@@ -1621,6 +1686,7 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
         return MOE_EUNSUPPORTED;
     Params q = p;
     q.ksplit = 1;
+    q.stage_out = row_stores_ok(q, epi);
     if (bm_hint <= 32) return run_pipe<32, 256, 1, EPI_F32, 64, 3, true, 4, true>(q, stream);
     if (bm_hint <= 96) return run_pipe<96, 256, 1, EPI_F32, 64, 3, true, 4, true>(q, stream);
     if (bm_hint == 160) return run_pipe<160, 256, 1, EPI_F32, 64, 3, false, 4, true>(q, stream);
@@ -1634,6 +1700,7 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
     // rows per weight byte)
     Params q = p;
     q.ksplit = 1;
+    q.stage_out = row_stores_ok(q, epi);
     // about one row tile per expert: each weight byte is read once
     if (bm_hint <= 32) return dispatch_pipe<32, 256, 1, 64, true>(q, epi, stream);
     if (bm_hint <= 96)  // 128-byte row pieces per stage, one block per CU

@@ -70,6 +70,11 @@ struct Params {
   float* partial;
   size_t partial_bytes;
   int ksplit;
+  // Set by launch() for grouped problems whose output rows can be written
+  // 16 bytes per lane (fp32 or SiTU-GLU outputs, no residue or pre-activation
+  // stores, N and ldc multiples of 8, C 16-byte aligned): the kernel stages
+  // each tile through LDS and writes whole rows with non-temporal stores.
+  int stage_out;
 };
 
 // Bytes of fp32 partials launch() uses for a bf16 dense problem (0: no split).
