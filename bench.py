@@ -31,9 +31,9 @@ PEAK_FP4_TFLOPS = 10100.0  # dense fp4 MFMA (the W4A4 experts' E2M1 x E2M1 produ
 # WRITE_SIZE runs scaled by a 1 GiB device copy (profiles/layer_<workload>.txt,
 # profiles/routing_qb_57344x896.txt); None where not measured for the current
 # kernel.  Keyed by (workload, qb mode).
-TRAFFIC = {("k3_prefill", "batch"): 27.032e9,      # gemm_pipe<96, 256, 1, 3, 64, 3, true, 4, false>
+TRAFFIC = {("k3_prefill", "batch"): 27.006e9,      # gemm_pipe<96, 256, 1, 3, 64, 3, true, 4, false>
            ("k3_decode", "batch"): 26.313e9,       # gemm_pipe<32, 256, 1, 3, 64, 3, true, 4, false>
-           ("k3_prefill_16k", "batch"): 29.248e9,  # gemm_pipe<320, 256, 2, 3, 64, 2, true, 8, false>
+           ("k3_prefill_16k", "batch"): 29.230e9,  # gemm_pipe<320, 256, 2, 3, 64, 2, true, 8, false>
            ("k3_mxfp4", "batch"): 9.928e9,         # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 0, 3>
            ("k3_mxfp4", "frozen"): 13.244e9,       # the same kernel, skewed loads (several tiles per expert)
            ("k3_mxfp4_a8", "batch"): 9.291e9,      # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 8, 2>
