@@ -820,59 +820,68 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && BKP == 32 && BM * BN <= 128 * 
     }
     return;
   }
-  // Staged output (grouped problems, see Params::stage_out): per 32-row
-  // fragment pass, every wave writes its results (fp32, or SiTU-GLU as bf16)
-  // into stage 0 of the ring, rows padded by 32 bytes so that the two row
-  // groups of one store land on different banks; then each lane copies 16
-  // bytes, a wave's store covering whole output rows, with the non-temporal
-  // policy (the outputs are read once, by the next kernel).  Bit-identical
-  // to the direct epilogue below; writing rows instead of 2- and 4-byte
-  // pieces, and keeping them out of L2, costs less of the weight stream's
-  // bandwidth.
+  // Staged output (grouped and K-grouped problems, see Params::stage_out):
+  // per pass, every wave of the pass's row groups writes one 32-row fragment
+  // of its results (fp32, or SiTU-GLU as bf16) into stage 0 of the ring
+  // (all row groups at once when they fit, else one at a time), rows padded
+  // by 32 bytes so that the two row halves of one store land on different
+  // banks; then each lane copies 16 bytes, a wave's store covering whole
+  // output rows, with the non-temporal policy (the outputs are read once, by
+  // the next kernel).  Bit-identical to the direct epilogue below; writing
+  // rows instead of 2- and 4-byte pieces, and keeping them out of L2, costs
+  // less of the weight stream's bandwidth.
   constexpr int ST_ESZ = (EPI == EPI_SITU) ? 2 : 4;
   constexpr int ST_RB = BN_OUT * ST_ESZ, ST_RBP = ST_RB + 32;
-  if constexpr ((EPI == EPI_F32 || EPI == EPI_SITU) && WM * 32 * ST_RBP <= SW * 2 &&
+  if constexpr ((EPI == EPI_F32 || EPI == EPI_SITU) && 32 * ST_RBP <= SW * 2 &&
                 ST_RB % 16 == 0) {
     if (p.stage_out && kn == 1) {
       typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+      constexpr int GP = WM * 32 * ST_RBP <= SW * 2 ? WM : 1;  // row groups per pass
       constexpr int CPR = ST_RB / 16;  // 16-byte chunks per output row
-      constexpr int ROWS = WM * 32;    // rows per pass
       char* const sb = reinterpret_cast<char*>(stg[0]);
+      char* const cbase = static_cast<char*>(p.C) + cgrp * ST_ESZ;
       lds_barrier();  // every wave is done with the ring
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if constexpr (EPI == EPI_SITU) {
+        for (int h0 = 0; h0 < WM; h0 += GP) {
+          if (h0 * WTM + i * 32 < tile.rows) {  // uniform: the pass holds valid rows
+            if (wm >= h0 && wm < h0 + GP) {
 #pragma unroll
-            for (int j = 0; j < FN; j += 2) {
-              const int oc = ((wn * FN + j) >> 1) * 32 + (lane & 31);
-              *reinterpret_cast<bf16_t*>(sb + lr * ST_RBP + oc * 2) =
-                  f32_to_bf16(situ_glu(acc[i][j][r], acc[i][j + 1][r]));
-            }
-          } else {
+              for (int r = 0; r < 16; ++r) {
+                const int lr = (wm - h0) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if constexpr (EPI == EPI_SITU) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              const int oc = wn * WTN + j * 32 + (lane & 31);
-              *reinterpret_cast<float*>(sb + lr * ST_RBP + oc * 4) = acc[i][j][r];
+                  for (int j = 0; j < FN; j += 2) {
+                    const int oc = ((wn * FN + j) >> 1) * 32 + (lane & 31);
+                    *reinterpret_cast<bf16_t*>(sb + lr * ST_RBP + oc * 2) =
+                        f32_to_bf16(situ_glu(acc[i][j][r], acc[i][j + 1][r]));
+                  }
+                } else {
+#pragma unroll
+                  for (int j = 0; j < FN; ++j) {
+                    const int oc = wn * WTN + j * 32 + (lane & 31);
+                    *reinterpret_cast<float*>(sb + lr * ST_RBP + oc * 4) = acc[i][j][r];
+                  }
+                }
+              }
             }
+            lds_barrier();
+#pragma unroll
+            for (int c0 = 0; c0 < GP * 32 * CPR; c0 += 64 * NW) {
+              const int c = c0 + tid;
+              const int lr = c / CPR, ch = c % CPR;
+              const int row = (h0 + (lr >> 5)) * WTM + i * 32 + (lr & 31);
+              const int col = tile.n0 + ch * (16 / ST_ESZ);
+              if (c < GP * 32 * CPR && row < tile.rows && col < p.N) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sb + lr * ST_RBP + ch * 16);
+                char* dst = cbase + ((static_cast<int64_t>(tile.row0) + row) * p.ldc + col) * ST_ESZ;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
+              }
+            }
+            lds_barrier();
           }
         }
-        lds_barrier();
-#pragma unroll
-        for (int c0 = 0; c0 < ROWS * CPR; c0 += 64 * NW) {
-          const int c = c0 + tid;
-          const int lr = c / CPR, ch = c % CPR;
-          const int row = (lr >> 5) * WTM + i * 32 + (lr & 31);
-          const int col = tile.n0 + ch * (16 / ST_ESZ);
-          if (c < ROWS * CPR && row < tile.rows && col < p.N) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sb + lr * ST_RBP + ch * 16);
-            char* dst = static_cast<char*>(p.C) + ((tile.row0 + row) * p.ldc + col) * ST_ESZ;
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
-          }
-        }
-        lds_barrier();
       }
       return;
     }
@@ -1739,6 +1748,7 @@ int launch(const Params& p, int epi, int bfmt, bool act_bf16, int bm_hint, hipSt
       return MOE_EUNSUPPORTED;
     Params q = p;
     q.ksplit = 1;
+    q.stage_out = epi == EPI_F32 && q.c_group_stride % 8 == 0 ? row_stores_ok(q, epi) : 0;
     if (epi == EPI_SGD) return run_pipe<256, 256, 2, EPI_SGD, 64, 2, false, 8>(q, stream);
     return dispatch_pipe<256, 256, 2, 64, false, 8>(q, epi, stream);
   }
