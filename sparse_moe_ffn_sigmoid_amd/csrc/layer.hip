@@ -253,9 +253,11 @@ __global__ __launch_bounds__(256) void mx4_quantize(const bf16_t* __restrict__ i
 }
 
 // y_t = sum_j w[t][j] * yp[inv[t][j]] in fp32 (j ascending), then
-// RMSNorm: y * rsqrt(mean(y^2) + eps) * gamma.  One block per token.  With
-// bf16 output, out_lo (when given) receives bf16(v - bf16(v)), so that the
-// up-projection can take the normalised row to about 16 bits.
+// RMSNorm: y * rsqrt(mean(y^2) + eps) * gamma.  One block per token; each
+// lane owns groups of 4 consecutive columns (16-byte loads of the slot rows,
+// which are read once: non-temporal).  With bf16 output, out_lo (when given)
+// receives bf16(v - bf16(v)), so that the up-projection can take the
+// normalised row to about 16 bits.  L is a multiple of 4 and at most 4096.
 template <typename ACT>
 __global__ __launch_bounds__(256) void combine_rmsnorm(const float* __restrict__ yp,
                                                        const int32_t* __restrict__ inv,
@@ -263,37 +265,45 @@ __global__ __launch_bounds__(256) void combine_rmsnorm(const float* __restrict__
                                                        const float* __restrict__ gamma, int k,
                                                        int L, float eps, ACT* __restrict__ out,
                                                        bf16_t* __restrict__ out_lo) {
-  constexpr int MAXV = 16;  // L <= 256 * MAXV
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int MAXG = 4;  // column groups of 4 per lane: L <= 256 * 4 * MAXG
   __shared__ float s_red[256];
   const int t = blockIdx.x;
-  float acc[MAXV];
+  const int L4 = L >> 2;
+  f32x4_t acc[MAXG];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) acc[i] = 0.f;
+  for (int i = 0; i < MAXG; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // four slot rows per round trip: their loads are all in flight together
   constexpr int RB = 4;
   for (int j0 = 0; j0 < k; j0 += RB) {
-    float v[RB][MAXV];
+    f32x4_t v[RB][MAXG];
     float wj[RB];
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
       const int j = j0 + q;
       wj[q] = j < k ? w[static_cast<int64_t>(t) * k + j] : 0.f;
-      const float* src =
-          j < k ? yp + static_cast<int64_t>(inv[static_cast<int64_t>(t) * k + j]) * L : nullptr;
+      const f32x4_t* src =
+          j < k ? reinterpret_cast<const f32x4_t*>(
+                      yp + static_cast<int64_t>(inv[static_cast<int64_t>(t) * k + j]) * L)
+                : nullptr;
 #pragma unroll
-      for (int i = 0; i < MAXV; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        v[q][i] = (src && c < L) ? src[c] : 0.f;
+      for (int i = 0; i < MAXG; ++i) {
+        const int c4 = threadIdx.x + 256 * i;
+        v[q][i] = (src && c4 < L4) ? __builtin_nontemporal_load(src + c4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll
     for (int q = 0; q < RB; ++q)
 #pragma unroll
-      for (int i = 0; i < MAXV; ++i) acc[i] = fmaf(wj[q], v[q][i], acc[i]);
+      for (int i = 0; i < MAXG; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wj[q], v[q][i][e], acc[i][e]);
   }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) ss = fmaf(acc[i], acc[i], ss);
+  for (int i = 0; i < MAXG; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fmaf(acc[i][e], acc[i][e], ss);
   s_red[threadIdx.x] = ss;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -302,13 +312,17 @@ __global__ __launch_bounds__(256) void combine_rmsnorm(const float* __restrict__
   }
   const float scale = rsqrtf(s_red[0] / static_cast<float>(L) + eps);
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    if (c < L) {
-      const float v = acc[i] * scale * gamma[c];
-      const ACT o = from_f32<ACT>(v);
-      out[static_cast<int64_t>(t) * L + c] = o;
-      if (out_lo) out_lo[static_cast<int64_t>(t) * L + c] = f32_to_bf16(v - static_cast<float>(to_f32(o)));
+  for (int i = 0; i < MAXG; ++i) {
+    const int c4 = threadIdx.x + 256 * i;
+    if (c4 < L4) {
+      const int64_t o0 = static_cast<int64_t>(t) * L + 4 * c4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = acc[i][e] * scale * gamma[4 * c4 + e];
+        const ACT o = from_f32<ACT>(v);
+        out[o0 + e] = o;
+        if (out_lo) out_lo[o0 + e] = f32_to_bf16(v - static_cast<float>(to_f32(o)));
+      }
     }
   }
 }
