@@ -31,13 +31,13 @@ PEAK_FP4_TFLOPS = 10100.0  # dense fp4 MFMA (the W4A4 experts' E2M1 x E2M1 produ
 # WRITE_SIZE runs scaled by a 1 GiB device copy (profiles/layer_<workload>.txt,
 # profiles/routing_qb_57344x896.txt); None where not measured for the current
 # kernel.  Keyed by (workload, qb mode).
-TRAFFIC = {("k3_prefill", "batch"): 27.006e9,      # gemm_pipe<96, 256, 1, 3, 64, 3, true, 4, false>
+TRAFFIC = {("k3_prefill", "batch"): 27.007e9,      # gemm_pipe<96, 256, 1, 3, 64, 3, true, 4, false>
            ("k3_decode", "batch"): 26.313e9,       # gemm_pipe<32, 256, 1, 3, 64, 3, true, 4, false>
-           ("k3_prefill_16k", "batch"): 29.230e9,  # gemm_pipe<320, 256, 2, 3, 64, 2, true, 8, false>
+           ("k3_prefill_16k", "batch"): 29.231e9,  # gemm_pipe<320, 256, 2, 3, 64, 2, true, 8, false>
            ("k3_mxfp4", "batch"): 9.927e9,         # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 0, 3>
-           ("k3_mxfp4", "frozen"): 12.859e9,       # the same kernel, skewed loads (several tiles per expert)
+           ("k3_mxfp4", "frozen"): 12.663e9,       # the same kernel, skewed loads (several tiles per expert)
            ("k3_mxfp4_a8", "batch"): 9.111e9,      # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 8, 2>
-           ("k3_mxfp4_a4", "batch"): 8.591e9,      # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 4, 3>
+           ("k3_mxfp4_a4", "batch"): 8.592e9,      # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 4, 3>
            ("tiny", "batch"): 2.369e6,             # gemm_f32<EPI_SITU>
            ("qb", "batch"): 23.216e9}              # route_loop<14>
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
