@@ -31,15 +31,15 @@ PEAK_FP4_TFLOPS = 10100.0  # dense fp4 MFMA (the W4A4 experts' E2M1 x E2M1 produ
 # WRITE_SIZE runs scaled by a 1 GiB device copy (profiles/layer_<workload>.txt,
 # profiles/routing_qb_57344x896.txt); None where not measured for the current
 # kernel.  Keyed by (workload, qb mode).
-TRAFFIC = {("k3_prefill", "batch"): 27.007e9,      # gemm_pipe<96, 256, 1, 3, 64, 3, true, 4, false>
+TRAFFIC = {("k3_prefill", "batch"): 27.006e9,      # gemm_pipe<96, 256, 1, 3, 64, 3, true, 4, false>
            ("k3_decode", "batch"): 26.313e9,       # gemm_pipe<32, 256, 1, 3, 64, 3, true, 4, false>
            ("k3_prefill_16k", "batch"): 29.231e9,  # gemm_pipe<320, 256, 2, 3, 64, 2, true, 8, false>
-           ("k3_mxfp4", "batch"): 9.927e9,         # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 0, 3>
-           ("k3_mxfp4", "frozen"): 12.663e9,       # the same kernel, skewed loads (several tiles per expert)
+           ("k3_mxfp4", "batch"): 9.928e9,         # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 0, 3>
+           ("k3_mxfp4", "frozen"): 12.680e9,       # the same kernel, skewed loads (several tiles per expert)
            ("k3_mxfp4_a8", "batch"): 9.111e9,      # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 8, 2>
            ("k3_mxfp4_a4", "batch"): 8.592e9,      # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 4, 3>
            ("tiny", "batch"): 2.369e6,             # gemm_f32<EPI_SITU>
-           ("qb", "batch"): 23.216e9}              # route_loop<14>
+           ("qb", "batch"): 23.217e9}              # route_loop<14>
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
 
 
@@ -63,18 +63,19 @@ def weight_bytes(s, touched):
 
 def gate_up_bytes(s, touched, T):
     """Algorithmic HBM bytes of one routed gate/up launch: the gate and up
-    weights of every expert that received a token, the gathered latent rows
-    it reads and the SiTU-GLU output it writes."""
+    weights of every expert that received a token, the latent rows z read
+    once (a token's row serves all k of its experts) and the SiTU-GLU output
+    written (one row per token and chosen expert)."""
     eb = 2 if s.act == "bf16" else 4
     if s.routed in ("mxfp4", "mxfp4_a8", "mxfp4_a4"):
         w = touched * 2 * (s.m * s.latent // 2 + s.m * s.latent // 32)
     else:
         w = touched * 2 * s.m * s.latent * eb
-    if s.routed == "mxfp4_a8":  # E4M3 codes and E8M0 scales of the gathered rows
-        return w + T * s.k * (s.latent + s.latent // 32) + T * s.k * s.m * eb
-    if s.routed == "mxfp4_a4":  # E2M1 codes (two per byte) and E8M0 scales of the gathered rows
-        return w + T * s.k * (s.latent // 2 + s.latent // 32) + T * s.k * s.m * eb
-    return w + T * s.k * s.latent * eb + T * s.k * s.m * eb
+    if s.routed == "mxfp4_a8":  # E4M3 codes and E8M0 scales of z
+        return w + T * (s.latent + s.latent // 32) + T * s.k * s.m * eb
+    if s.routed == "mxfp4_a4":  # E2M1 codes (two per byte) and E8M0 scales of z
+        return w + T * (s.latent // 2 + s.latent // 32) + T * s.k * s.m * eb
+    return w + T * s.latent * eb + T * s.k * s.m * eb
 
 
 def cpu_baseline(inp, shape, sample_tokens):
