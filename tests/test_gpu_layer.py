@@ -81,6 +81,7 @@ def test_tiny_fp32_layer():
     dict(),                                                   # several tiles, ragged rows
     dict(T=37, n=24, k=3, d=448, latent=192, m=128, shared=192),
     dict(T=16, n=64, k=4),                                     # ~1 row per expert (small-M tile)
+    dict(T=500, n=16, k=2, latent=320),                        # 62-63 rows: one 96-row tile, column tails in both GEMMs
     dict(T=600, n=16, k=4),                                    # 150 rows per expert: one 160-row tile
     dict(T=1000, n=16, k=4, seed=7),                           # 250 rows: one 320-row tile (8 waves)
     dict(T=1200, n=16, k=4, d=512, seed=1),                    # 300 rows: one 320-row tile, ragged
