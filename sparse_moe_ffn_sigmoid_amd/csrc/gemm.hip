@@ -8,12 +8,25 @@
 // the routed down-projection per expert, and the up-projection concatenated
 // along K with the shared down-projection (so the shared-expert add is free).
 //
-// bf16 kernel: 256 threads as a WM x WN grid of waves, v_mfma_f32_32x32x16_bf16
-// on 32x32 blocks, BK = 64, double-buffered LDS with rows padded by 16 bytes
-// (conflict-free 16-byte fragment reads), global loads for tile k+1 issued
-// before the MFMAs of tile k.  MXFP4 B tiles are decoded to bf16 (exact:
-// E2M1 value with the E8M0 exponent added) when they are written to LDS.
-// The epilogue goes through LDS so that stores are row-contiguous.
+// Kernels:
+// * gemm_pipe: the main bf16 kernel.  Waves in a WM x WN grid,
+//   v_mfma_f32_32x32x16_bf16 on 32x32 blocks; tiles go from HBM straight into
+//   LDS (global_load_lds_dwordx4) through a ring of 2 - 3 stages with
+//   XOR-swizzled 16-byte chunks; dense, grouped (experts, gathered rows) and
+//   K-grouped (expert weight gradients) problems; B stored [N][K] or [K][N]
+//   (ds_read_b64_tr_b16).  Dense products store straight from the
+//   accumulators; grouped and K-grouped ones stage each fragment pass through
+//   the ring and write whole rows, 16 bytes per lane, non-temporally; the
+//   in-place SGD update is staged the same way.
+// * gemm_pipe_fp4: MXFP4 routed experts.  E2M1 codes go to LDS as they are
+//   and are decoded per fragment (E8M0 scales from a per-block panel or the
+//   ring), or, with quantised activations (W4A8 / W4A4), multiplied as codes
+//   by the scaled MFMA; grouped outputs staged like gemm_pipe's.
+// * gemm_bf16: register-staged kernel for shapes outside the pipelined
+//   kernels' limits (LDS rows padded by 16 bytes, MXFP4 decoded while
+//   written to LDS, epilogue through LDS).
+// * gemm_f32: the fp32 layer (FMA), and splitk_reduce: the fixed-order sum
+//   of split-K partials with the epilogue.
 #include "gemm.hpp"
 
 #include <atomic>
