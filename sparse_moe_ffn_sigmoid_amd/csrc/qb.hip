@@ -829,10 +829,15 @@ __device__ __attribute__((always_inline)) inline int64_t quantile_bias(const Arg
   const int lane = tid & 63, wid = tid >> 6;
   const int64_t cut = -be * 1024;
   // LDS after the scratch: every margin (8 bytes a token) when it fits, else
-  // every token's bucket (2 bytes), else nothing (the gather recomputes)
+  // every token's bucket (2 bytes), else every token's coarse bucket (1 byte:
+  // the bucket / 8; the gather recomputes the margins of the tokens whose
+  // coarse bucket can hold the wanted ranks), else nothing (the gather
+  // recomputes every margin)
   const bool mcached = T <= a.bucket_cap / 4;
   const bool cached = !mcached && T <= a.bucket_cap;
+  const bool ccached = !mcached && !cached && T <= 2 * a.bucket_cap;
   int64_t* mcache = reinterpret_cast<int64_t*>(bcache);
+  uint8_t* ccache = reinterpret_cast<uint8_t*>(bcache);
 
   for (int i = tid; i < NBUCKET; i += NT) Q.hist[i] = 0;
   if (tid == 0) Q.cnt = 0;
@@ -860,6 +865,7 @@ __device__ __attribute__((always_inline)) inline int64_t quantile_bias(const Arg
         atomicAdd(&Q.hist[b], 1);
         if (mcached) mcache[t] = M;
         if (cached) bcache[t] = static_cast<int16_t>(b);
+        if (ccached) ccache[t] = static_cast<uint8_t>(b >> 3);
       }
     }
   }
@@ -927,6 +933,16 @@ __device__ __attribute__((always_inline)) inline int64_t quantile_bias(const Arg
     for (int t = tid; t < T; t += NT) {
       const int b = bcache[t];
       if (b <= b1 && b >= b2) gather(margin_of(a, be, e, t, small));
+    }
+  } else if (ccached) {
+    const int c1 = b1 >> 3, c2 = b2 >> 3;
+    for (int t = tid; t < T; t += NT) {
+      const int cb = ccache[t];
+      if (cb <= c1 && cb >= c2) {
+        const int64_t M = margin_of(a, be, e, t, small);
+        const int b = bucket_of(M - cut);
+        if (b <= b1 && b >= b2) gather(M);
+      }
     }
   } else {
     for (int t = tid; t < T; t += NT) {
