@@ -39,7 +39,7 @@ TRAFFIC = {("k3_prefill", "batch"): 27.006e9,      # gemm_pipe<96, 256, 1, 3, 64
            ("k3_mxfp4_a8", "batch"): 9.111e9,      # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 8, 2>
            ("k3_mxfp4_a4", "batch"): 8.592e9,      # gemm_pipe_fp4<320, 256, 2, 3, 8, true, 4, 3>
            ("tiny", "batch"): 2.369e6,             # gemm_f32<EPI_SITU>
-           ("qb", "batch"): 23.217e9}              # route_loop<14>
+           ("qb", "batch"): 20.967e9}              # route_loop<14>
 METRIC = "Stable LatentMoE layer tokens/s on 1 MI355X; MFMA util & HBM GB/s vs peak"
 
 
