@@ -65,6 +65,11 @@ CASES = [
     ("pivot_k_n_minus_1", 300, 40, 39, 0.5),
     ("pivot_k63", 400, 200, 63, 0.5),
     ("pivot_tokens_per_wave", 7000, 128, 6, 1.0),
+    # quantile rounds of large batches: past the 2-byte bucket cache in LDS
+    # (about 41 K tokens) each token keeps a 1-byte coarse bucket; past twice
+    # that, the gather recomputes every margin
+    ("coarse_bucket_cache", 60000, 16, 2, 0.5),
+    ("uncached_gather", 120000, 16, 2, 0.5),
     # fewer tokens than the four waves of one top-k block; every target 0 or 1
     ("one_token", 1, 64, 4, 0.5),
     ("three_tokens", 3, 64, 4, 0.5),
